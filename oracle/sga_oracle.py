@@ -1,0 +1,190 @@
+"""Plain, slow, float64 CPU oracle for the Sparse Gated Attention (SGA) hot path.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import, call or run this module. It shares no code with
+the HIP library or its Python binding, and imports neither.
+
+What it computes, and the passages it follows:
+
+* Visibility. A query token at position p of its sequence sees the cached rows
+  0..p, its own row included. The A.X K2 fact sheet (archdb.vladsavinov.com,
+  "A.X K2") lists every layer as a global, full-context MLA layer. The news
+  article (rebasdaily, section on long tasks that cannot re-read all old
+  content) says each query reads at most 2,048 positions whatever the context
+  length.
+* Indexer (fact sheet, fact "token-selection mechanism inside global layers":
+  a DSA-style indexer with 64 ReLU-scored heads of width 128; fact "width of the
+  sparse-attention indexer key cached per token": 128). The score of cached
+  position s for query t is I[t,s] = sum_h w[t,h] * max(0, q[t,h,:] . k[s,:]).
+  The pages print no formula; this is the DSA-style form with per-query head
+  weights.
+* Top-k (same fact: top-2048 positions per query; news article: at most 2,048).
+  Positions are ordered by score (descending), with equal scores ordered by
+  lower position first. The first min(k, visible) positions are kept. They
+  are returned in ascending position order, padded with -1.
+* Absorbed MLA attention over the kept rows (fact sheet facts: 64 query heads;
+  QK dim per head 192 = 128 NoPE + 64 RoPE; compressed KV latent 512; shared
+  positional key 64; no QK normalisation; no QKV bias). Each cached row holds
+  576 values: latent (512) then RoPE key (64). The absorbed query of head h
+  also has 576 values. Logit z_j = sm_scale * q[h] . row_j over all 576
+  columns. Values are the first 512 columns only (the latent). The output
+  stays in latent space. The softmax is over the kept rows. lse is the natural
+  log-sum-exp of z.
+* Gate (fact sheet fact "gate applied to the attention output before the output
+  projection": a head-specific sigmoid gate projected jointly with the query;
+  the nlp.com.ai "A.X K2 FP8" summary says it is meant to suppress attention
+  sinks). out[h,:] = o[h,:] * 1/(1+exp(-g[h])), one logit per (token, head).
+  The gate multiplies each head's output by one scalar, and the later per-head
+  value up-projection is linear. So gating the latent-space output is the same
+  as gating after the up-projection.
+
+Storage formats decoded here from their bit-level definitions:
+- bf16: the upper 16 bits of an IEEE-754 binary32;
+- OCP E4M3FN: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; a zero
+  exponent field is subnormal; S.1111.111 is NaN; there is no infinity.
+An fp8 row's value is its decoded payload times its fp32 row scale.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_scores",
+           "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT"]
+
+D_LATENT = 512
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64: a bf16 is the top half of a binary32."""
+    b = np.asarray(bits).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def e4m3fn_table() -> np.ndarray:
+    """The 256 values of OCP E4M3FN, built from the format's field definition."""
+    table = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            table[code] = np.nan
+        elif e == 0:
+            table[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            table[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return table
+
+
+_E4M3 = e4m3fn_table()
+
+
+def decode_e4m3fn(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """uint8 payload rows [n, D] and fp32 row scales [n] -> float64 [n, D]."""
+    vals = _E4M3[np.asarray(payload, dtype=np.uint8)]
+    return vals * np.asarray(scale, dtype=np.float64)[:, None]
+
+
+@dataclass
+class Store:
+    """A flat cache: raw bits per row plus the format ('bf16' or 'e4m3fn')."""
+    bits: np.ndarray                  # uint16 [rows, D] (bf16) or uint8 [rows, D] (e4m3fn)
+    fmt: str
+    scale: Optional[np.ndarray] = None  # float32 [rows] for e4m3fn
+
+    def rows(self, idx) -> np.ndarray:
+        if self.fmt == "bf16":
+            return decode_bf16(self.bits[idx])
+        if self.fmt == "e4m3fn":
+            return decode_e4m3fn(self.bits[idx], self.scale[idx])
+        raise ValueError(self.fmt)
+
+
+def index_scores(q_idx: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """One query's indexer scores over `keys`.
+
+    q_idx [H, D] indexer query heads, w [H] head weights, keys [n, D] -> [n].
+    The per-head dot products are clipped at zero first, then weighted and summed.
+    """
+    dots = keys.astype(np.float64) @ q_idx.astype(np.float64).T      # [n, H]
+    return np.maximum(dots, 0.0) @ w.astype(np.float64)              # [n]
+
+
+def select_topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Keep the first min(k, n) positions in the order (score desc, position asc).
+
+    Returns int32 [k]: the kept positions in ascending order, then -1 padding.
+    -0.0 and +0.0 compare equal, so they tie and the tie goes to the lower position.
+    """
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -np.asarray(scores, dtype=np.float64)))
+    kept = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:kept.shape[0]] = kept
+    return out
+
+
+def sparse_mla(q_abs: np.ndarray, rows: np.ndarray, sm_scale: float, d_v: int = D_LATENT):
+    """Absorbed MLA attention of one query over the gathered cache rows.
+
+    q_abs [H, 576], rows [m, 576] -> (o [H, d_v], lse [H]). With no rows the
+    output is zero and lse is -inf.
+    """
+    H = q_abs.shape[0]
+    if rows.shape[0] == 0:
+        return np.zeros((H, d_v)), np.full(H, -np.inf)
+    z = float(sm_scale) * (q_abs.astype(np.float64) @ rows.T)      # [H, m]
+    zmax = z.max(axis=1)
+    e = np.exp(z - zmax[:, None])
+    denom = e.sum(axis=1)
+    o = (e @ rows[:, :d_v]) / denom[:, None]
+    lse = zmax + np.log(denom)
+    return o, lse
+
+
+def sigmoid_gate(o: np.ndarray, g: np.ndarray) -> np.ndarray:
+    """out[h, :] = o[h, :] * sigmoid(g[h])."""
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-np.asarray(g, dtype=np.float64)))
+    return o * sig[:, None]
+
+
+def forward(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store: Store,
+            q_abs, kv_store: Store, gate, k: int, sm_scale: float,
+            tokens: Optional[Sequence[int]] = None, keep_scores: bool = False) -> dict:
+    """Indexer -> top-k -> sparse MLA -> gate, one query token at a time.
+
+    q_idx [T,H,128], w [T,H], q_abs [T,H,576], gate [T,H] or None (ungated).
+    Returns indices int32 [n,k], out float64 [n,H,512], lse float64 [n,H] for
+    the chosen tokens (all by default), and optionally the score rows.
+    """
+    T = len(token_pos)
+    tokens = list(range(T)) if tokens is None else list(tokens)
+    H = q_abs.shape[1]
+    res = {"tokens": tokens,
+           "indices": np.full((len(tokens), k), -1, dtype=np.int32),
+           "out": np.zeros((len(tokens), H, D_LATENT)),
+           "lse": np.full((len(tokens), H), -np.inf)}
+    if keep_scores:
+        res["scores"] = []
+    for i, t in enumerate(tokens):
+        b = int(token_seq[t])
+        p = int(token_pos[t])
+        assert p < int(seq_len[b]), "a token must sit inside its sequence"
+        base = int(seq_start[b])
+        n = p + 1                                         # rows 0..p are visible
+        keys = k_store.rows(slice(base, base + n))
+        scores = index_scores(np.asarray(q_idx[t], np.float64), np.asarray(w[t], np.float64), keys)
+        idx = select_topk(scores, k)
+        kept = idx[idx >= 0].astype(np.int64)
+        o, lse = sparse_mla(np.asarray(q_abs[t], np.float64), kv_store.rows(base + kept), sm_scale)
+        res["indices"][i] = idx
+        res["out"][i] = o if gate is None else sigmoid_gate(o, gate[t])
+        res["lse"][i] = lse
+        if keep_scores:
+            res["scores"].append(scores)
+    return res

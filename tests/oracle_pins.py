@@ -1,0 +1,316 @@
+"""Checks that pin the CPU oracle to facts outside itself.
+
+Each check takes the oracle module and raises AssertionError when it disagrees
+with one of these:
+- a hand-worked example (tests/golden);
+- a closed form;
+- a library routine (torch's scaled_dot_product_attention, logsumexp, dtype casts);
+- a brute-force definition on tiny inputs.
+test_oracle_pins.py runs the checks on the real oracle. test_oracle_mutations.py
+runs them on oracles with planted mistakes and expects at least one check to fail.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import torch
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- formats
+def check_bf16_decode(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = orc.decode_bf16(bits)
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), "bf16 decode disagrees with torch's bfloat16"
+
+
+def check_e4m3fn_table(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3fn_table()
+    same = (got == ref) | (np.isnan(got) & np.isnan(ref))
+    assert same.all(), "E4M3FN table disagrees with torch.float8_e4m3fn"
+    # named values of the OCP format: max normal, min subnormal, one, NaN
+    assert got[0x7E] == 448.0 and got[0xFE] == -448.0
+    assert got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+    scaled = orc.decode_e4m3fn(np.array([[0x38, 0x7E]], np.uint8), np.array([0.25], np.float32))
+    assert scaled.tolist() == [[0.25, 112.0]]
+
+
+# ---------------------------------------------------------------- indexer
+def check_indexer_worked_example(orc):
+    g = _golden("indexer_worked_example.json")
+    s = orc.index_scores(np.array(g["q_idx"], float), np.array(g["w"], float), np.array(g["keys"], float))
+    assert s.tolist() == [float(x) for x in g["scores"]], s
+
+
+def check_indexer_exact_integer(orc):
+    """For integer inputs the fp64 result must be the exact integer result
+    (|sums| < 2**53). Also checks that positive scaling of a key scales its score."""
+    rng = np.random.default_rng(5)
+    q = rng.integers(-3, 4, size=(64, 128))
+    w = rng.integers(-4, 5, size=64)
+    keys = rng.integers(-3, 4, size=(300, 128))
+    got = orc.index_scores(q.astype(float), w.astype(float), keys.astype(float))
+    # exact integer arithmetic, one head at a time
+    exact = np.zeros(300, dtype=np.int64)
+    for h in range(64):
+        d = keys.astype(np.int64) @ q[h].astype(np.int64)
+        exact += w[h] * np.where(d > 0, d, 0)
+    assert np.array_equal(got, exact.astype(float))
+    got2 = orc.index_scores(q.astype(float), w.astype(float), 4.0 * keys.astype(float))
+    assert np.array_equal(got2, 4.0 * got)
+
+
+# ---------------------------------------------------------------- top-k
+def _rank_select(scores, k):
+    """Definition by rank: position i is kept iff fewer than k positions precede
+    it (higher score, or equal score at a lower position)."""
+    n = len(scores)
+    kept = []
+    for i in range(n):
+        ahead = sum(1 for j in range(n) if scores[j] > scores[i] or (scores[j] == scores[i] and j < i))
+        if ahead < k:
+            kept.append(i)
+    return kept + [-1] * (k - len(kept))
+
+
+def check_topk_worked_example(orc):
+    g = _golden("indexer_worked_example.json")
+    for k, exp in g["topk"].items():
+        got = orc.select_topk(np.array(g["scores"], float), int(k))
+        assert got.tolist() == exp, (k, got)
+
+
+def check_topk_rank_definition(orc):
+    rng = np.random.default_rng(7)
+    for trial in range(40):
+        n = int(rng.integers(1, 120))
+        k = int(rng.integers(1, 140))
+        scores = rng.integers(-4, 5, size=n).astype(float)   # many ties on purpose
+        if trial % 5 == 0:
+            scores = rng.standard_normal(n)
+        got = orc.select_topk(scores, k)
+        assert got.tolist() == _rank_select(list(scores), k), (n, k)
+
+
+def check_topk_enumeration(orc):
+    """For n <= 8 enumerate every subset of size min(k, n) and keep those in which
+    every member precedes every non-member; exactly one must exist, and it is the
+    oracle's answer."""
+    rng = np.random.default_rng(11)
+    for _ in range(60):
+        n = int(rng.integers(1, 9))
+        k = int(rng.integers(1, 10))
+        scores = rng.integers(0, 3, size=n).astype(float)
+        m = min(k, n)
+
+        def before(i, j):
+            return scores[i] > scores[j] or (scores[i] == scores[j] and i < j)
+
+        winners = [set(c) for c in itertools.combinations(range(n), m)
+                   if all(before(i, j) for i in c for j in range(n) if j not in c)]
+        assert len(winners) == 1
+        got = orc.select_topk(scores, k)
+        assert sorted(winners[0]) + [-1] * (k - m) == got.tolist()
+
+
+def check_topk_special_cases(orc):
+    assert orc.select_topk(np.full(50, 7.0), 10).tolist() == list(range(10))
+    assert orc.select_topk(np.arange(5, 0, -1, dtype=float), 8).tolist() == [0, 1, 2, 3, 4, -1, -1, -1]
+    # -0.0 and +0.0 tie: the lower position wins
+    assert orc.select_topk(np.array([-1.0, 0.0, -0.0, 0.0]), 2).tolist() == [1, 2]
+    assert orc.select_topk(np.array([-1.0, -0.0, 0.0]), 1).tolist() == [1]
+    assert orc.select_topk(np.array([3.0]), 1).tolist() == [0]
+
+
+# ---------------------------------------------------------------- attention
+def check_attention_closed_form(orc):
+    g = _golden("attention_two_rows.json")
+    rows = np.zeros((2, 576))
+    rows[0, 530] = g["a"]
+    rows[0, :3] = g["v0"]
+    rows[1, :3] = g["v1"]
+    q = np.zeros((1, 576))
+    q[0, 530] = math.log(3.0) / (g["sm_scale"] * g["a"])
+    o, lse = orc.sparse_mla(q, rows, g["sm_scale"])
+    assert o.shape == (1, 512)
+    assert np.allclose(o[0, :3], g["expected_o_first3"], rtol=0, atol=1e-14)
+    assert np.all(o[0, 3:] == 0.0)
+    assert abs(lse[0] - g["expected_lse"]) < 1e-14
+    gated = orc.sigmoid_gate(o, np.array([g["gate_logit"]]))
+    assert np.allclose(gated[0, :3], g["expected_gated_first3"], rtol=0, atol=1e-14)
+
+
+def check_attention_vs_sdpa(orc):
+    """Selecting every row reproduces dense attention over those rows
+    (torch scaled_dot_product_attention, fp64, one shared K/V for all heads)."""
+    rng = np.random.default_rng(3)
+    m = 37
+    rows = rng.standard_normal((m, 576)) / 24
+    q = rng.standard_normal((64, 576)) * 4        # sharp softmax
+    tau = 1 / math.sqrt(192)
+    o, lse = orc.sparse_mla(q, rows, tau)
+    Q = torch.from_numpy(q)[None, :, None, :]                       # [1,H,1,576]
+    K = torch.from_numpy(rows)[None, None].expand(1, 64, m, 576)
+    V = torch.from_numpy(rows[:, :512])[None, None].expand(1, 64, m, 512)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=tau)[0, :, 0].numpy()
+    assert np.allclose(o, ref, rtol=1e-12, atol=1e-14)
+    z = torch.from_numpy(tau * (q @ rows.T))
+    assert np.allclose(lse, torch.logsumexp(z, dim=1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def check_attention_special_cases(orc):
+    rng = np.random.default_rng(4)
+    rows = rng.standard_normal((9, 576))
+    q = rng.standard_normal((64, 576))
+    o1, lse1 = orc.sparse_mla(q, rows[3:4], 0.07)
+    assert np.array_equal(o1, np.broadcast_to(rows[3, :512], (64, 512)))   # one row: weight 1
+    assert np.allclose(lse1, 0.07 * (q @ rows[3]), rtol=1e-14, atol=1e-14)
+    o0, _ = orc.sparse_mla(np.zeros((64, 576)), rows, 0.07)                 # zero query: mean
+    assert np.allclose(o0, np.broadcast_to(rows[:, :512].mean(axis=0), (64, 512)), rtol=1e-13, atol=1e-15)
+    perm = rng.permutation(9)                                               # order of rows is irrelevant
+    a, la = orc.sparse_mla(q, rows, 0.07)
+    b, lb = orc.sparse_mla(q, rows[perm], 0.07)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-15) and np.allclose(la, lb, rtol=1e-13)
+    oe, le = orc.sparse_mla(q, rows[:0], 0.07)                              # no rows
+    assert np.all(oe == 0) and np.all(np.isneginf(le))
+
+
+def check_gate(orc):
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((64, 512))
+    g = np.full(64, np.inf)
+    assert np.array_equal(orc.sigmoid_gate(o, g), o)                        # +inf: ungated
+    out = orc.sigmoid_gate(o, -g)
+    assert np.all(out == 0)                                                 # -inf: closed
+    assert np.array_equal(orc.sigmoid_gate(o, np.zeros(64)), 0.5 * o)       # 0: half
+    h = orc.sigmoid_gate(o, np.full(64, math.log(3.0)))                     # sigmoid(ln 3) = 3/4
+    assert np.allclose(h, 0.75 * o, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- whole path
+def _dense_causal_gated(q_abs, kv, pos, tau, gate):
+    """Dense causal attention through torch SDPA with an explicit mask s <= p,
+    then the sigmoid gate (torch.sigmoid)."""
+    n = kv.shape[0]
+    T = q_abs.shape[0]
+    mask = torch.from_numpy(np.arange(n)[None, :] <= np.asarray(pos)[:, None])    # [T, n]
+    Q = torch.from_numpy(q_abs).permute(1, 0, 2)[None]                             # [1,H,T,576]
+    K = torch.from_numpy(kv)[None, None].expand(1, q_abs.shape[1], n, 576)
+    V = torch.from_numpy(kv[:, :512])[None, None].expand(1, q_abs.shape[1], n, 512)
+    o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, attn_mask=mask[None, None], scale=tau)
+    o = o[0].permute(1, 0, 2)                                                      # [T,H,512]
+    return (o * torch.sigmoid(torch.from_numpy(gate))[..., None]).numpy()
+
+
+def check_forward_dense_limit(orc):
+    """With k at least the context, the whole path is dense causal attention
+    (own row included) followed by the gate."""
+    rng = np.random.default_rng(8)
+    n = 40
+    kv_bits = torch.from_numpy(rng.standard_normal((n, 576)).astype(np.float32) / 24).to(torch.bfloat16)
+    kv = kv_bits.to(torch.float64).numpy()
+    k_bits = torch.from_numpy(rng.integers(-3, 4, (n, 128)).astype(np.float32)).to(torch.bfloat16)
+    pos = np.array([0, 1, 17, 39], dtype=np.int32)
+    T = len(pos)
+    q_idx = rng.integers(-3, 4, (T, 64, 128)).astype(float)
+    w = rng.integers(0, 5, (T, 64)).astype(float)
+    q_abs = rng.standard_normal((T, 64, 576))
+    gate = rng.standard_normal((T, 64)) * 2
+    tau = 1 / math.sqrt(192)
+    ks = orc.Store(k_bits.view(torch.int16).numpy().view(np.uint16), "bf16")
+    vs = orc.Store(kv_bits.view(torch.int16).numpy().view(np.uint16), "bf16")
+    res = orc.forward(np.zeros(T, np.int32), pos, np.zeros(1, np.int64), np.array([n], np.int32),
+                      q_idx, w, ks, q_abs, vs, gate, 64, tau)
+    ref = _dense_causal_gated(q_abs, kv, pos, tau, gate)
+    assert np.allclose(res["out"], ref, rtol=1e-11, atol=1e-14)
+    for i, p in enumerate(pos):
+        assert res["indices"][i].tolist() == list(range(p + 1)) + [-1] * (64 - p - 1)
+
+
+def check_forward_selects_by_indexer(orc):
+    """When k is smaller than the context, the kept rows are the top-k rows of the
+    indexer score under the tie rule (rank definition), and the attention equals
+    dense attention restricted to exactly those rows."""
+    rng = np.random.default_rng(9)
+    n = 30
+    kv_bits = torch.from_numpy(rng.standard_normal((n, 576)).astype(np.float32) / 24).to(torch.bfloat16)
+    kv = kv_bits.to(torch.float64).numpy()
+    k_int = rng.integers(-1, 2, (n, 128))
+    k_bits = torch.from_numpy(k_int.astype(np.float32)).to(torch.bfloat16)
+    pos = np.array([29, 12], dtype=np.int32)
+    q_idx = rng.integers(-1, 2, (2, 64, 128)).astype(float)
+    w = rng.integers(0, 3, (2, 64)).astype(float)
+    q_abs = rng.standard_normal((2, 64, 576))
+    tau = 1 / math.sqrt(192)
+    ks = orc.Store(k_bits.view(torch.int16).numpy().view(np.uint16), "bf16")
+    vs = orc.Store(kv_bits.view(torch.int16).numpy().view(np.uint16), "bf16")
+    k = 7
+    res = orc.forward(np.zeros(2, np.int32), pos, np.zeros(1, np.int64), np.array([n], np.int32),
+                      q_idx, w, ks, q_abs, vs, None, k, tau)
+    for i, p in enumerate(pos):
+        # exact integer scores over rows 0..p
+        sc = []
+        for s in range(p + 1):
+            tot = 0
+            for h in range(64):
+                d = int(np.dot(k_int[s], q_idx[i, h].astype(int)))
+                tot += int(w[i, h]) * max(d, 0)
+            sc.append(tot)
+        want = _rank_select(sc, k)
+        assert res["indices"][i].tolist() == want
+        kept = [s for s in want if s >= 0]
+        Q = torch.from_numpy(q_abs[i])[None, :, None, :]
+        K = torch.from_numpy(kv[kept])[None, None].expand(1, 64, len(kept), 576)
+        V = torch.from_numpy(kv[kept, :512])[None, None].expand(1, 64, len(kept), 512)
+        ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=tau)[0, :, 0].numpy()
+        assert np.allclose(res["out"][i], ref, rtol=1e-11, atol=1e-14)
+
+
+def check_forward_fp8_store(orc):
+    """An fp8 cache row is its decoded payload times its scale: the path over an
+    fp8 store equals the path over the same values stored exactly in bf16
+    (E4M3 values times powers of two are exact in bf16)."""
+    rng = np.random.default_rng(10)
+    n = 24
+    codes = rng.integers(0, 256, (n, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38                         # no NaN codes
+    scale = np.ldexp(1.0, rng.integers(-3, 3, n)).astype(np.float32)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32) * torch.from_numpy(scale)[:, None]
+    vals_bits = vals.to(torch.bfloat16)
+    assert torch.equal(vals_bits.to(torch.float32), vals)
+    kcodes = torch.from_numpy(rng.integers(-3, 4, (n, 128)).astype(np.float32)).to(torch.float8_e4m3fn)
+    kscale = np.ldexp(1.0, rng.integers(-2, 3, n)).astype(np.float32)
+    kvals = (kcodes.to(torch.float32) * torch.from_numpy(kscale)[:, None]).to(torch.bfloat16)
+    q_idx = rng.integers(-3, 4, (1, 64, 128)).astype(float)
+    w = rng.integers(0, 5, (1, 64)).astype(float)
+    q_abs = rng.standard_normal((1, 64, 576))
+    tau = 1 / math.sqrt(192)
+    args = (np.zeros(1, np.int32), np.array([n - 1], np.int32), np.zeros(1, np.int64), np.array([n], np.int32))
+    a = orc.forward(*args, q_idx, w, orc.Store(kcodes.view(torch.uint8).numpy(), "e4m3fn", kscale), q_abs,
+                    orc.Store(codes, "e4m3fn", scale), None, 5, tau)
+    b = orc.forward(*args, q_idx, w, orc.Store(kvals.view(torch.int16).numpy().view(np.uint16), "bf16"), q_abs,
+                    orc.Store(vals_bits.view(torch.int16).numpy().view(np.uint16), "bf16"), None, 5, tau)
+    assert np.array_equal(a["indices"], b["indices"])
+    assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
+
+
+ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_example,
+              check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
+              check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
+              check_attention_vs_sdpa, check_attention_special_cases, check_gate,
+              check_forward_dense_limit, check_forward_selects_by_indexer, check_forward_fp8_store]

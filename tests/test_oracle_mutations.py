@@ -1,0 +1,116 @@
+"""Plant plausible mistakes in copies of the oracle (CPU only) and check that the
+pins catch every one of them."""
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import sga_oracle as base
+
+
+def _clone(**overrides):
+    m = types.ModuleType("mutant")
+    for name in dir(base):
+        setattr(m, name, getattr(base, name))
+    for k, v in overrides.items():
+        setattr(m, k, v)
+    # forward must call the mutated pieces
+    def forward(*a, **kw):
+        saved = {k: getattr(base, k) for k in overrides}
+        try:
+            for k, v in overrides.items():
+                setattr(base, k, v)
+            return base.forward(*a, **kw)
+        finally:
+            for k, v in saved.items():
+                setattr(base, k, v)
+    m.forward = forward
+    return m
+
+
+def _relu_after_weight(q, w, keys):
+    return np.maximum((keys @ q.T) @ w, 0.0)
+
+
+def _weight_then_relu(q, w, keys):
+    return np.maximum((keys @ q.T) * w[None, :], 0.0).sum(axis=1)
+
+
+def _ties_high_index(scores, k):
+    n = scores.shape[0]
+    order = np.lexsort((-np.arange(n), -scores))
+    kept = np.sort(order[:min(k, n)])
+    out = np.full(k, -1, np.int32)
+    out[:kept.shape[0]] = kept
+    return out
+
+
+def _unsorted_output(scores, k):
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores))[:min(k, n)]
+    out = np.full(k, -1, np.int32)
+    out[:order.shape[0]] = order
+    return out
+
+
+def _values_from_tail(q, rows, s, d_v=512):
+    z = s * (q @ rows.T)
+    e = np.exp(z - z.max(1, keepdims=True))
+    return (e @ rows[:, 64:]) / e.sum(1, keepdims=True), z.max(1) + np.log(np.exp(z - z.max(1, keepdims=True)).sum(1))
+
+
+def _logits_latent_only(q, rows, s, d_v=512):
+    z = s * (q[:, :512] @ rows[:, :512].T)
+    zm = z.max(1)
+    e = np.exp(z - zm[:, None])
+    return (e @ rows[:, :512]) / e.sum(1)[:, None], zm + np.log(e.sum(1))
+
+
+_ORIG_MLA = base.sparse_mla
+
+
+def _lse_log2(q, rows, s, d_v=512):
+    o, lse = _ORIG_MLA(q, rows, s, d_v)
+    return o, lse / np.log(2.0)
+
+
+def _gate_sign(o, g):
+    return o * (1.0 / (1.0 + np.exp(np.asarray(g, float))))[:, None]
+
+
+def _bad_e4m3_table():
+    t = base.e4m3fn_table().copy()
+    t[1:8] = t[1:8] * 2          # subnormals with the wrong exponent
+    return t
+
+
+MUTANTS = {
+    "relu_after_weighting": dict(index_scores=_relu_after_weight),
+    "weight_inside_relu": dict(index_scores=_weight_then_relu),
+    "ties_to_high_index": dict(select_topk=_ties_high_index),
+    "indices_not_ascending": dict(select_topk=_unsorted_output),
+    "values_from_wrong_columns": dict(sparse_mla=_values_from_tail),
+    "rope_dropped_from_logits": dict(sparse_mla=_logits_latent_only),
+    "lse_in_base_2": dict(sparse_mla=_lse_log2),
+    "gate_sign_flipped": dict(sigmoid_gate=_gate_sign),
+    "e4m3_subnormals": dict(e4m3fn_table=_bad_e4m3_table),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name):
+    mutant = _clone(**MUTANTS[name])
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert caught, f"no pin caught the planted mistake {name}"
+
+
+def test_real_oracle_passes_all_pins():
+    for check in oracle_pins.ALL_CHECKS:
+        check(oracle)
