@@ -1,0 +1,206 @@
+/*
+ * sga.h: C ABI of libsga, a gfx950 (MI355X) implementation of Sparse Gated
+ * Attention (SGA): indexer -> top-k -> sparse absorbed-MLA attention -> sigmoid
+ * gate.
+ *
+ * Sources for what each call computes:
+ * - A.X K2 fact sheet (archdb.vladsavinov.com, "A.X K2"), the facts on the
+ *   token mixer, the attention shapes, the gate and the token-selection
+ *   mechanism;
+ * - the "A.X K2 Technical Report" abstract (arXiv:2608.30181), on SGA reading
+ *   2,048 positions per query;
+ * - the rebasdaily article on A.X K2, in its section on long tasks that cannot
+ *   re-read all old content: at most 2,048 positions per query.
+ *
+ * Conventions that hold for every call:
+ * - Pointers are device pointers unless marked (host). The caller owns every
+ *   buffer. The library never allocates or frees device memory. Scratch comes
+ *   from a caller-provided workspace `ws` of `ws_bytes` bytes, at least the
+ *   matching *_workspace_size(); its contents on entry do not matter.
+ * - Every call only enqueues work on `stream` and returns. The caller
+ *   synchronises. Calls keep no state between them, so calls on different
+ *   streams with different workspaces may run concurrently. Outputs must not
+ *   alias inputs or the workspace.
+ * - Errors: problems the host can see (null required pointers, bad sizes,
+ *   unsupported dtypes, a small workspace, a non-finite sm_scale) make the call
+ *   return a non-zero sga_status before anything is launched. Outputs are then
+ *   left untouched. A failed launch returns SGA_ERR_HIP. Nothing aborts, and no
+ *   C++ exception crosses the ABI.
+ * - Fixed model dimensions: 64 query heads; indexer 64 heads x 128;
+ *   cached latent row 576 = 512 latent + 64 RoPE key; values are the first
+ *   512 columns.
+ * - Element types: bf16 is IEEE bfloat16. SGA_FP8_E4M3 is OCP E4M3FN (max 448,
+ *   no infinities) with one fp32 scale per cached row. A row's value is
+ *   payload * scale. Scales must be finite and positive.
+ */
+#ifndef SGA_H
+#define SGA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGA_API __attribute__((visibility("default")))
+
+#define SGA_HEADS 64        /* query heads */
+#define SGA_IDX_HEADS 64    /* indexer heads */
+#define SGA_IDX_DIM 128     /* indexer head width = cached indexer key width */
+#define SGA_D_LATENT 512    /* compressed KV latent = value width */
+#define SGA_D_ROPE 64       /* shared RoPE key width */
+#define SGA_D_QK 576        /* cached latent row width, absorbed query width */
+#define SGA_MAX_LEN (1 << 20) /* longest visible context a query may have */
+#define SGA_MAX_K 65536     /* largest top-k */
+#define SGA_MAX_TOKENS 65535 /* most query tokens in one call */
+
+typedef enum sga_status {
+  SGA_OK = 0,
+  SGA_ERR_INVALID_ARG = 1,  /* null pointer, bad size, non-finite scale */
+  SGA_ERR_UNSUPPORTED = 2,  /* dtype or size outside what the kernels handle */
+  SGA_ERR_WORKSPACE = 3,    /* workspace missing or smaller than required */
+  SGA_ERR_HIP = 4           /* a HIP launch or query failed */
+} sga_status;
+
+typedef enum sga_dtype {
+  SGA_BF16 = 0,
+  SGA_FP8_E4M3 = 1          /* OCP E4M3FN payload + fp32 scale per row */
+} sga_dtype;
+
+/*
+ * A ragged batch of query tokens over per-sequence caches stored back to back
+ * in flat row arrays. Token t belongs to sequence b = token_seq[t] and sits at
+ * position p = token_pos[t] (0-based) of it.
+ *
+ * The token sees cached rows 0..p of its sequence, its own row included.
+ * Those are flat rows seq_start[b] .. seq_start[b] + p.
+ *
+ * The host fields are read on the host. The pointer fields point to device
+ * memory and are read only by kernels. The kernels clamp what they read:
+ *   visible rows n_t = min(p + 1, seq_len[b], max_len, cache_rows - seq_start[b]).
+ * Inconsistent metadata therefore never reads outside the caches or writes
+ * outside the outputs. It only changes which rows count as visible. A token
+ * with n_t <= 0 sees nothing: its indices are all -1, its output is 0 and its
+ * lse is -inf.
+ */
+typedef struct sga_batch {
+  int32_t num_tokens;        /* (host) 0 <= T <= SGA_MAX_TOKENS; T == 0 is a no-op */
+  int32_t num_seqs;          /* (host) B >= 1 when T > 0 */
+  int32_t max_len;           /* (host) >= p + 1 for every token; 1..SGA_MAX_LEN */
+  int32_t reserved;          /* must be 0 */
+  int64_t cache_rows;        /* (host) rows in the flat caches (k_idx and kv) */
+  const int32_t* token_seq;  /* [T] */
+  const int32_t* token_pos;  /* [T] */
+  const int64_t* seq_start;  /* [B] first flat row of each sequence */
+  const int32_t* seq_len;    /* [B] rows cached for each sequence */
+} sga_batch;
+
+/*
+ * Optional timing hooks for sga_forward. Each non-NULL event is recorded on
+ * the call's stream at the named point. Recording an event is the only effect.
+ */
+typedef struct sga_trace {
+  hipEvent_t indexer_begin;  /* before the indexer kernel */
+  hipEvent_t indexer_end;    /* after the indexer kernel */
+  hipEvent_t topk_end;       /* after the last top-k kernel */
+  hipEvent_t attn_end;       /* after the attention (and combine) kernels */
+} sga_trace;
+
+/*
+ * sga_index_scores: indexer scores.
+ * Source: the fact sheet's token-selection fact (a DSA-style indexer of 64
+ * ReLU-scored heads of width 128) and its cached-indexer-key-width fact (128).
+ *
+ * For each token t and each visible position s < n_t:
+ *   scores[t*ld + s] = sum_h w[t*64+h] * max(0, sum_d q_idx[t,h,d] * key[row(s), d])
+ * where key = k_idx (bf16), or payload * k_idx_scale[row] (fp8).
+ *   q_idx       [T,64,128] bf16, row-major.
+ *   w           [T,64] fp32 head weights.
+ *   k_idx       [cache_rows,128] bf16 or fp8 payload, row-major (256 or 128 B per row).
+ *   k_idx_scale [cache_rows] fp32 for fp8; must be NULL for bf16.
+ *   scores      [T, ld] fp32, ld >= max_len. Only entries s < n_t are written.
+ * Accumulation is fp32 (bf16 products are exact in fp32). With integer-valued
+ * inputs every partial sum is an integer, so the scores are exact whenever
+ * |score| < 2^24. For fp8 keys each head's dot product is taken over the
+ * payload and then multiplied by the row scale.
+ */
+SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, const float* w,
+                                    const void* k_idx, const float* k_idx_scale,
+                                    sga_dtype k_idx_dtype, float* scores, int64_t ld,
+                                    hipStream_t stream);
+
+/*
+ * sga_topk: per-token top-k selection over indexer scores.
+ * Source: the fact sheet's token-selection fact (top-2048 tokens per query);
+ * the rebasdaily article (at most 2,048 positions per query at any length).
+ *
+ * For token t, positions 0..n_t-1 are ordered by scores[t*ld + s] descending.
+ * Equal scores are ordered by lower position first, and -0.0 equals +0.0.
+ * The first min(k, n_t) positions are kept and written to indices[t*k ..]
+ * in ascending position order, then padded with -1.
+ * The result is exact: it depends only on the score values, never on
+ * rounding or scheduling. Scores must not be NaN; for NaN inputs the result is
+ * unspecified but stays in bounds.
+ *   scores  [T, ld] fp32 (only s < n_t read). indices [T, k] int32.
+ *   ws      >= sga_topk_workspace_size(T, max_len, k) bytes.
+ */
+SGA_API size_t sga_topk_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k);
+SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
+                            int32_t* indices, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sga_sparse_mla_attn: absorbed MLA attention over the selected latent rows,
+ * with the per-head sigmoid gate applied to the output.
+ * Source: the fact sheet's attention facts (64 query heads; QK dim 192 =
+ * 128 NoPE + 64 RoPE; 512-wide latent and 64-wide shared RoPE key cached per
+ * token; no QK norm, no QKV bias) and its gate fact (a head-specific sigmoid
+ * gate on the attention output before o_proj).
+ *
+ * For token t, let J = the entries j of indices[t*k .. t*k+k-1] with
+ * 0 <= j < n_t. Other entries, -1 included, are skipped. For each head h:
+ *   z_j   = sm_scale * sum_{c<576} q_abs[t,h,c] * row_j[c],  row_j = kv[seq_start[b] + j]
+ *   o     = sum_j softmax(z)_j * row_j[0:512]
+ *   out[t,h,:] = o * sigmoid(gate_logits[t*64+h])   (o itself when gate_logits == NULL)
+ *   lse[t*64+h] = log(sum_j exp(z_j))                (natural log)
+ * An fp8 row is payload * kv_scale[row]. With J empty, out = 0 and lse = -inf.
+ *   q_abs [T,64,576] bf16. kv [cache_rows,576] bf16 or fp8 payload.
+ *   kv_scale [cache_rows] fp32 for fp8, NULL for bf16. indices [T,k] int32.
+ *   out [T,64,512] fp32. lse [T,64] fp32 or NULL.
+ * Logits and softmax are fp32. Probabilities enter the value product as
+ * bf16, and accumulation is fp32.
+ */
+SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k);
+SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs, const void* kv,
+                                       const float* kv_scale, sga_dtype kv_dtype,
+                                       const int32_t* indices, int32_t k, float sm_scale,
+                                       const float* gate_logits, float* out, float* lse,
+                                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * sga_forward: the whole path, indexer -> top-k -> attention -> gate, for one
+ * batch. Its results equal sga_index_scores, then sga_topk, then
+ * sga_sparse_mla_attn, called with the same arguments.
+ * indices_out [T,k] receives the selected positions when non-NULL.
+ * trace may be NULL.
+ */
+SGA_API size_t sga_forward_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k);
+SGA_API sga_status sga_forward(const sga_batch* batch,
+                               const void* q_idx, const float* w, const void* k_idx,
+                               const float* k_idx_scale, sga_dtype k_idx_dtype,
+                               const void* q_abs, const void* kv, const float* kv_scale,
+                               sga_dtype kv_dtype, int32_t k, float sm_scale,
+                               const float* gate_logits, float* out, float* lse,
+                               int32_t* indices_out, void* ws, size_t ws_bytes,
+                               const sga_trace* trace, hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+SGA_API const char* sga_status_string(sga_status status);
+/* Library version as major*10000 + minor*100 + patch. */
+SGA_API int sga_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SGA_H */

@@ -1,0 +1,351 @@
+// Host side of libsga: argument checks, workspace planning and kernel launches
+// for the C ABI declared in include/sga.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "sga.h"
+#include "sga_kernels.h"
+
+namespace {
+
+using sga::AttnArgs;
+using sga::BatchView;
+using sga::IndexerArgs;
+using sga::TopkArgs;
+using sga::TopkCtrl;
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Carves consecutive, 256-byte aligned regions out of a workspace.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += align_up(count * sizeof(T));
+    return p;
+  }
+};
+
+int64_t bitmap_words(int32_t max_len) { return ((int64_t)max_len + 63) / 64 * 2; }
+
+// ---------------------------------------------------------------- top-k layout
+struct TopkLayout {
+  uint32_t* hist;
+  TopkCtrl* ctrl;
+  uint32_t* sel;
+  uint32_t* cand;
+  int64_t words, cand_cap;
+  size_t clear_words;  // hist + ctrl are contiguous and cleared per call
+};
+
+TopkLayout carve_topk(Carver& c, int32_t T, int32_t max_len) {
+  TopkLayout L;
+  L.words = bitmap_words(max_len);
+  L.cand_cap = max_len;
+  // hist and ctrl are carved back to back and cleared by one fill kernel
+  size_t hist_bytes = (size_t)T * sga::kHist1 * sizeof(uint32_t);
+  size_t ctrl_bytes = (size_t)T * sizeof(TopkCtrl);
+  char* start = c.base ? c.base + c.used : nullptr;
+  c.used += align_up(hist_bytes + ctrl_bytes);
+  L.hist = reinterpret_cast<uint32_t*>(start);
+  L.ctrl = start ? reinterpret_cast<TopkCtrl*>(start + hist_bytes) : nullptr;
+  L.clear_words = (hist_bytes + ctrl_bytes) / sizeof(uint32_t);
+  L.sel = c.take<uint32_t>((size_t)T * L.words);
+  L.cand = c.take<uint32_t>((size_t)T * L.cand_cap);
+  return L;
+}
+
+// ---------------------------------------------------------------- attention plan
+struct AttnPlan {
+  int splits, rows_per_split;
+};
+
+AttnPlan plan_attention(int32_t T, int32_t k) {
+  const int tile = sga::kAttnTileRows;
+  const int tiles = (k + tile - 1) / tile;
+  int want = (T > 0) ? (256 + T - 1) / T : 1;   // aim for about 256 workgroups
+  int max_splits = tiles / 4 > 0 ? tiles / 4 : 1;  // at least 4 tiles per split
+  int splits = want < max_splits ? want : max_splits;
+  if (splits < 1) splits = 1;
+  int tiles_per = (tiles + splits - 1) / splits;
+  splits = (tiles + tiles_per - 1) / tiles_per;
+  return AttnPlan{splits, tiles_per * tile};
+}
+
+struct AttnLayout {
+  float* part_o;
+  float* part_ml;
+};
+
+AttnLayout carve_attn(Carver& c, int32_t T, const AttnPlan& p) {
+  AttnLayout L{nullptr, nullptr};
+  if (p.splits > 1) {
+    L.part_o = c.take<float>((size_t)T * p.splits * sga::kHeads * sga::kDLatent);
+    L.part_ml = c.take<float>((size_t)T * p.splits * sga::kHeads * 2);
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------- checks
+sga_status check_batch(const sga_batch* b) {
+  if (!b) return SGA_ERR_INVALID_ARG;
+  if (b->num_tokens < 0 || b->num_seqs < 0 || b->reserved != 0) return SGA_ERR_INVALID_ARG;
+  if (b->num_tokens == 0) return SGA_OK;
+  if (b->num_seqs < 1 || b->max_len < 1 || b->cache_rows < 1) return SGA_ERR_INVALID_ARG;
+  if (b->max_len > SGA_MAX_LEN || b->num_tokens > SGA_MAX_TOKENS) return SGA_ERR_UNSUPPORTED;
+  if (!b->token_seq || !b->token_pos || !b->seq_start || !b->seq_len) return SGA_ERR_INVALID_ARG;
+  return SGA_OK;
+}
+
+sga_status check_store(const void* data, const float* scale, sga_dtype dt) {
+  if (!data || !aligned16(data)) return SGA_ERR_INVALID_ARG;
+  if (dt == SGA_BF16) return scale ? SGA_ERR_INVALID_ARG : SGA_OK;
+  if (dt == SGA_FP8_E4M3) return scale ? SGA_OK : SGA_ERR_INVALID_ARG;
+  return SGA_ERR_UNSUPPORTED;
+}
+
+BatchView view_of(const sga_batch* b) {
+  BatchView v;
+  v.token_seq = b->token_seq;
+  v.token_pos = b->token_pos;
+  v.seq_start = b->seq_start;
+  v.seq_len = b->seq_len;
+  v.num_seqs = b->num_seqs;
+  v.max_len = b->max_len;
+  v.cache_rows = b->cache_rows;
+  return v;
+}
+
+sga_status hip_status(hipError_t e) { return e == hipSuccess ? SGA_OK : SGA_ERR_HIP; }
+
+#define SGA_TRY(expr)                      \
+  do {                                     \
+    sga_status _s = (expr);                \
+    if (_s != SGA_OK) return _s;           \
+  } while (0)
+#define SGA_HIP(expr)                      \
+  do {                                     \
+    if ((expr) != hipSuccess) return SGA_ERR_HIP; \
+  } while (0)
+
+sga_status record(hipEvent_t e, hipStream_t s) {
+  if (!e) return SGA_OK;
+  return hip_status(hipEventRecord(e, s));
+}
+
+sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
+                    int32_t* indices, const TopkLayout& L, bool hist_ready, hipStream_t stream) {
+  TopkArgs a;
+  a.batch = view_of(batch);
+  a.num_tokens = batch->num_tokens;
+  a.scores = scores;
+  a.ld = ld;
+  a.k = k;
+  a.indices = indices;
+  a.hist = L.hist;
+  a.ctrl = L.ctrl;
+  a.sel = L.sel;
+  a.words = L.words;
+  a.cand = L.cand;
+  a.cand_cap = L.cand_cap;
+  if (!hist_ready) {
+    SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
+    SGA_HIP(sga::launch_topk_hist(a, stream));
+  }
+  SGA_HIP(sga::launch_topk_select(a, stream));
+  SGA_HIP(sga::launch_topk_finalize(a, stream));
+  return SGA_OK;
+}
+
+sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* kv,
+                         const float* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
+                         int32_t k, float sm_scale, const float* gate, float* out, float* lse,
+                         const AttnPlan& plan, const AttnLayout& L, hipStream_t stream) {
+  AttnArgs a;
+  a.batch = view_of(batch);
+  a.num_tokens = batch->num_tokens;
+  a.q_abs = static_cast<const uint16_t*>(q_abs);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.kv_scale = kv_scale;
+  a.indices = indices;
+  a.k = k;
+  a.sm_scale = sm_scale;
+  a.gate = gate;
+  a.out = out;
+  a.lse = lse;
+  a.splits = plan.splits;
+  a.rows_per_split = plan.rows_per_split;
+  a.part_o = L.part_o;
+  a.part_ml = L.part_ml;
+  SGA_HIP(sga::launch_attention(a, kv_dtype == SGA_FP8_E4M3, stream));
+  SGA_HIP(sga::launch_combine(a, stream));
+  return SGA_OK;
+}
+
+size_t topk_ws(int32_t T, int32_t max_len) {
+  Carver c(nullptr);
+  carve_topk(c, T, max_len);
+  return c.used;
+}
+
+size_t attn_ws(int32_t T, int32_t k) {
+  Carver c(nullptr);
+  carve_attn(c, T, plan_attention(T, k));
+  return c.used;
+}
+
+}  // namespace
+
+extern "C" {
+
+SGA_API const char* sga_status_string(sga_status s) {
+  switch (s) {
+    case SGA_OK: return "SGA_OK";
+    case SGA_ERR_INVALID_ARG: return "SGA_ERR_INVALID_ARG: null pointer, bad size or non-finite scale";
+    case SGA_ERR_UNSUPPORTED: return "SGA_ERR_UNSUPPORTED: dtype or size outside what the kernels handle";
+    case SGA_ERR_WORKSPACE: return "SGA_ERR_WORKSPACE: workspace missing or too small";
+    case SGA_ERR_HIP: return "SGA_ERR_HIP: a HIP launch or query failed";
+  }
+  return "unknown sga_status";
+}
+
+SGA_API int sga_version(void) { return 100; }
+
+SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, const float* w,
+                                    const void* k_idx, const float* k_idx_scale,
+                                    sga_dtype k_idx_dtype, float* scores, int64_t ld,
+                                    hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (batch->num_tokens == 0) return SGA_OK;
+  if (!q_idx || !w || !scores || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
+  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
+  if (ld < batch->max_len) return SGA_ERR_INVALID_ARG;
+  IndexerArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = view_of(batch);
+  a.num_tokens = batch->num_tokens;
+  a.q_idx = static_cast<const uint16_t*>(q_idx);
+  a.w = w;
+  a.k_idx = static_cast<const uint8_t*>(k_idx);
+  a.k_scale = k_idx_scale;
+  a.scores = scores;
+  a.ld = ld;
+  return hip_status(sga::launch_indexer(a, k_idx_dtype == SGA_FP8_E4M3, false, stream));
+}
+
+SGA_API size_t sga_topk_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k) {
+  (void)k;
+  if (num_tokens <= 0 || max_len <= 0) return 0;
+  return topk_ws(num_tokens, max_len);
+}
+
+SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
+                            int32_t* indices, void* ws, size_t ws_bytes, hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (k < 1) return SGA_ERR_INVALID_ARG;
+  if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
+  if (batch->num_tokens == 0) return SGA_OK;
+  if (!scores || !indices || ld < batch->max_len) return SGA_ERR_INVALID_ARG;
+  size_t need = topk_ws(batch->num_tokens, batch->max_len);
+  if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
+  Carver c(ws);
+  TopkLayout L = carve_topk(c, batch->num_tokens, batch->max_len);
+  return run_topk(batch, scores, ld, k, indices, L, false, stream);
+}
+
+SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k) {
+  if (num_tokens <= 0 || k <= 0) return 0;
+  return attn_ws(num_tokens, k);
+}
+
+SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs, const void* kv,
+                                       const float* kv_scale, sga_dtype kv_dtype,
+                                       const int32_t* indices, int32_t k, float sm_scale,
+                                       const float* gate_logits, float* out, float* lse,
+                                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (k < 1) return SGA_ERR_INVALID_ARG;
+  if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return SGA_ERR_INVALID_ARG;
+  if (batch->num_tokens == 0) return SGA_OK;
+  if (!q_abs || !indices || !out || !aligned16(q_abs) || !aligned16(out)) return SGA_ERR_INVALID_ARG;
+  SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+  AttnPlan plan = plan_attention(batch->num_tokens, k);
+  size_t need = attn_ws(batch->num_tokens, k);
+  if (need > 0 && (!ws || ws_bytes < need)) return SGA_ERR_WORKSPACE;
+  Carver c(ws);
+  AttnLayout L = carve_attn(c, batch->num_tokens, plan);
+  return run_attention(batch, q_abs, kv, kv_scale, kv_dtype, indices, k, sm_scale, gate_logits,
+                       out, lse, plan, L, stream);
+}
+
+SGA_API size_t sga_forward_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k) {
+  if (num_tokens <= 0 || max_len <= 0 || k <= 0) return 0;
+  Carver c(nullptr);
+  c.take<float>((size_t)num_tokens * max_len);     // scores
+  c.take<int32_t>((size_t)num_tokens * k);         // indices
+  carve_topk(c, num_tokens, max_len);
+  carve_attn(c, num_tokens, plan_attention(num_tokens, k));
+  return c.used;
+}
+
+SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const float* w,
+                               const void* k_idx, const float* k_idx_scale, sga_dtype k_idx_dtype,
+                               const void* q_abs, const void* kv, const float* kv_scale,
+                               sga_dtype kv_dtype, int32_t k, float sm_scale,
+                               const float* gate_logits, float* out, float* lse,
+                               int32_t* indices_out, void* ws, size_t ws_bytes,
+                               const sga_trace* trace, hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (k < 1) return SGA_ERR_INVALID_ARG;
+  if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return SGA_ERR_INVALID_ARG;
+  if (batch->num_tokens == 0) return SGA_OK;
+  if (!q_idx || !w || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
+  if (!q_abs || !out || !aligned16(q_abs) || !aligned16(out)) return SGA_ERR_INVALID_ARG;
+  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
+  SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+  const int32_t T = batch->num_tokens;
+  size_t need = sga_forward_workspace_size(T, batch->max_len, k);
+  if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
+
+  Carver c(ws);
+  float* scores = c.take<float>((size_t)T * batch->max_len);
+  int32_t* idx_ws = c.take<int32_t>((size_t)T * k);
+  TopkLayout TL = carve_topk(c, T, batch->max_len);
+  AttnPlan plan = plan_attention(T, k);
+  AttnLayout AL = carve_attn(c, T, plan);
+  int32_t* indices = indices_out ? indices_out : idx_ws;
+
+  SGA_HIP(sga::launch_clear(TL.hist, (int64_t)TL.clear_words, stream));
+  IndexerArgs ia;
+  ia.batch = view_of(batch);
+  ia.num_tokens = T;
+  ia.q_idx = static_cast<const uint16_t*>(q_idx);
+  ia.w = w;
+  ia.k_idx = static_cast<const uint8_t*>(k_idx);
+  ia.k_scale = k_idx_scale;
+  ia.scores = scores;
+  ia.ld = batch->max_len;
+  ia.hist = TL.hist;
+  ia.ctrl = TL.ctrl;
+  ia.k = k;
+  if (trace) SGA_TRY(record(trace->indexer_begin, stream));
+  SGA_HIP(sga::launch_indexer(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
+  if (trace) SGA_TRY(record(trace->indexer_end, stream));
+  SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
+  if (trace) SGA_TRY(record(trace->topk_end, stream));
+  SGA_TRY(run_attention(batch, q_abs, kv, kv_scale, kv_dtype, indices, k, sm_scale, gate_logits,
+                        out, lse, plan, AL, stream));
+  if (trace) SGA_TRY(record(trace->attn_end, stream));
+  return SGA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Workgroup-level scan and radix-cut helpers for the top-k kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sga_device.h"
+
+namespace sga {
+
+// Exclusive prefix sum of one uint32 per thread over a workgroup of NT threads
+// (NT a multiple of 64). scratch: NT/64 + 1 words of LDS. All threads must call.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wid] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t acc = 0;
+    for (int i = 0; i < NT / 64; ++i) {
+      uint32_t s = scratch[i];
+      scratch[i] = acc;
+      acc += s;
+    }
+    scratch[NT / 64] = acc;
+  }
+  __syncthreads();
+  uint32_t r = scratch[wid] + x - v;
+  *total = scratch[NT / 64];
+  __syncthreads();
+  return r;
+}
+
+// Radix cut over a histogram h[0..nbins) in LDS, digits ranked from the top:
+// finds d with S(d+1) < r <= S(d), S(d) = sum of h[b] for b >= d, 1 <= r <= S(0).
+// Writes res[0] = d and res[1] = S(d+1). nbins must be a multiple of NT.
+template <int NT>
+__device__ __forceinline__ void block_find_cut(const uint32_t* h, int nbins, uint32_t r,
+                                               uint32_t* scratch, uint32_t* res) {
+  const int per = nbins / NT;
+  const int top = nbins - (int)threadIdx.x * per;
+  uint32_t sum = 0;
+  for (int i = 1; i <= per; ++i) sum += h[top - i];
+  uint32_t total;
+  uint32_t above = block_excl_scan<NT>(sum, scratch, &total);
+  if (above < r && r <= above + sum) {
+    uint32_t acc = above;
+    for (int i = 1; i <= per; ++i) {
+      uint32_t c = h[top - i];
+      if (acc + c >= r) {
+        res[0] = (uint32_t)(top - i);
+        res[1] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+}
+
+// Device-scope relaxed load that bypasses the non-coherent vector L1.
+__device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Flushes a workgroup's LDS digit-1 histogram into the token's global
+// histogram. The last workgroup of the token to finish then computes the
+// first radix cut (digit1, above1) for k_eff = min(k, n). All threads call.
+// lds_hist: kHist1 words of LDS. scratch: at least NT/64 + 3 words.
+template <int NT>
+__device__ __forceinline__ void hist1_flush_and_cut(uint32_t* lds_hist, uint32_t* ghist,
+                                                    uint32_t* done, uint32_t* out_digit1,
+                                                    uint32_t* out_above1, int n, int k,
+                                                    unsigned nblocks, uint32_t* scratch) {
+  __syncthreads();
+  for (int b = threadIdx.x; b < kHist1; b += NT) {
+    uint32_t c = lds_hist[b];
+    if (c) atomicAdd(&ghist[b], c);
+  }
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) scratch[NT / 64 + 2] = (atomicAdd(done, 1u) == nblocks - 1) ? 1u : 0u;
+  __syncthreads();
+  if (scratch[NT / 64 + 2] == 0u) return;
+  __threadfence();
+  if (n <= k) return;  // everything visible is kept; no cut needed
+  for (int b = threadIdx.x; b < kHist1; b += NT) lds_hist[b] = load_agent(&ghist[b]);
+  __syncthreads();
+  uint32_t* res = scratch + NT / 64 + 3;  // two words after the flag
+  block_find_cut<NT>(lds_hist, kHist1, (uint32_t)k, scratch, res);
+  if (threadIdx.x == 0) {
+    *out_digit1 = res[0];
+    *out_above1 = res[1];
+  }
+}
+
+}  // namespace sga

@@ -1,0 +1,119 @@
+// Device-side helpers shared by the SGA kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sga {
+
+// ---------------------------------------------------------------- vector types
+// bf16 data travels as 16-bit integers. It is bit-cast to __bf16 vectors only
+// at the MFMA call.
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kHeads = 64;
+constexpr int kIdxHeads = 64;
+constexpr int kIdxDim = 128;
+constexpr int kDLatent = 512;
+constexpr int kDQK = 576;
+
+// ---------------------------------------------------------------- MFMA
+// D(32x32) += A(32x16) * B(16x32). Lane l holds A[l%32][8*(l/32)+i] and
+// B[8*(l/32)+i][l%32] (i = 0..7). Accumulator register r holds
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+// D(16x16) += A(16x32) * B(32x16). Lane l holds A[l%16][8*(l/16)+i] and
+// B[8*(l/16)+i][l%16]. Accumulator register r holds D[4*(l/16)+r][l%16].
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- conversions
+// Four OCP E4M3FN bytes -> four bf16 (exact: every E4M3 value is a bf16 value),
+// packed two per dword.
+__device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t packed) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, true);
+  u32x2 r;
+  // keep the upper 16 bits of each fp32 (exact for E4M3 values)
+  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  return r;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------- radix keys
+// Order-preserving map from fp32 scores to uint32 keys: a larger score gives a
+// larger key. -0.0 maps to the key of +0.0, so they tie.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kDigit1Bits = 11;  // key bits 31..21
+constexpr int kDigit2Bits = 11;  // key bits 20..10
+constexpr int kDigit3Bits = 10;  // key bits 9..0
+constexpr int kHist1 = 1 << kDigit1Bits;
+
+// ---------------------------------------------------------------- visibility
+// Visible rows of a token, clamped so inconsistent metadata never leaves the
+// caches or the output rows.
+__device__ __forceinline__ int visible_rows(int pos, int seq_len, int max_len,
+                                            int64_t seq_start, int64_t cache_rows) {
+  int64_t n = (int64_t)pos + 1;
+  if (n > seq_len) n = seq_len;
+  if (n > max_len) n = max_len;
+  int64_t room = cache_rows - seq_start;
+  if (seq_start < 0) room = 0;
+  if (n > room) n = room;
+  return n > 0 ? (int)n : 0;
+}
+
+struct BatchView {
+  const int32_t* token_seq;
+  const int32_t* token_pos;
+  const int64_t* seq_start;
+  const int32_t* seq_len;
+  int32_t num_seqs;
+  int32_t max_len;
+  int64_t cache_rows;
+
+  // Resolves token t: first flat row of its sequence and its visible row count.
+  __device__ __forceinline__ void token(int t, int64_t& base, int& n) const {
+    int b = token_seq[t];
+    if (b < 0 || b >= num_seqs) { base = 0; n = 0; return; }
+    base = seq_start[b];
+    n = visible_rows(token_pos[t], seq_len[b], max_len, base, cache_rows);
+  }
+};
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
+}
+
+}  // namespace sga

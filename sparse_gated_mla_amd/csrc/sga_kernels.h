@@ -1,0 +1,80 @@
+// Internal launch interface between the C ABI (sga_api.hip) and the kernel
+// translation units. Not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sga_device.h"
+
+namespace sga {
+
+// Per-token top-k control block in the workspace.
+struct TopkCtrl {
+  uint32_t done;        // chunks of this token that have flushed their histogram
+  uint32_t digit1;      // top 11 key bits of the k-th largest score
+  uint32_t above1;      // scores whose top 11 key bits exceed digit1
+  uint32_t cand_count;  // candidates (top bits == digit1) appended so far
+};
+
+constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup
+constexpr int kSelectChunk = 4096;    // positions per select workgroup
+constexpr int kAttnTileRows = 32;     // latent rows per attention tile
+
+struct IndexerArgs {
+  BatchView batch;
+  int num_tokens;
+  const uint16_t* q_idx;   // [T,64,128] bf16
+  const float* w;          // [T,64]
+  const uint8_t* k_idx;    // [rows,128] bf16 (256 B) or fp8 (128 B) rows
+  const float* k_scale;    // [rows] for fp8
+  float* scores;           // [T,ld]
+  int64_t ld;
+  // top-k first level, filled by the fused variant
+  uint32_t* hist;          // [T,2048]
+  TopkCtrl* ctrl;          // [T]
+  int k;
+};
+
+struct TopkArgs {
+  BatchView batch;
+  int num_tokens;
+  const float* scores;
+  int64_t ld;
+  int k;
+  int32_t* indices;        // [T,k]
+  uint32_t* hist;          // [T,2048]
+  TopkCtrl* ctrl;          // [T]
+  uint32_t* sel;           // [T,words]
+  int64_t words;           // bitmap words per token
+  uint32_t* cand;          // [T,cand_cap]
+  int64_t cand_cap;
+};
+
+struct AttnArgs {
+  BatchView batch;
+  int num_tokens;
+  const uint16_t* q_abs;   // [T,64,576] bf16
+  const uint8_t* kv;       // [rows,576] bf16 or fp8
+  const float* kv_scale;   // [rows] for fp8
+  const int32_t* indices;  // [T,k]
+  int k;
+  float sm_scale;
+  const float* gate;       // [T,64] or null
+  float* out;              // [T,64,512]
+  float* lse;              // [T,64] or null
+  int splits;              // row splits per token
+  int rows_per_split;      // multiple of kAttnTileRows
+  float* part_o;           // [T,splits,64,512]
+  float* part_ml;          // [T,splits,64,2]
+};
+
+hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
+hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
+hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);
+size_t topk_finalize_lds_bytes(int64_t words);
+hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_combine(const AttnArgs& a, hipStream_t s);
+
+}  // namespace sga

@@ -1,0 +1,183 @@
+"""GPU parity: each C-ABI entry point against the CPU oracle on seeded inputs,
+at sizes the oracle finishes in seconds, plus edge cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sga_inputs as si
+from gpu_helpers import (Dev, assert_lse_close, assert_out_close, run_oracle, say, stores)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_forward(wl, gate=True, what=""):
+    say(f"[forward] {what or wl.name}: T={wl.num_tokens} max_len={wl.max_len} k={wl.k} fp8={wl.fp8}")
+    dev = Dev(wl)
+    idx, out, lse = dev.forward(gate=gate)
+    ref = run_oracle(wl, gate=gate)
+    assert np.array_equal(idx.cpu().numpy(), ref["indices"]), "indices differ"
+    assert_out_close(out.cpu().numpy(), ref["out"], wl.fp8, what)
+    assert_lse_close(lse.cpu().numpy(), ref["lse"], what)
+    return dev, (idx, out, lse), ref
+
+
+def test_index_scores_tiny_exact():
+    wl = si.config(0)
+    say("[index_scores] tiny decode")
+    dev = Dev(wl)
+    s = dev.scores().cpu().numpy()
+    ref = run_oracle(wl, keep_scores=True)
+    for i, r in enumerate(ref["scores"]):
+        n = r.shape[0]
+        assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
+        assert np.all(np.isnan(s[i, n:])), "wrote beyond the visible rows"
+
+
+def test_topk_tiny_exact():
+    wl = si.config(0)
+    say("[topk] tiny decode, oracle scores")
+    dev = Dev(wl)
+    ref = run_oracle(wl, keep_scores=True)
+    sc = torch.full((wl.num_tokens, wl.max_len), float("nan"))
+    for i, r in enumerate(ref["scores"]):
+        sc[i, :r.shape[0]] = torch.from_numpy(r.astype(np.float32))
+    idx = dev.topk(sc.cuda())
+    assert np.array_equal(idx.cpu().numpy(), ref["indices"])
+
+
+def test_attention_tiny_given_indices():
+    wl = si.config(0)
+    say("[attention] tiny decode, oracle indices")
+    dev = Dev(wl)
+    for gate in (True, False):
+        ref = run_oracle(wl, gate=gate)
+        out, lse = dev.attention(torch.from_numpy(ref["indices"]).cuda(), gate=gate)
+        assert_out_close(out.cpu().numpy(), ref["out"], False, f"gate={gate}")
+        assert_lse_close(lse.cpu().numpy(), ref["lse"])
+
+
+def test_forward_tiny():
+    _check_forward(si.config(0))
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 33, 2047, 2048, 2049, 5000])
+def test_context_lengths_around_k(S):
+    # one sequence; tokens at its last position and at a few earlier ones
+    pos = sorted({S - 1, max(0, S // 2), 0})
+    wl = si.build(f"len{S}", [S], [(0, p) for p in pos], seed=S)
+    _check_forward(wl)
+
+
+@pytest.mark.parametrize("k", [1, 7, 100, 1000])
+def test_small_k(k):
+    wl = si.build(f"k{k}", [3000], [(0, 2999), (0, 1500)], seed=k, k=k)
+    _check_forward(wl)
+
+
+def test_all_equal_scores():
+    wl = si.build("equal", [6000], [(0, 5999), (0, 4000)], seed=3)
+    wl.q_idx.zero_()                               # every score is 0: ties everywhere
+    _, (idx, _, _), _ = _check_forward(wl)
+    assert idx.cpu().numpy()[0].tolist() == list(range(2048))
+
+
+def test_negative_weights_and_wide_values():
+    wl = si.build("negw", [5000], [(0, 4999), (0, 2500), (0, 2100)], seed=4, w_range=(-4, 4))
+    _check_forward(wl)
+
+
+def test_gate_infinities():
+    wl = si.build("gate_inf", [3000], [(0, 2999), (0, 2000)], seed=5)
+    dev = Dev(wl)
+    _, ungated, _ = dev.forward(gate=False)
+    dev.gate = torch.full_like(dev.gate, float("inf"))
+    _, g_pos, _ = dev.forward()
+    assert torch.equal(g_pos, ungated), "gate logit +inf must give the ungated output exactly"
+    dev.gate = torch.full_like(dev.gate, float("-inf"))
+    _, g_neg, _ = dev.forward()
+    assert torch.all(g_neg == 0)
+
+
+def test_sharp_softmax():
+    wl = si.build("sharp", [4500], [(0, 4499), (0, 3000)], seed=6, q_abs_mult=8.0)
+    _check_forward(wl)
+
+
+def test_ragged_batch_many_tokens_per_sequence():
+    lens = [100, 2500, 4097, 1, 2049]
+    rng = np.random.default_rng(7)
+    toks = []
+    for b, L in enumerate(lens):
+        for p in rng.choice(L, size=min(L, 3), replace=False):
+            toks.append((b, int(p)))
+    rng.shuffle(toks)
+    wl = si.build("ragged", lens, toks, seed=7)
+    _check_forward(wl)
+
+
+def test_fp8_caches_small():
+    wl = si.build("fp8_small", [3000, 2100], [(0, 2999), (1, 2099), (0, 1000)], seed=8, fp8=True)
+    _check_forward(wl)
+
+
+def test_attention_skips_invalid_indices():
+    wl = si.build("badidx", [3000], [(0, 2999), (0, 1200)], seed=9)
+    dev = Dev(wl)
+    ref = run_oracle(wl)
+    idx = ref["indices"].copy()
+    # poison some entries: -1, beyond the visible rows, far out of range
+    idx[0, 5] = -1
+    idx[0, 9] = 3000
+    idx[1, 3] = 1300
+    idx[1, 4] = 1 << 30
+    keep = [[j for j in row if 0 <= j <= p] for row, p in zip(idx, wl.token_pos)]
+    ks, vs = stores(wl)
+    want = []
+    for i, kept in enumerate(keep):
+        o, l = oracle.sparse_mla(wl.q_abs[i].double().numpy(), vs.rows(np.array(kept, np.int64)), wl.sm_scale)
+        want.append(oracle.sigmoid_gate(o, wl.gate[i].double().numpy()))
+    out, _ = dev.attention(torch.from_numpy(idx).cuda())
+    assert_out_close(out.cpu().numpy(), np.stack(want), False, "poisoned indices")
+
+
+def test_token_without_visible_rows():
+    wl = si.build("novis", [50], [(0, 10), (0, 49)], seed=10)
+    dev = Dev(wl)
+    dev.batch.token_pos[0] = -1                  # sees nothing
+    idx, out, lse = dev.forward()
+    assert torch.all(idx[0] == -1)
+    assert torch.all(out[0] == 0)
+    assert torch.all(torch.isneginf(lse[0]))
+    ref = run_oracle(wl, tokens=[1])
+    assert np.array_equal(idx[1].cpu().numpy(), ref["indices"][0])
+
+
+def test_empty_batch_is_a_noop():
+    wl = si.build("empty", [10], [], seed=11)
+    dev = Dev(wl)
+    out = torch.empty((0, 64, 512), dtype=torch.float32, device="cuda")
+    import sparse_gated_mla_amd as sga
+    sga.sga_forward(dev.batch, dev.q_idx, dev.w, dev.k_idx, None, dev.q_abs, dev.kv, None, 2048,
+                    wl.sm_scale, dev.gate, out)
+    torch.cuda.synchronize()
+
+
+def test_unfused_steps_equal_forward():
+    wl = si.build("steps", [7000, 3000], [(0, 6999), (1, 2999), (0, 5000)], seed=12)
+    dev = Dev(wl)
+    idx_f, out_f, lse_f = dev.forward()
+    s = dev.scores()
+    idx_s = dev.topk(s)
+    out_s, lse_s = dev.attention(idx_s)
+    assert torch.equal(idx_f, idx_s)
+    assert torch.equal(out_f, out_s) and torch.equal(lse_f, lse_s)
+
+
+def test_repeat_calls_are_deterministic():
+    wl = si.build("repeat", [9000, 4000], [(0, 8999), (1, 3999)], seed=13)
+    dev = Dev(wl)
+    a = dev.forward()
+    b = dev.forward()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
