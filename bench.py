@@ -1,0 +1,261 @@
+"""Benchmark of the SGA decode hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_decode_128k]
+
+One step is one sga_forward call (indexer -> top-k -> sparse MLA attention ->
+gate) over the whole batch. The default workload is 16 sequences at 128K
+context, one query token each, top-2048. The inputs are seeded synthetic
+caches (sga_inputs) and are resident in HBM before the timed region starts.
+Two copies of the inputs alternate between steps, so no step finds the
+previous step's data in the 256 MB Infinity Cache.
+
+Prints one JSON line with:
+- query-tokens/s;
+- roofline: the indexer kernel, timed with HIP events on the library's stream
+  inside the timed steps, against the 8 TB/s HBM peak. The algorithmic bytes
+  are the indexer keys it must read plus its query inputs;
+- cpu_baseline: the float64 CPU oracle, timed on this host over whole batches
+  of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import sga_inputs as si  # noqa: E402
+import sparse_gated_mla_amd as sga  # noqa: E402
+
+METRIC = "SGA decode query-tokens/sec at 128K ctx, k=2048; achieved HBM GB/s vs peak"
+HBM_PEAK_GBPS = 8000.0
+WORKLOADS = {"tiny_decode_4k": 0, "batched_decode_ragged_16k_32k": 1, "long_decode_128k": 2,
+             "extended_decode_256k_fp8": 4}
+PMC_FILE = os.path.join(ROOT, "profiles", "indexer_long_decode_128k_pmc.json")
+INDEXER_SRC = os.path.join(ROOT, "sparse_gated_mla_amd", "csrc", "indexer.hip")
+
+
+# ---------------------------------------------------------------- HIP events
+class HipEvents:
+    """hipEventCreate / hipEventElapsedTime through libamdhip64 (raw handles for sga_trace)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def create(self) -> ctypes.c_void_p:
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed: {rc}")
+        self.events.append(e)
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.events:
+            self.hip.hipEventDestroy(e)
+        self.events = []
+
+
+# ---------------------------------------------------------------- byte model
+def visible(wl) -> np.ndarray:
+    return wl.token_pos.astype(np.int64) + 1
+
+
+def indexer_bytes(wl) -> int:
+    """Algorithmic bytes of one indexer launch: every visible indexer key once
+    (128 elements, plus a 4-byte scale for fp8) and each token's 64x128 bf16
+    query and 64 fp32 head weights. Keys shared by several tokens of one
+    sequence count once."""
+    per_row = 128 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)
+    rows = 0
+    for b in range(wl.num_seqs):
+        sel = wl.token_seq == b
+        if sel.any():
+            rows += int(visible(wl)[sel].max())
+    return rows * per_row + wl.num_tokens * (64 * 128 * 2 + 64 * 4)
+
+
+def step_bytes(wl) -> int:
+    """Algorithmic bytes of one whole step: the indexer's bytes plus, per token,
+    its min(k, visible) selected latent rows (576 elements, plus a scale for fp8),
+    its 64x576 bf16 absorbed query, 64 gate logits, and its fp32 output
+    (64x512) and lse (64)."""
+    per_row = 576 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)
+    sel_rows = int(np.minimum(visible(wl), wl.k).sum())
+    per_tok = 64 * 576 * 2 + 64 * 4 + 64 * 512 * 4 + 64 * 4
+    return indexer_bytes(wl) + sel_rows * per_row + wl.num_tokens * per_tok
+
+
+# ---------------------------------------------------------------- traffic
+def src_digest() -> str:
+    with open(INDEXER_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per indexer launch from the committed rocprofv3 counter summary,
+    or None when it is missing or was taken on a different indexer source."""
+    try:
+        with open(PMC_FILE) as f:
+            d = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if d.get("indexer_source_sha256_16") != src_digest():
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU oracle
+def cpu_baseline(wl, min_seconds: float):
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    ks = (oracle.Store(wl.k_idx.view(torch.uint8).numpy(), "e4m3fn", wl.k_idx_scale.numpy()) if wl.fp8
+          else oracle.Store(wl.k_idx.view(torch.int16).numpy().view(np.uint16), "bf16"))
+    vs = (oracle.Store(wl.kv.view(torch.uint8).numpy(), "e4m3fn", wl.kv_scale.numpy()) if wl.fp8
+          else oracle.Store(wl.kv.view(torch.int16).numpy().view(np.uint16), "bf16"))
+    args = (wl.token_seq, wl.token_pos, wl.seq_start, wl.seq_len, wl.q_idx.double().numpy(),
+            wl.w.double().numpy(), ks, wl.q_abs.double().numpy(), vs, wl.gate.double().numpy(),
+            wl.k, wl.sm_scale)
+    done, t0 = 0, time.perf_counter()
+    passes = 0
+    while True:
+        oracle.forward(*args)
+        done += wl.num_tokens
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    return {"value": done / el, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{passes} full pass(es) over the {wl.num_tokens}-token {wl.name} batch "
+                      f"({done} query tokens, {el:.1f} s, float64 numpy)"}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="long_decode_128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=2, help="input sets alternated between steps")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device copy of known size (for counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path runs on one GPU with no collectives)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        a = torch.ones(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return
+
+    wl = si.config(WORKLOADS[args.workload])
+    T = wl.num_tokens
+    sets = []
+    for c in range(max(1, args.copies)):
+        d = lambda x: None if x is None else x.to(dev)
+        batch = sga.batch_to_device(wl.token_seq, wl.token_pos, wl.seq_start, wl.seq_len,
+                                    wl.cache_rows, device=dev, max_len=wl.max_len)
+        sets.append(dict(batch=batch, q_idx=d(wl.q_idx), w=d(wl.w), k_idx=d(wl.k_idx),
+                         k_idx_scale=d(wl.k_idx_scale), q_abs=d(wl.q_abs), kv=d(wl.kv),
+                         kv_scale=d(wl.kv_scale), gate=d(wl.gate)))
+    out = torch.empty((T, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+    ws = sga.workspace(sga.sga_forward_workspace_size(T, wl.max_len, wl.k), dev)
+
+    ev = HipEvents()
+    K, W = args.steps, args.warmup
+    tr = [sga.SgaTrace(ev.create().value, ev.create().value, ev.create().value, ev.create().value)
+          for _ in range(K)]
+
+    def step(i, trace=None):
+        s = sets[i % len(sets)]
+        sga.sga_forward(s["batch"], s["q_idx"], s["w"], s["k_idx"], s["k_idx_scale"], s["q_abs"],
+                        s["kv"], s["kv_scale"], wl.k, wl.sm_scale, s["gate"], out, lse, idx,
+                        ws=ws, trace=trace)
+
+    for i in range(W):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i, tr[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    idx_ms = [ev.elapsed_ms(tr[i].indexer_begin, tr[i].indexer_end) for i in range(K)]
+    topk_ms = [ev.elapsed_ms(tr[i].indexer_end, tr[i].topk_end) for i in range(K)]
+    attn_ms = [ev.elapsed_ms(tr[i].topk_end, tr[i].attn_end) for i in range(K)]
+    ev.close()
+    ms_per_step = 1e3 * wall / K
+    value = T * K / wall
+    ib = indexer_bytes(wl)
+    idx_avg_s = float(np.mean(idx_ms)) / 1e3
+    achieved = ib / idx_avg_s / 1e9
+    sb = step_bytes(wl)
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if wl.fp8 else "bf16",
+        "data": "synthetic",
+        "config": dict(si.describe(wl), parallelism="single GPU"),
+        "roofline": {"bound": "hbm", "kernel": "indexer_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ib,
+                     "avg_launch_us": round(idx_avg_s * 1e6, 2)},
+        "extra": {"step_algorithmic_bytes": sb,
+                  "step_gbps": round(sb / (ms_per_step / 1e3) / 1e9, 1),
+                  "step_frac_of_hbm_peak": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                  "indexer_us": round(float(np.mean(idx_ms)) * 1e3, 2),
+                  "topk_us": round(float(np.mean(topk_ms)) * 1e3, 2),
+                  "attention_us": round(float(np.mean(attn_ms)) * 1e3, 2),
+                  "input_copies": len(sets)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -232,32 +232,31 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merges the split partials of one token by log-sum-exp, then gates.
-__global__ __launch_bounds__(kThreads) void combine_kernel(AttnArgs a) {
-  const int t = blockIdx.x;
+// Merges the split partials of one (token, head) by log-sum-exp, then gates.
+// One workgroup of 128 threads per (head, token); each thread owns 4 columns.
+__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x, t = blockIdx.y;
   const int S = a.splits;
-  for (int i = threadIdx.x; i < kHeads * (kDLatent / 4); i += kThreads) {
-    const int h = i / (kDLatent / 4), d4 = i % (kDLatent / 4);
-    const int64_t th = (int64_t)t * kHeads + h;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_ml[2 * (((int64_t)t * S + s) * kHeads + h)]);
-    float L = 0.0f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const int64_t ps = ((int64_t)t * S + s) * kHeads + h;
-        const float ms = a.part_ml[2 * ps];
-        if (ms == -INFINITY) continue;
-        const float wgt = __builtin_amdgcn_exp2f(ms - M);
-        L += a.part_ml[2 * ps + 1] * wgt;
-        acc += *reinterpret_cast<const f32x4*>(a.part_o + ps * kDLatent + 4 * d4) * wgt;
-      }
+  const int64_t th = (int64_t)t * kHeads + h;
+  const float* ml = a.part_ml + 2 * ((int64_t)t * S * kHeads + h);   // stride 2*kHeads per split
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * kHeads * s]);
+  float L = 0.0f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (M != -INFINITY) {
+    const float* po = a.part_o + ((int64_t)t * S * kHeads + h) * kDLatent + 4 * threadIdx.x;
+    for (int s = 0; s < S; ++s) {
+      const float ms = ml[2 * kHeads * s];
+      if (ms == -INFINITY) continue;
+      const float wgt = __builtin_amdgcn_exp2f(ms - M);
+      L += ml[2 * kHeads * s + 1] * wgt;
+      acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * wgt;
     }
-    const float gs = gate_factor(a.gate, th);
-    const float inv = L > 0.0f ? gs / L : 0.0f;
-    *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 4 * d4) = acc * inv;
-    if (a.lse && d4 == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
   }
+  const float gs = gate_factor(a.gate, th);
+  const float inv = L > 0.0f ? gs / L : 0.0f;
+  *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 4 * threadIdx.x) = acc * inv;
+  if (a.lse && threadIdx.x == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -272,7 +271,7 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s) {
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s) {
   if (a.num_tokens == 0 || a.splits == 1) return hipSuccess;
-  combine_kernel<<<a.num_tokens, kThreads, 0, s>>>(a);
+  combine_kernel<<<dim3(kHeads, a.num_tokens), 128, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -3,18 +3,29 @@
 // Source: A.X K2 fact sheet (archdb), token-selection fact: a DSA-style indexer
 // of 64 ReLU-scored heads of width 128; cached indexer key width 128.
 //
-// Mapping onto gfx950: one workgroup streams kIndexerChunk positions of one
-// token's key cache. Each wave takes 32 positions at a time and contracts
-// them with the token's 64x128 query on v_mfma_f32_32x32x16_bf16:
-//   A = query heads (M = 32 heads per block, two blocks), from registers;
-//   B = keys (N = 32 positions, K = 16 dims per step, 8 steps), loaded
-//       straight from HBM. Each lane loads 16 contiguous bytes per step.
-// The contraction order over the 128 dims is permuted the same way in A and
-// B: lane group g of step s covers dims 64g + 8s .. 64g + 8s + 7. So lanes
-// l and l+32 read the two 128-byte halves of the same key row.
-// Epilogue, per lane: ReLU, times w, summed over its 32 heads. One cross-half
-// shuffle then gives the score of each position. fp8 keys are widened to bf16
-// exactly. The row scale multiplies each head's dot product before the ReLU.
+// Mapping onto gfx950:
+// - Streaming. A workgroup streams kIndexerChunk positions of one token's key
+//   cache; its four waves take 32-position tiles in turn. Every load
+//   instruction reads 1 KiB of contiguous keys (16 B per lane), so each wave
+//   instruction covers whole cache lines. Each wave keeps two tiles of loads
+//   in flight.
+// - Re-layout. A wave writes its tile into a private 8 KiB LDS region. The
+//   16-byte slots of each row are XOR-swizzled by row, so the 16 lanes of a
+//   b128 write or read hit distinct banks. The wave then reads the tile back in
+//   the operand layout of v_mfma_f32_32x32x16_bf16. No workgroup barrier is
+//   needed: each wave owns its region, and its LDS operations complete in order.
+// - Contraction.
+//     A = query heads (M = 32 heads per block, two blocks), kept in registers;
+//     B = keys (N = 32 positions, K = 16 dims per step, 8 steps).
+//   The dims are visited in a permuted order, the same in A and B: lane group
+//   g of step s covers dims 64g + 8s .. 64g + 8s + 7.
+// - Epilogue, per lane: ReLU, times w, summed over the lane's 32 heads. One
+//   cross-half shuffle then gives each position's score.
+// - fp8. Keys are widened to bf16 exactly on the LDS read. The row scale
+//   multiplies each head's dot product before the ReLU.
+// - Fused top-k. The variant used by the whole forward pass also counts the
+//   top 11 key bits of every score into a per-token histogram (the first radix
+//   level of the top-k).
 #include "sga_block.h"
 #include "sga_kernels.h"
 
@@ -25,40 +36,105 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;
 
-template <bool kFp8>
-__device__ __forceinline__ void load_key_tile(const uint8_t* __restrict__ k_idx, int64_t row,
-                                              int g, u32x4 (&kb)[8]) {
-  if constexpr (!kFp8) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(k_idx + row * 256 + g * 128);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kb[s] = __builtin_nontemporal_load(src + s);
-  } else {
-    const u32x4* src = reinterpret_cast<const u32x4*>(k_idx + row * 128 + g * 64);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) kb[s] = __builtin_nontemporal_load(src + s);  // raw fp8 bytes
-  }
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+
+// A buffer resource over [p, p + bytes): loads past the end return zeros.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
 template <bool kFp8>
-__device__ __forceinline__ void widen_keys(u32x4 (&kb)[8]) {
-  if constexpr (kFp8) {
-    // kb[0..3] hold 64 fp8 keys (dims 64g + 16s + 0..15); widen in place,
-    // back to front, into 8 steps of 8 bf16.
+struct KeyTile {
+  // bf16 tile: 32 rows x 256 B = 8 loads of 1 KiB; load s, lane l -> row 4s + l/16,
+  //   16-byte chunk l%16.
+  // fp8 tile:  32 rows x 128 B = 4 loads of 1 KiB; load s, lane l -> row 8s + l/8,
+  //   chunk l%8; plus the fp32 scale of row l%32.
+  static constexpr int kLoads = kFp8 ? 4 : 8;
+  static constexpr int kRowBytes = kFp8 ? 128 : 256;
+  u32x4 v[kLoads];
+  float scale;
+
+  // Loads tile `tile` of the workgroup's chunk. Rows past the chunk read as zeros.
+  __device__ __forceinline__ void load(rsrc_t keys, rsrc_t scales, int tile, int lane) {
+    const int off = tile * kTile * kRowBytes + lane * 16;
 #pragma unroll
-    for (int s = 3; s >= 0; --s) {
-      u32x4 raw = kb[s];
-      u32x2 a = e4m3x4_to_bf16x4(raw.x), b = e4m3x4_to_bf16x4(raw.y);
-      u32x2 c = e4m3x4_to_bf16x4(raw.z), d = e4m3x4_to_bf16x4(raw.w);
-      kb[2 * s] = u32x4{a.x, a.y, b.x, b.y};
-      kb[2 * s + 1] = u32x4{c.x, c.y, d.x, d.y};
+    for (int s = 0; s < kLoads; ++s)
+      v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off + s * 1024, 0, 0));
+    if constexpr (kFp8)
+      scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                            scales, (tile * kTile + (lane & 31)) * 4, 0, 0));
+    // keep each tile's loads together and in program order, so the wait for
+    // one tile never covers the loads of the tile issued after it
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // swizzled 16-byte slot of chunk c in row r
+  static __device__ __forceinline__ int slot(int r, int c) {
+    return kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+  }
+
+  __device__ __forceinline__ void store(uint8_t* lds, int lane) const {
+#pragma unroll
+    for (int s = 0; s < kLoads; ++s) {
+      const int r = kFp8 ? (8 * s + (lane >> 3)) : (4 * s + (lane >> 4));
+      const int c = kFp8 ? (lane & 7) : (lane & 15);
+      *reinterpret_cast<u32x4*>(lds + r * kRowBytes + 16 * slot(r, c)) = v[s];
     }
   }
+
+  // B operands for the 8 k-steps: row n = lane%32, dims 64g + 8s .. +7 (g = lane/32)
+  static __device__ __forceinline__ void operands(const uint8_t* lds, int lane, u32x4 (&b)[8]) {
+    const int n = lane & 31, g = lane >> 5;
+    if constexpr (!kFp8) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        b[s] = *reinterpret_cast<const u32x4*>(lds + n * 256 + 16 * slot(n, 8 * g + s));
+    } else {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // chunk 4g + s holds dims 64g + 16s .. +15 = steps 2s and 2s+1
+        u32x4 raw = *reinterpret_cast<const u32x4*>(lds + n * 128 + 16 * slot(n, 4 * g + s));
+        u32x2 a = e4m3x4_to_bf16x4(raw.x), bb = e4m3x4_to_bf16x4(raw.y);
+        u32x2 c = e4m3x4_to_bf16x4(raw.z), d = e4m3x4_to_bf16x4(raw.w);
+        b[2 * s] = u32x4{a.x, a.y, bb.x, bb.y};
+        b[2 * s + 1] = u32x4{c.x, c.y, d.x, d.y};
+      }
+    }
+  }
+};
+
+// Scores one staged tile: writes each position's score into lds_scores.
+template <bool kFp8>
+__device__ __forceinline__ void score_tile(const uint8_t* lds, float kscale, int lane,
+                                           const u32x4 (&qa)[2][8], const float (&wr)[2][16],
+                                           int tile, float* lds_scores) {
+  u32x4 b[8];
+  KeyTile<kFp8>::operands(lds, lane, b);
+  f32x16 acc0 = {}, acc1 = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    acc0 = mfma32x32x16(qa[0][s], b[s], acc0);
+    acc1 = mfma32x32x16(qa[1][s], b[s], acc1);
+  }
+  float sc = 0.0f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float d0 = acc0[r], d1 = acc1[r];
+    if constexpr (kFp8) { d0 *= kscale; d1 *= kscale; }
+    sc = fmaf(wr[0][r], fmaxf(d0, 0.0f), sc);
+    sc = fmaf(wr[1][r], fmaxf(d1, 0.0f), sc);
+  }
+  sc += __shfl_xor(sc, 32);
+  if (lane < 32) lds_scores[tile * kTile + lane] = sc;
 }
 
 template <bool kFp8, bool kHist>
-__global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
+  constexpr int kTileBytes = KeyTile<kFp8>::kRowBytes * kTile;
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
+  __shared__ float lds_scores[kIndexerChunk];
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
-  __shared__ uint32_t scratch[32];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nidx = lane & 31, g = lane >> 5;
@@ -68,11 +144,12 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
 
   if constexpr (kHist) {
     for (int b = threadIdx.x; b < kHist1; b += kThreads) lds_hist[b] = 0;
-    __syncthreads();
   }
 
   const int chunk0 = blockIdx.x * kIndexerChunk;
-  if (chunk0 < n) {
+  const int len = min(n - chunk0, kIndexerChunk);   // positions of this chunk (<= 0: none)
+  if (len > 0) {
+    uint8_t* lds = lds_tiles + wave * kTileBytes;
     // query heads as MFMA A operands: qa[mb][s] = q[32mb + l%32][64g + 8s .. +7]
     u32x4 qa[2][8];
     const uint16_t* q = a.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
@@ -89,53 +166,40 @@ __global__ __launch_bounds__(kThreads) void indexer_kernel(IndexerArgs a) {
       for (int r = 0; r < 16; ++r)
         wr[mb][r] = a.w[(int64_t)t * kIdxHeads + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4)];
 
-    const int chunk_end = min(n, chunk0 + kIndexerChunk);
-    const int ntiles = (chunk_end - chunk0 + kTile - 1) / kTile;
-    float* srow = a.scores + (int64_t)t * a.ld;
+    const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * KeyTile<kFp8>::kRowBytes,
+                                  (uint32_t)len * KeyTile<kFp8>::kRowBytes);
+    const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + base + chunk0) : (const void*)a.k_idx,
+                                    kFp8 ? (uint32_t)len * 4u : 0u);
+    const int ntiles = (len + kTile - 1) / kTile;
+    const int mine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
 
-    int tile = wave;
-    u32x4 kb[8];
-    if (tile < ntiles) {
-      int pos = min(chunk0 + tile * kTile + nidx, n - 1);
-      load_key_tile<kFp8>(a.k_idx, base + pos, g, kb);
-    }
-    for (; tile < ntiles; tile += kWaves) {
-      u32x4 cur[8];
-#pragma unroll
-      for (int s = 0; s < 8; ++s) cur[s] = kb[s];
-      const int pos = chunk0 + tile * kTile + nidx;
-      float kscale = 1.0f;
-      if constexpr (kFp8) kscale = a.k_scale[base + min(pos, n - 1)];
-      if (tile + kWaves < ntiles) {
-        int npos = min(chunk0 + (tile + kWaves) * kTile + nidx, n - 1);
-        load_key_tile<kFp8>(a.k_idx, base + npos, g, kb);
-      }
-      widen_keys<kFp8>(cur);
-      f32x16 acc0 = {}, acc1 = {};
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        acc0 = mfma32x32x16(qa[0][s], cur[s], acc0);
-        acc1 = mfma32x32x16(qa[1][s], cur[s], acc1);
-      }
-      float sc = 0.0f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float d0 = acc0[r], d1 = acc1[r];
-        if constexpr (kFp8) { d0 *= kscale; d1 *= kscale; }
-        sc = fmaf(wr[0][r], fmaxf(d0, 0.0f), sc);
-        sc = fmaf(wr[1][r], fmaxf(d1, 0.0f), sc);
-      }
-      sc += __shfl_xor(sc, 32);
-      if (g == 0 && pos < chunk_end) {
-        srow[pos] = sc;
-        if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
-      }
+    // this wave's tiles: wave, wave + 4, ...; two in flight. Loads are never
+    // skipped (past the chunk they read zeros), so each wait is exact.
+    KeyTile<kFp8> s0, s1;
+    s0.load(keys, scales, wave, lane);
+    s1.load(keys, scales, wave + kWaves, lane);
+    for (int i = 0; i < mine; i += 2) {
+      const int t0 = wave + i * kWaves;
+      s0.store(lds, lane);
+      const float sc0 = s0.scale;
+      s0.load(keys, scales, t0 + 2 * kWaves, lane);
+      score_tile<kFp8>(lds, sc0, lane, qa, wr, t0, lds_scores);
+      s1.store(lds, lane);
+      const float sc1 = s1.scale;
+      s1.load(keys, scales, t0 + 3 * kWaves, lane);
+      if (i + 1 < mine) score_tile<kFp8>(lds, sc1, lane, qa, wr, t0 + kWaves, lds_scores);
     }
   }
-  if constexpr (kHist) {
-    hist1_flush_and_cut<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1, &a.ctrl[t].done,
-                                  &a.ctrl[t].digit1, &a.ctrl[t].above1, n, a.k, gridDim.x, scratch);
+  __syncthreads();
+  if (len > 0) {
+    float* srow = a.scores + (int64_t)t * a.ld + chunk0;
+    for (int i = threadIdx.x; i < len; i += kThreads) {
+      const float sc = lds_scores[i];
+      srow[i] = sc;
+      if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
+    }
   }
+  if constexpr (kHist) hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
 }
 
 }  // namespace

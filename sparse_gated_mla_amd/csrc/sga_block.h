@@ -68,35 +68,32 @@ __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Flushes a workgroup's LDS digit-1 histogram into the token's global
-// histogram. The last workgroup of the token to finish then computes the
-// first radix cut (digit1, above1) for k_eff = min(k, n). All threads call.
-// lds_hist: kHist1 words of LDS. scratch: at least NT/64 + 3 words.
+// Adds a workgroup's LDS digit-1 histogram into the token's global histogram
+// (relaxed device-scope atomics; visible to the next kernel on the stream).
+// No fence and no cross-workgroup hand-off: the cut is taken by the next kernel.
 template <int NT>
-__device__ __forceinline__ void hist1_flush_and_cut(uint32_t* lds_hist, uint32_t* ghist,
-                                                    uint32_t* done, uint32_t* out_digit1,
-                                                    uint32_t* out_above1, int n, int k,
-                                                    unsigned nblocks, uint32_t* scratch) {
+__device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* ghist) {
   __syncthreads();
   for (int b = threadIdx.x; b < kHist1; b += NT) {
     uint32_t c = lds_hist[b];
     if (c) atomicAdd(&ghist[b], c);
   }
-  __threadfence();
+}
+
+// First radix cut of a token from its global digit-1 histogram: the digit of
+// the k-th largest score and the count of scores with a larger digit.
+// Every thread of the workgroup gets the result. lds_hist: kHist1 words;
+// scratch: at least NT/64 + 3 words.
+template <int NT>
+__device__ __forceinline__ void hist1_cut(const uint32_t* ghist, uint32_t* lds_hist, uint32_t k,
+                                          uint32_t* scratch, uint32_t& digit1, uint32_t& above1) {
+  for (int b = threadIdx.x; b < kHist1; b += NT) lds_hist[b] = ghist[b];
   __syncthreads();
-  if (threadIdx.x == 0) scratch[NT / 64 + 2] = (atomicAdd(done, 1u) == nblocks - 1) ? 1u : 0u;
+  uint32_t* res = scratch + NT / 64 + 1;
+  block_find_cut<NT>(lds_hist, kHist1, k, scratch, res);
+  digit1 = res[0];
+  above1 = res[1];
   __syncthreads();
-  if (scratch[NT / 64 + 2] == 0u) return;
-  __threadfence();
-  if (n <= k) return;  // everything visible is kept; no cut needed
-  for (int b = threadIdx.x; b < kHist1; b += NT) lds_hist[b] = load_agent(&ghist[b]);
-  __syncthreads();
-  uint32_t* res = scratch + NT / 64 + 3;  // two words after the flag
-  block_find_cut<NT>(lds_hist, kHist1, (uint32_t)k, scratch, res);
-  if (threadIdx.x == 0) {
-    *out_digit1 = res[0];
-    *out_above1 = res[1];
-  }
 }
 
 }  // namespace sga

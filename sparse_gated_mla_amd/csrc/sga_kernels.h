@@ -10,10 +10,10 @@ namespace sga {
 
 // Per-token top-k control block in the workspace.
 struct TopkCtrl {
-  uint32_t done;        // chunks of this token that have flushed their histogram
   uint32_t digit1;      // top 11 key bits of the k-th largest score
   uint32_t above1;      // scores whose top 11 key bits exceed digit1
   uint32_t cand_count;  // candidates (top bits == digit1) appended so far
+  uint32_t pad;
 };
 
 constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup

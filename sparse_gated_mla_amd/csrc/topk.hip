@@ -6,13 +6,13 @@
 //
 // Exact radix select on order-preserving uint32 keys, in three stages:
 //   1. digit-1 histogram: the top 11 key bits of every score, built from the
-//      indexer epilogue (fused path) or by topk_hist_kernel. The last
-//      workgroup of each token finds digit1, the top-11-bit value of the k-th
-//      largest score.
-//   2. topk_select_kernel (many workgroups per token): positions whose digit
-//      is above digit1 go straight into a selection bitmap. One ballot gives
-//      64 positions. Positions whose digit equals digit1 are appended to a
-//      candidate list.
+//      indexer epilogue (fused path) or by topk_hist_kernel.
+//   2. topk_select_kernel (many workgroups per token): each workgroup first
+//      reads the token's histogram and finds digit1, the top-11-bit value of
+//      the k-th largest score. No cross-workgroup hand-off or device-scope
+//      fence is needed. Positions whose digit is above digit1 go straight
+//      into a selection bitmap; one ballot gives 64 positions. Positions whose
+//      digit equals digit1 are appended to a candidate list.
 //   3. topk_finalize_kernel (one workgroup per token): two more radix levels
 //      (11 and 10 bits) over the candidates find the exact k-th key. Ties at
 //      that key are kept lowest position first, using a prefix count over a
@@ -37,7 +37,6 @@ __global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, in
 
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
   __shared__ uint32_t lds_hist[kHist1];
-  __shared__ uint32_t scratch[32];
   const int t = blockIdx.y;
   int64_t base;
   int n;
@@ -49,13 +48,12 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
   const float* srow = a.scores + (int64_t)t * a.ld;
   for (int p = c0 + threadIdx.x; p < c1; p += kHistThreads)
     atomicAdd(&lds_hist[score_key(srow[p]) >> (32 - kDigit1Bits)], 1u);
-  hist1_flush_and_cut<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1, &a.ctrl[t].done,
-                                    &a.ctrl[t].digit1, &a.ctrl[t].above1, n, a.k, gridDim.x,
-                                    scratch);
+  hist1_flush<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t stage[kSelectChunk];
+  __shared__ uint32_t stage[kSelectChunk];   // also holds the histogram for the cut
+  __shared__ uint32_t scratch[32];
   __shared__ uint32_t stage_count;
   __shared__ uint32_t stage_base;
   const int t = blockIdx.y;
@@ -66,7 +64,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   const int c0 = blockIdx.x * kSelectChunk;
   if (c0 >= n) return;
   const int c1 = min(n, c0 + kSelectChunk);
-  const uint32_t d1 = a.ctrl[t].digit1;
+  // first radix cut, taken redundantly by every workgroup of the token
+  uint32_t d1, above1;
+  hist1_cut<kSelThreads>(a.hist + (int64_t)t * kHist1, stage, (uint32_t)a.k, scratch, d1, above1);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.ctrl[t].digit1 = d1;
+    a.ctrl[t].above1 = above1;
+  }
   if (threadIdx.x == 0) stage_count = 0;
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
