@@ -52,7 +52,7 @@ extern "C" {
 #define SGA_D_LATENT 512    /* compressed KV latent = value width */
 #define SGA_D_ROPE 64       /* shared RoPE key width */
 #define SGA_D_QK 576        /* cached latent row width, absorbed query width */
-#define SGA_MAX_LEN (1 << 20) /* longest visible context a query may have */
+#define SGA_MAX_LEN (1 << 19) /* longest visible context a query may have (512K) */
 #define SGA_MAX_K 65536     /* largest top-k */
 #define SGA_MAX_TOKENS 65535 /* most query tokens in one call */
 

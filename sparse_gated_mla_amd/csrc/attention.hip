@@ -85,14 +85,219 @@ struct TileLoader {
   }
 };
 
+// Online-softmax state of one wave: 16 heads (one per lane column) and their
+// latent-space output o^T[d][head], d = 16*db + 4*(lane/16) + r.
+struct HeadState {
+  float m_run, l_run;
+  f32x4 o[32];
+};
+
+__device__ __forceinline__ void init_state(HeadState& st) {
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 32; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// Attends the wave's 16 heads over one staged 32-row tile (bf16 rows of
+// kRowStride elements). rscale[r] is the row's scale (fp8), 1 (bf16), or
+// negative for a skipped row.
+template <bool kFp8>
+__device__ __forceinline__ void attend_tile(const uint16_t* __restrict__ tile,
+                                            const float* __restrict__ rscale, HeadState& st,
+                                            const u32x4 (&qb)[18], float zscale, int lane) {
+  const int n16 = lane & 15, g = lane >> 4;
+  // logits^T for rows 16b + 4g + r
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint16_t* rowp = tile + (16 * b + n16) * kRowStride + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 18; ++s) {
+      u32x4 av = *reinterpret_cast<const u32x4*>(rowp + 32 * s);
+      acc[b] = mfma16x16x32(av, qb[s], acc[b]);
+    }
+  }
+  float z[2][4], rsc[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rs = rscale[16 * b + 4 * g + r];
+      rsc[b][r] = rs;
+      float v = acc[b][r] * zscale;
+      if constexpr (kFp8) v *= rs;
+      z[b][r] = rs < 0.0f ? -INFINITY : v;
+      tmax = fmaxf(tmax, z[b][r]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(st.m_run, tmax);
+  const float alpha = (st.m_run == -INFINITY) ? (m_new == -INFINITY ? 1.0f : 0.0f)
+                                              : __builtin_amdgcn_exp2f(st.m_run - m_new);
+  float p[2][4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float e = (z[b][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[b][r] - m_new);
+      psum += e;
+      if constexpr (kFp8) e *= fmaxf(rsc[b][r], 0.0f);
+      p[b][r] = e;
+    }
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int db = 0; db < 32; ++db) st.o[db] *= alpha;
+  }
+  // probabilities as bf16 hi/lo B operands: k-slot 8g+i <-> row 4g+i (i<4), 16+4g+i-4
+  uint32_t hi_b[8], lo_b[8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t h = f32_to_bf16_rne(p[b][r]);
+      float rem = p[b][r] - __uint_as_float(h << 16);
+      hi_b[4 * b + r] = h;
+      lo_b[4 * b + r] = f32_to_bf16_rne(rem);
+    }
+  const u32x4 phi = {hi_b[0] | (hi_b[1] << 16), hi_b[2] | (hi_b[3] << 16),
+                     hi_b[4] | (hi_b[5] << 16), hi_b[6] | (hi_b[7] << 16)};
+  const u32x4 plo = {lo_b[0] | (lo_b[1] << 16), lo_b[2] | (lo_b[3] << 16),
+                     lo_b[4] | (lo_b[5] << 16), lo_b[6] | (lo_b[7] << 16)};
+  // transposed reads: lane s reads row 4(s/16) + (s%16)/4 [+16], columns 4(s%4) .. +3
+  // of each 16-column block
+  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_col = 4 * (lane & 3);
+  const uint16_t* tr0 = tile + tr_row * kRowStride + tr_col;
+  const uint16_t* tr1 = tr0 + 16 * kRowStride;
+#pragma unroll
+  for (int db = 0; db < 32; ++db) {
+    s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr0 + 16 * db));
+    s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr1 + 16 * db));
+    u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+    const u32x4 vt = {w0.x, w0.y, w1.x, w1.y};
+    st.o[db] = mfma16x16x32(vt, phi, st.o[db]);
+    st.o[db] = mfma16x16x32(vt, plo, st.o[db]);
+  }
+}
+
+// Writes a wave's result: the gated, normalised output when the token has one
+// split, else the unnormalised partial plus (m, l).
+__device__ __forceinline__ void finish(const AttnArgs& a, HeadState& st, int t, int split,
+                                       int head, int lane) {
+  const int g = lane >> 4;
+  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const int64_t th = (int64_t)t * kHeads + head;
+  if (a.splits == 1) {
+    const float gs = gate_factor(a.gate, th);
+    const float inv = l_tot > 0.0f ? gs / l_tot : 0.0f;
+    float* dst = a.out + th * kDLatent + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db] * inv;
+    if (a.lse && g == 0) a.lse[th] = l_tot > 0.0f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t ps = ((int64_t)t * a.splits + split) * kHeads + head;
+    float* dst = a.part_o + ps * kDLatent + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db];
+    if (g == 0) {
+      a.part_ml[2 * ps] = st.m_run;
+      a.part_ml[2 * ps + 1] = l_tot;
+    }
+  }
+}
+
+__device__ __forceinline__ void load_query(const AttnArgs& a, int t, int head, int lane,
+                                           u32x4 (&qb)[18]) {
+  const int g = lane >> 4;
+  const uint16_t* q = a.q_abs + ((int64_t)t * kHeads + head) * kDQK;
+#pragma unroll
+  for (int s = 0; s < 18; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g);
+}
+
+// bf16 rows, staged straight from HBM into LDS: a workgroup issues every load
+// of up to kSuperRows rows at once (buffer_load ... lds), waits once, then
+// attends the staged tiles. LDS row r of tile i starts at 16-byte unit
+// 73*r of the tile's region (72 units of data + 1 of padding).
+constexpr int kSuperTiles = 4;
+constexpr int kSuperRows = kSuperTiles * kAttnTileRows;      // 128
+constexpr int kUnitsPerRow = kRowStride * 2 / 16;            // 73
+constexpr int kTileLoads = (kAttnTileRows * kUnitsPerRow + 63) / 64;  // 37 wave loads
+constexpr int kTileRegion = kTileLoads * 64 * 16;            // 37888 B
+
+__global__ __launch_bounds__(kThreads) void attn_bf16_direct_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kSuperTiles * kTileRegion];
+  __shared__ int32_t lds_idx[kSuperRows];
+  __shared__ float lds_rscale[kSuperRows];
+  const int t = blockIdx.y, split = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int head = 16 * wave + (lane & 15);
+  int64_t base;
+  int n;
+  a.batch.token(t, base, n);
+  const int32_t* idx_row = a.indices + (int64_t)t * a.k;
+  const int j_begin = split * a.rows_per_split;
+  const int j_end = min(a.k, j_begin + a.rows_per_split);
+
+  u32x4 qb[18];
+  load_query(a, t, head, lane, qb);
+  HeadState st;
+  init_state(st);
+  const float zscale = a.sm_scale * kLog2e;
+  // rows of this token's sequence; out-of-range offsets read as zeros
+  const uint32_t seq_bytes = (uint32_t)max(n, 0) * (2u * kDQK);
+  const __amdgpu_buffer_rsrc_t rows = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.kv + base * 2 * kDQK), (short)0, (int)seq_bytes, 0x00020000);
+
+  for (int j0 = j_begin; j0 < j_end; j0 += kSuperRows) {
+    const int nrows = min(kSuperRows, j_end - j0);
+    const int ntiles = (nrows + kAttnTileRows - 1) / kAttnTileRows;
+    __syncthreads();  // the previous super-tile is fully consumed
+    if (threadIdx.x < kSuperRows) {
+      const int j = j0 + threadIdx.x;
+      const int idx = j < j_end ? idx_row[j] : -1;
+      const bool ok = idx >= 0 && idx < n;
+      lds_idx[threadIdx.x] = ok ? idx : -1;
+      lds_rscale[threadIdx.x] = ok ? 1.0f : -1.0f;
+    }
+    __syncthreads();
+    for (int i = 0; i < ntiles; ++i) {
+      for (int l = wave; l < kTileLoads; l += kThreads / 64) {
+        const int u = l * 64 + lane;
+        const int r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+        int off = (int)seq_bytes;  // out of range: zeros
+        if (r < kAttnTileRows && c < kUnitsPerRow - 1) {
+          const int idx = lds_idx[i * kAttnTileRows + r];
+          if (idx >= 0) off = idx * (2 * kDQK) + c * 16;
+        }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rows, (__attribute__((address_space(3))) void*)(lds + i * kTileRegion + l * 1024), 16,
+            off, 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int i = 0; i < ntiles; ++i)
+      attend_tile<false>(reinterpret_cast<const uint16_t*>(lds + i * kTileRegion),
+                         lds_rscale + i * kAttnTileRows, st, qb, zscale, lane);
+  }
+  finish(a, st, t, split, head, lane);
+}
+
+// Rows staged through registers one tile ahead (fp8 rows are widened to bf16
+// on the way into LDS).
 template <bool kFp8>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds_kv[kAttnTileRows * kRowStride];
   __shared__ float lds_rscale[kAttnTileRows];   // row scale, or -1 for a skipped row
   const int t = blockIdx.y, split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int n16 = lane & 15, g = lane >> 4;
-  const int head = 16 * wave + n16;
+  const int head = 16 * wave + (lane & 15);
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -102,26 +307,14 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int j_end = min(a.k, j_begin + a.rows_per_split);
   const int ntiles = j_end > j_begin ? (j_end - j_begin + kAttnTileRows - 1) / kAttnTileRows : 0;
 
-  // absorbed query as the B operand: qb[s] = q[head][32s + 8g .. +7]
   u32x4 qb[18];
-  const uint16_t* q = a.q_abs + ((int64_t)t * kHeads + head) * kDQK;
-#pragma unroll
-  for (int s = 0; s < 18; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s + 8 * g);
-
+  load_query(a, t, head, lane, qb);
+  HeadState st;
+  init_state(st);
   const float zscale = a.sm_scale * kLog2e;
-  float m_run = -INFINITY, l_run = 0.0f;
-  f32x4 o[32];
-#pragma unroll
-  for (int db = 0; db < 32; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   TileLoader<kFp8> ld;
   if (ntiles > 0) ld.load(a, idx_row, j_begin, j_end, base, n);
-
-  // transposed-read addresses: lane s reads row (4(s/16) + (s%16)/4) [+16],
-  // columns 4(s%4) .. +3 of each 16-column block
-  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
-  const int tr_col = 4 * (lane & 3);
-
   for (int tile = 0; tile < ntiles; ++tile) {
     const int jt = j_begin + tile * kAttnTileRows;
     __syncthreads();  // previous tile fully consumed
@@ -135,124 +328,44 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     }
     __syncthreads();
     if (tile + 1 < ntiles) ld.load(a, idx_row, jt + kAttnTileRows, j_end, base, n);
-
-    // logits^T for rows 16b + 4g + r
-    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const uint16_t* rowp = lds_kv + (16 * b + n16) * kRowStride + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 18; ++s) {
-        u32x4 av = *reinterpret_cast<const u32x4*>(rowp + 32 * s);
-        acc[b] = mfma16x16x32(av, qb[s], acc[b]);
-      }
-    }
-    float z[2][4], rsc[2][4];
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float rs = lds_rscale[16 * b + 4 * g + r];
-        rsc[b][r] = rs;
-        float v = acc[b][r] * zscale;
-        if constexpr (kFp8) v *= rs;
-        z[b][r] = rs < 0.0f ? -INFINITY : v;
-        tmax = fmaxf(tmax, z[b][r]);
-      }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_run == -INFINITY) ? (m_new == -INFINITY ? 1.0f : 0.0f)
-                                             : __builtin_amdgcn_exp2f(m_run - m_new);
-    float p[2][4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float e = (z[b][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[b][r] - m_new);
-        psum += e;
-        if constexpr (kFp8) e *= fmaxf(rsc[b][r], 0.0f);
-        p[b][r] = e;
-      }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int db = 0; db < 32; ++db) o[db] *= alpha;
-    }
-    // probabilities as bf16 hi/lo B operands: k-slot 8g+i <-> row 4g+i (i<4), 16+4g+i-4
-    uint32_t hi_b[8], lo_b[8];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        uint32_t h = f32_to_bf16_rne(p[b][r]);
-        float rem = p[b][r] - __uint_as_float(h << 16);
-        hi_b[4 * b + r] = h;
-        lo_b[4 * b + r] = f32_to_bf16_rne(rem);
-      }
-    const u32x4 phi = {hi_b[0] | (hi_b[1] << 16), hi_b[2] | (hi_b[3] << 16),
-                       hi_b[4] | (hi_b[5] << 16), hi_b[6] | (hi_b[7] << 16)};
-    const u32x4 plo = {lo_b[0] | (lo_b[1] << 16), lo_b[2] | (lo_b[3] << 16),
-                       lo_b[4] | (lo_b[5] << 16), lo_b[6] | (lo_b[7] << 16)};
-    const uint16_t* tr0 = lds_kv + tr_row * kRowStride + tr_col;
-    const uint16_t* tr1 = tr0 + 16 * kRowStride;
-#pragma unroll
-    for (int db = 0; db < 32; ++db) {
-      s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr0 + 16 * db));
-      s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr1 + 16 * db));
-      u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
-      const u32x4 vt = {w0.x, w0.y, w1.x, w1.y};
-      o[db] = mfma16x16x32(vt, phi, o[db]);
-      o[db] = mfma16x16x32(vt, plo, o[db]);
-    }
+    attend_tile<kFp8>(lds_kv, lds_rscale, st, qb, zscale, lane);
   }
-
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const int64_t th = (int64_t)t * kHeads + head;
-  if (a.splits == 1) {
-    const float gs = gate_factor(a.gate, th);
-    const float inv = l_tot > 0.0f ? gs / l_tot : 0.0f;
-    float* dst = a.out + th * kDLatent + 4 * g;
-#pragma unroll
-    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db] * inv;
-    if (a.lse && g == 0) a.lse[th] = l_tot > 0.0f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
-  } else {
-    const int64_t ps = ((int64_t)t * a.splits + split) * kHeads + head;
-    float* dst = a.part_o + ps * kDLatent + 4 * g;
-#pragma unroll
-    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = o[db];
-    if (g == 0) {
-      a.part_ml[2 * ps] = m_run;
-      a.part_ml[2 * ps + 1] = l_tot;
-    }
-  }
+  finish(a, st, t, split, head, lane);
 }
 
 // Merges the split partials of one (token, head) by log-sum-exp, then gates.
 // One workgroup of 128 threads per (head, token); each thread owns 4 columns.
+constexpr int kMaxCombine = 64;
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
+  __shared__ float wgt[kMaxCombine];
+  __shared__ float tot[2];
   const int h = blockIdx.x, t = blockIdx.y;
   const int S = a.splits;
   const int64_t th = (int64_t)t * kHeads + h;
   const float* ml = a.part_ml + 2 * ((int64_t)t * S * kHeads + h);   // stride 2*kHeads per split
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * kHeads * s]);
-  float L = 0.0f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (M != -INFINITY) {
-    const float* po = a.part_o + ((int64_t)t * S * kHeads + h) * kDLatent + 4 * threadIdx.x;
-    for (int s = 0; s < S; ++s) {
-      const float ms = ml[2 * kHeads * s];
-      if (ms == -INFINITY) continue;
-      const float wgt = __builtin_amdgcn_exp2f(ms - M);
-      L += ml[2 * kHeads * s + 1] * wgt;
-      acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * wgt;
-    }
+  if (threadIdx.x < 64) {
+    const int s = threadIdx.x;
+    const float ms = s < S ? ml[2 * kHeads * s] : -INFINITY;
+    const float ls = s < S ? ml[2 * kHeads * s + 1] : 0.0f;
+    const float M = wave_max(ms);
+    const float w = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+    const float L = wave_sum(ls * w);
+    if (s < S) wgt[s] = w;
+    if (s == 0) { tot[0] = M; tot[1] = L; }
   }
+  __syncthreads();
+  const float M = tot[0], L = tot[1];
+  const float* po = a.part_o + ((int64_t)t * S * kHeads + h) * kDLatent + 4 * threadIdx.x;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 4 <= S; s += 4) {
+    f32x4 v0 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 0) * kHeads * kDLatent);
+    f32x4 v1 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 1) * kHeads * kDLatent);
+    f32x4 v2 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 2) * kHeads * kDLatent);
+    f32x4 v3 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 3) * kHeads * kDLatent);
+    acc += v0 * wgt[s] + v1 * wgt[s + 1] + v2 * wgt[s + 2] + v3 * wgt[s + 3];
+  }
+  for (; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * wgt[s];
   const float gs = gate_factor(a.gate, th);
   const float inv = L > 0.0f ? gs / L : 0.0f;
   *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 4 * threadIdx.x) = acc * inv;
@@ -265,7 +378,7 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid(a.splits, a.num_tokens);
   if (fp8) attn_kernel<true><<<grid, kThreads, 0, s>>>(a);
-  else attn_kernel<false><<<grid, kThreads, 0, s>>>(a);
+  else attn_bf16_direct_kernel<<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

@@ -16,6 +16,7 @@ using sga::TopkArgs;
 using sga::TopkCtrl;
 
 constexpr size_t kAlign = 256;
+constexpr int kTokenTopkMinTokens = 512;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -41,6 +42,7 @@ struct TopkLayout {
   TopkCtrl* ctrl;
   uint32_t* sel;
   uint32_t* cand;
+  uint32_t* cand_key;
   int64_t words, cand_cap;
   size_t clear_words;  // hist + ctrl are contiguous and cleared per call
 };
@@ -59,6 +61,7 @@ TopkLayout carve_topk(Carver& c, int32_t T, int32_t max_len) {
   L.clear_words = (hist_bytes + ctrl_bytes) / sizeof(uint32_t);
   L.sel = c.take<uint32_t>((size_t)T * L.words);
   L.cand = c.take<uint32_t>((size_t)T * L.cand_cap);
+  L.cand_key = c.take<uint32_t>((size_t)T * L.cand_cap);
   return L;
 }
 
@@ -72,6 +75,7 @@ AttnPlan plan_attention(int32_t T, int32_t k) {
   const int tiles = (k + tile - 1) / tile;
   int want = (T > 0) ? (256 + T - 1) / T : 1;   // aim for about 256 workgroups
   int max_splits = tiles / 4 > 0 ? tiles / 4 : 1;  // at least 4 tiles per split
+  if (max_splits > 64) max_splits = 64;          // the combine merges at most 64 partials
   int splits = want < max_splits ? want : max_splits;
   if (splits < 1) splits = 1;
   int tiles_per = (tiles + splits - 1) / splits;
@@ -154,13 +158,22 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
   a.sel = L.sel;
   a.words = L.words;
   a.cand = L.cand;
+  a.cand_key = L.cand_key;
   a.cand_cap = L.cand_cap;
   if (!hist_ready) {
     SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
     SGA_HIP(sga::launch_topk_hist(a, stream));
   }
-  SGA_HIP(sga::launch_topk_select(a, stream));
-  SGA_HIP(sga::launch_topk_finalize(a, stream));
+  // one workgroup per token only when the batch alone fills the GPU
+  const int token_cap = batch->num_tokens >= kTokenTopkMinTokens ? sga::topk_token_lds_cap(L.words) : 0;
+  if (token_cap > 0) {
+    a.lds_cand_cap = token_cap;
+    SGA_HIP(sga::launch_topk_token(a, stream));
+  } else {
+    a.lds_cand_cap = sga::topk_finalize_lds_cap(L.words);
+    SGA_HIP(sga::launch_topk_select(a, stream));
+    SGA_HIP(sga::launch_topk_finalize(a, stream));
+  }
   return SGA_OK;
 }
 

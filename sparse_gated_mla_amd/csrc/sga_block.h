@@ -38,19 +38,21 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratc
 
 // Radix cut over a histogram h[0..nbins) in LDS, digits ranked from the top:
 // finds d with S(d+1) < r <= S(d), S(d) = sum of h[b] for b >= d, 1 <= r <= S(0).
-// Writes res[0] = d and res[1] = S(d+1). nbins must be a multiple of NT.
+// Writes res[0] = d and res[1] = S(d+1). Thread j owns a run of bins from the
+// top; with fewer bins than threads the last threads own none.
 template <int NT>
 __device__ __forceinline__ void block_find_cut(const uint32_t* h, int nbins, uint32_t r,
                                                uint32_t* scratch, uint32_t* res) {
-  const int per = nbins / NT;
+  const int per = (nbins + NT - 1) / NT;
   const int top = nbins - (int)threadIdx.x * per;
+  const int cnt = top <= 0 ? 0 : (top < per ? top : per);
   uint32_t sum = 0;
-  for (int i = 1; i <= per; ++i) sum += h[top - i];
+  for (int i = 1; i <= cnt; ++i) sum += h[top - i];
   uint32_t total;
   uint32_t above = block_excl_scan<NT>(sum, scratch, &total);
   if (above < r && r <= above + sum) {
     uint32_t acc = above;
-    for (int i = 1; i <= per; ++i) {
+    for (int i = 1; i <= cnt; ++i) {
       uint32_t c = h[top - i];
       if (acc + c >= r) {
         res[0] = (uint32_t)(top - i);
@@ -87,7 +89,12 @@ __device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* 
 template <int NT>
 __device__ __forceinline__ void hist1_cut(const uint32_t* ghist, uint32_t* lds_hist, uint32_t k,
                                           uint32_t* scratch, uint32_t& digit1, uint32_t& above1) {
-  for (int b = threadIdx.x; b < kHist1; b += NT) lds_hist[b] = ghist[b];
+  static_assert(kHist1 % NT == 0, "whole bins per thread");
+  uint32_t h[kHist1 / NT];   // every load in flight before the first LDS store
+#pragma unroll
+  for (int u = 0; u < kHist1 / NT; ++u) h[u] = ghist[u * NT + threadIdx.x];
+#pragma unroll
+  for (int u = 0; u < kHist1 / NT; ++u) lds_hist[u * NT + threadIdx.x] = h[u];
   __syncthreads();
   uint32_t* res = scratch + NT / 64 + 1;
   block_find_cut<NT>(lds_hist, kHist1, k, scratch, res);

@@ -70,10 +70,13 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-constexpr int kDigit1Bits = 11;  // key bits 31..21
-constexpr int kDigit2Bits = 11;  // key bits 20..10
-constexpr int kDigit3Bits = 10;  // key bits 9..0
+// Radix digits of the select: 12 + 12 + 8 key bits.
+constexpr int kDigit1Bits = 12;  // key bits 31..20
+constexpr int kDigit2Bits = 12;  // key bits 19..8
+constexpr int kDigit3Bits = 8;   // key bits 7..0
 constexpr int kHist1 = 1 << kDigit1Bits;
+constexpr int kHist2 = 1 << kDigit2Bits;
+constexpr int kHist3 = 1 << kDigit3Bits;
 
 // ---------------------------------------------------------------- visibility
 // Visible rows of a token, clamped so inconsistent metadata never leaves the

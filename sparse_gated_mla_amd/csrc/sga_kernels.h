@@ -46,8 +46,10 @@ struct TopkArgs {
   TopkCtrl* ctrl;          // [T]
   uint32_t* sel;           // [T,words]
   int64_t words;           // bitmap words per token
-  uint32_t* cand;          // [T,cand_cap]
+  uint32_t* cand;          // [T,cand_cap] candidate positions
+  uint32_t* cand_key;      // [T,cand_cap] their radix keys
   int64_t cand_cap;
+  int lds_cand_cap;        // candidates the finalize kernel can stage in LDS
 };
 
 struct AttnArgs {
@@ -71,9 +73,14 @@ struct AttnArgs {
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
+hipError_t launch_topk_cut(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);
-size_t topk_finalize_lds_bytes(int64_t words);
+constexpr size_t kFinalizeLds = 160 * 1024;  // dynamic LDS of the finalize kernels
+constexpr int64_t kMaxTokenWords = 8192;     // bitmap words for the one-kernel top-k (256K)
+int topk_finalize_lds_cap(int64_t words);
+int topk_token_lds_cap(int64_t words);       // 0: use the multi-kernel top-k
+hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s);
 

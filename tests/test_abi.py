@@ -73,7 +73,7 @@ def test_index_scores_rejects_bad_arguments(lib):
     assert call(b, dt=7) == 2                  # unknown dtype
     assert call(_batch(T=-1)) == 1
     assert call(_batch(B=0)) == 1
-    assert call(_batch(max_len=(1 << 20) + 1)) == 2
+    assert call(_batch(max_len=(1 << 19) + 1)) == 2
     assert call(_batch(ptr=0)) == 1            # null metadata
     bad = _batch()
     bad.reserved = 3

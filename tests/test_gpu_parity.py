@@ -181,3 +181,23 @@ def test_repeat_calls_are_deterministic():
     b = dev.forward()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_all_equal_scores_spill_past_lds():
+    # 50000 tied candidates: more than the one-kernel top-k keeps in LDS
+    wl = si.build("equal_spill", [50000], [(0, 49999), (0, 30000)], seed=14)
+    wl.q_idx.zero_()
+    _, (idx, _, _), _ = _check_forward(wl)
+    assert idx.cpu().numpy()[1].tolist() == list(range(2048))
+
+
+def test_context_beyond_256k_multikernel_topk():
+    # above 256K positions the top-k runs as cut / select / finalize kernels
+    wl = si.build("len300k", [300000, 5000], [(0, 299999), (1, 4999), (0, 262144)], seed=15)
+    _check_forward(wl)
+
+
+def test_longest_supported_context():
+    # 512K positions: the largest visible context the library accepts
+    wl = si.build("len512k", [1 << 19], [(0, (1 << 19) - 1), (0, 70000)], seed=16)
+    _check_forward(wl)
