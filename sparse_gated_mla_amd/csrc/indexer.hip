@@ -35,35 +35,51 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;
+constexpr int kStages = 3;   // key tiles in flight per wave
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
+constexpr int kNonTemporal = 2;         // cache-policy bit: streaming (read-once) data
 
 // A buffer resource over [p, p + bytes): loads past the end return zeros.
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
 }
 
+// A wave's key tile: 32 rows of one 128-row group of the chunk. The four
+// waves share each group: load step s of wave w reads the 1 KiB block
+// 4s + w of the group, so the four waves' loads of one step are adjacent and
+// the workgroup streams through contiguous memory. Tile row r (the MFMA
+// column) is group row (r / kRowsPerLoad) * 4 * kRowsPerLoad + w * kRowsPerLoad
+// + r % kRowsPerLoad.
 template <bool kFp8>
 struct KeyTile {
-  // bf16 tile: 32 rows x 256 B = 8 loads of 1 KiB; load s, lane l -> row 4s + l/16,
-  //   16-byte chunk l%16.
-  // fp8 tile:  32 rows x 128 B = 4 loads of 1 KiB; load s, lane l -> row 8s + l/8,
-  //   chunk l%8; plus the fp32 scale of row l%32.
+  // bf16 tile: 8 loads of 1 KiB (4 rows of 256 B each); load s, lane l -> tile
+  //   row 4s + l/16, 16-byte chunk l%16.
+  // fp8 tile:  4 loads of 1 KiB (8 rows of 128 B each); load s, lane l -> tile
+  //   row 8s + l/8, chunk l%8; plus the fp32 scale of tile row l%32.
   static constexpr int kLoads = kFp8 ? 4 : 8;
   static constexpr int kRowBytes = kFp8 ? 128 : 256;
+  static constexpr int kRowsPerLoad = 1024 / kRowBytes;
+  static constexpr int kGroupRows = kWaves * kTile;
   u32x4 v[kLoads];
   float scale;
 
-  // Loads tile `tile` of the workgroup's chunk. Rows past the chunk read as zeros.
-  __device__ __forceinline__ void load(rsrc_t keys, rsrc_t scales, int tile, int lane) {
-    const int off = tile * kTile * kRowBytes + lane * 16;
+  // chunk position of tile row r of wave w in group grp
+  static __device__ __forceinline__ int position(int grp, int w, int r) {
+    return grp * kGroupRows + (r / kRowsPerLoad) * (kWaves * kRowsPerLoad) + w * kRowsPerLoad +
+           r % kRowsPerLoad;
+  }
+
+  // Loads this wave's tile of group grp. Rows past the chunk read as zeros.
+  __device__ __forceinline__ void load(rsrc_t keys, rsrc_t scales, int grp, int w, int lane) {
+    const int off = grp * kGroupRows * kRowBytes + w * 1024 + lane * 16;
 #pragma unroll
     for (int s = 0; s < kLoads; ++s)
-      v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off + s * 1024, 0, 0));
+      v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off + s * kWaves * 1024, 0, kNonTemporal));
     if constexpr (kFp8)
       scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            scales, (tile * kTile + (lane & 31)) * 4, 0, 0));
+                                            scales, position(grp, w, lane & 31) * 4, 0, 0));
     // keep each tile's loads together and in program order, so the wait for
     // one tile never covers the loads of the tile issued after it
     __builtin_amdgcn_sched_barrier(0);
@@ -105,10 +121,12 @@ struct KeyTile {
 };
 
 // Scores one staged tile: writes each position's score into lds_scores.
+// lds_w holds the token's 64 head weights; each lane reads the 32 that match
+// its accumulator rows (4 consecutive heads per b128 read).
 template <bool kFp8>
 __device__ __forceinline__ void score_tile(const uint8_t* lds, float kscale, int lane,
-                                           const u32x4 (&qa)[2][8], const float (&wr)[2][16],
-                                           int tile, float* lds_scores) {
+                                           const u32x4 (&qa)[2][8], const float* lds_w,
+                                           int grp, int w, float* lds_scores) {
   u32x4 b[8];
   KeyTile<kFp8>::operands(lds, lane, b);
   f32x16 acc0 = {}, acc1 = {};
@@ -117,16 +135,23 @@ __device__ __forceinline__ void score_tile(const uint8_t* lds, float kscale, int
     acc0 = mfma32x32x16(qa[0][s], b[s], acc0);
     acc1 = mfma32x32x16(qa[1][s], b[s], acc1);
   }
+  const int g = lane >> 5;
   float sc = 0.0f;
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    float d0 = acc0[r], d1 = acc1[r];
-    if constexpr (kFp8) { d0 *= kscale; d1 *= kscale; }
-    sc = fmaf(wr[0][r], fmaxf(d0, 0.0f), sc);
-    sc = fmaf(wr[1][r], fmaxf(d1, 0.0f), sc);
+  for (int q = 0; q < 4; ++q) {
+    // accumulator rows 4q..4q+3 of block mb are heads 32mb + 8q + 4g + 0..3
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(lds_w + 8 * q + 4 * g);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(lds_w + 32 + 8 * q + 4 * g);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float d0 = acc0[4 * q + j], d1 = acc1[4 * q + j];
+      if constexpr (kFp8) { d0 *= kscale; d1 *= kscale; }
+      sc = fmaf(w0[j], fmaxf(d0, 0.0f), sc);
+      sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
+    }
   }
   sc += __shfl_xor(sc, 32);
-  if (lane < 32) lds_scores[tile * kTile + lane] = sc;
+  if (lane < 32) lds_scores[KeyTile<kFp8>::position(grp, w, lane)] = sc;
 }
 
 template <bool kFp8, bool kHist>
@@ -134,6 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   constexpr int kTileBytes = KeyTile<kFp8>::kRowBytes * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
   __shared__ float lds_scores[kIndexerChunk];
+  __shared__ __attribute__((aligned(16))) float lds_w[kIdxHeads];
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -145,6 +171,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   if constexpr (kHist) {
     for (int b = threadIdx.x; b < kHist1; b += kThreads) lds_hist[b] = 0;
   }
+  if (threadIdx.x < kIdxHeads) lds_w[threadIdx.x] = a.w[(int64_t)t * kIdxHeads + threadIdx.x];
+  __syncthreads();
 
   const int chunk0 = blockIdx.x * kIndexerChunk;
   const int len = min(n - chunk0, kIndexerChunk);   // positions of this chunk (<= 0: none)
@@ -158,36 +186,26 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         qa[mb][s] = *reinterpret_cast<const u32x4*>(q + (32 * mb + nidx) * kIdxDim + 64 * g + 8 * s);
-    // head weights matching the accumulator rows held by this lane
-    float wr[2][16];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        wr[mb][r] = a.w[(int64_t)t * kIdxHeads + 32 * mb + 8 * (r / 4) + 4 * g + (r % 4)];
 
     const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * KeyTile<kFp8>::kRowBytes,
                                   (uint32_t)len * KeyTile<kFp8>::kRowBytes);
     const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + base + chunk0) : (const void*)a.k_idx,
                                     kFp8 ? (uint32_t)len * 4u : 0u);
-    const int ntiles = (len + kTile - 1) / kTile;
-    const int mine = ntiles > wave ? (ntiles - wave + kWaves - 1) / kWaves : 0;
+    const int ngroups = (len + KeyTile<kFp8>::kGroupRows - 1) / KeyTile<kFp8>::kGroupRows;
 
-    // this wave's tiles: wave, wave + 4, ...; two in flight. Loads are never
-    // skipped (past the chunk they read zeros), so each wait is exact.
-    KeyTile<kFp8> s0, s1;
-    s0.load(keys, scales, wave, lane);
-    s1.load(keys, scales, wave + kWaves, lane);
-    for (int i = 0; i < mine; i += 2) {
-      const int t0 = wave + i * kWaves;
-      s0.store(lds, lane);
-      const float sc0 = s0.scale;
-      s0.load(keys, scales, t0 + 2 * kWaves, lane);
-      score_tile<kFp8>(lds, sc0, lane, qa, wr, t0, lds_scores);
-      s1.store(lds, lane);
-      const float sc1 = s1.scale;
-      s1.load(keys, scales, t0 + 3 * kWaves, lane);
-      if (i + 1 < mine) score_tile<kFp8>(lds, sc1, lane, qa, wr, t0 + kWaves, lds_scores);
+    // this wave's tile of every group; kStages groups in flight. Loads are
+    // never skipped (past the chunk they read zeros), so each wait is exact.
+    KeyTile<kFp8> st[kStages];
+#pragma unroll
+    for (int j = 0; j < kStages; ++j) st[j].load(keys, scales, j, wave, lane);
+    for (int i = 0; i < ngroups; i += kStages) {
+#pragma unroll
+      for (int j = 0; j < kStages; ++j) {
+        st[j].store(lds, lane);
+        const float ks = st[j].scale;
+        st[j].load(keys, scales, i + j + kStages, wave, lane);
+        if (i + j < ngroups) score_tile<kFp8>(lds, ks, lane, qa, lds_w, i + j, wave, lds_scores);
+      }
     }
   }
   __syncthreads();
