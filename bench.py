@@ -46,11 +46,17 @@ INDEXER_SRC = os.path.join(ROOT, "sparse_gated_mla_amd", "csrc", "indexer.hip")
 
 # ---------------------------------------------------------------- HIP events
 class HipEvents:
-    """hipEventCreate / hipEventElapsedTime through libamdhip64 (raw handles for sga_trace)."""
+    """Timing-only HIP events through libamdhip64 (raw handles for sga_trace).
+
+    They are created with hipEventDisableSystemFence, so recording one between
+    two kernels adds no system-scope cache writeback: the timed kernels run as
+    they would untraced."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
         self.hip = ctypes.CDLL("libamdhip64.so")
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
@@ -58,9 +64,9 @@ class HipEvents:
 
     def create(self) -> ctypes.c_void_p:
         e = ctypes.c_void_p()
-        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
         if rc != 0:
-            raise RuntimeError(f"hipEventCreate failed: {rc}")
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
         self.events.append(e)
         return e
 

@@ -30,6 +30,7 @@ constexpr int kThreads = 256;
 constexpr int kRowStride = kDQK + 8;  // bf16 elements per LDS row (1168 B)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kNonTemporal = 2;   // cache-policy bit: rows are read once per token
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -201,13 +202,15 @@ __device__ __forceinline__ void finish(const AttnArgs& a, HeadState& st, int t, 
     for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db] * inv;
     if (a.lse && g == 0) a.lse[th] = l_tot > 0.0f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    const int64_t ps = ((int64_t)t * a.splits + split) * kHeads + head;
-    float* dst = a.part_o + ps * kDLatent + 4 * g;
+    // partial layout [token][split][column block db][head][16 columns]: for one
+    // db the wave stores one contiguous 1 KiB block
+    const int64_t ts = (int64_t)t * a.splits + split;
+    float* dst = a.part_o + ts * kHeads * kDLatent + head * 16 + 4 * g;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db];
+    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + db * (kHeads * 16)) = st.o[db];
     if (g == 0) {
-      a.part_ml[2 * ps] = st.m_run;
-      a.part_ml[2 * ps + 1] = l_tot;
+      a.part_ml[2 * (ts * kHeads + head)] = st.m_run;
+      a.part_ml[2 * (ts * kHeads + head) + 1] = l_tot;
     }
   }
 }
@@ -267,17 +270,28 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_direct_kernel(AttnArgs a) 
     }
     __syncthreads();
     for (int i = 0; i < ntiles; ++i) {
-      for (int l = wave; l < kTileLoads; l += kThreads / 64) {
+      // offsets of this wave's loads first (LDS index reads batched), then the loads
+      constexpr int kPerWave = (kTileLoads + kThreads / 64 - 1) / (kThreads / 64);
+      int offs[kPerWave];
+#pragma unroll
+      for (int q = 0; q < kPerWave; ++q) {
+        const int l = wave + q * (kThreads / 64);
         const int u = l * 64 + lane;
         const int r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
         int off = (int)seq_bytes;  // out of range: zeros
-        if (r < kAttnTileRows && c < kUnitsPerRow - 1) {
+        if (l < kTileLoads && r < kAttnTileRows && c < kUnitsPerRow - 1) {
           const int idx = lds_idx[i * kAttnTileRows + r];
           if (idx >= 0) off = idx * (2 * kDQK) + c * 16;
         }
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rows, (__attribute__((address_space(3))) void*)(lds + i * kTileRegion + l * 1024), 16,
-            off, 0, 0, 0);
+        offs[q] = off;
+      }
+#pragma unroll
+      for (int q = 0; q < kPerWave; ++q) {
+        const int l = wave + q * (kThreads / 64);
+        if (l < kTileLoads)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rows, (__attribute__((address_space(3))) void*)(lds + i * kTileRegion + l * 1024), 16,
+              offs[q], 0, 0, kNonTemporal);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
@@ -333,43 +347,47 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   finish(a, st, t, split, head, lane);
 }
 
-// Merges the split partials of one (token, head) by log-sum-exp, then gates.
-// One workgroup of 128 threads per (head, token); each thread owns 4 columns.
+// Merges the split partials by log-sum-exp, then gates. One workgroup per
+// (column block db, token): thread j takes head j/4 and columns
+// 16*db + 4*(j%4) .. +3; for each split it reads one contiguous 4 KiB block.
 constexpr int kMaxCombine = 64;
-__global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
-  __shared__ float wgt[kMaxCombine];
-  __shared__ float tot[2];
-  const int h = blockIdx.x, t = blockIdx.y;
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
+  const int db = blockIdx.x, t = blockIdx.y;
+  const int h = threadIdx.x >> 2, q = threadIdx.x & 3;
   const int S = a.splits;
   const int64_t th = (int64_t)t * kHeads + h;
   const float* ml = a.part_ml + 2 * ((int64_t)t * S * kHeads + h);   // stride 2*kHeads per split
-  if (threadIdx.x < 64) {
-    const int s = threadIdx.x;
-    const float ms = s < S ? ml[2 * kHeads * s] : -INFINITY;
-    const float ls = s < S ? ml[2 * kHeads * s + 1] : 0.0f;
-    const float M = wave_max(ms);
-    const float w = (M == -INFINITY || ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-    const float L = wave_sum(ls * w);
-    if (s < S) wgt[s] = w;
-    if (s == 0) { tot[0] = M; tot[1] = L; }
-  }
-  __syncthreads();
-  const float M = tot[0], L = tot[1];
-  const float* po = a.part_o + ((int64_t)t * S * kHeads + h) * kDLatent + 4 * threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * kHeads * s]);
+  const float* po = a.part_o + (int64_t)t * S * kHeads * kDLatent + db * (kHeads * 16) + h * 16 + 4 * q;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  int s = 0;
-  for (; s + 4 <= S; s += 4) {
-    f32x4 v0 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 0) * kHeads * kDLatent);
-    f32x4 v1 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 1) * kHeads * kDLatent);
-    f32x4 v2 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 2) * kHeads * kDLatent);
-    f32x4 v3 = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + 3) * kHeads * kDLatent);
-    acc += v0 * wgt[s] + v1 * wgt[s + 1] + v2 * wgt[s + 2] + v3 * wgt[s + 3];
+  float L = 0.0f;
+  if (M != -INFINITY) {
+    int s = 0;
+    for (; s + 4 <= S; s += 4) {
+      f32x4 v[4];
+      float wv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + u) * kHeads * kDLatent);
+        const float ms = ml[2 * kHeads * (s + u)];
+        wv[u] = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        L += ml[2 * kHeads * (s + u) + 1] * wv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += v[u] * wv[u];
+    }
+    for (; s < S; ++s) {
+      const float ms = ml[2 * kHeads * s];
+      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+      L += ml[2 * kHeads * s + 1] * w;
+      acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * w;
+    }
   }
-  for (; s < S; ++s) acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * wgt[s];
   const float gs = gate_factor(a.gate, th);
   const float inv = L > 0.0f ? gs / L : 0.0f;
-  *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 4 * threadIdx.x) = acc * inv;
-  if (a.lse && threadIdx.x == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 16 * db + 4 * q) = acc * inv;
+  if (a.lse && db == 0 && q == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -384,7 +402,7 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s) {
 
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s) {
   if (a.num_tokens == 0 || a.splits == 1) return hipSuccess;
-  combine_kernel<<<dim3(kHeads, a.num_tokens), 128, 0, s>>>(a);
+  combine_kernel<<<dim3(kDLatent / 16, a.num_tokens), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
