@@ -34,6 +34,12 @@ constexpr int kNonTemporal = 2;   // cache-policy bit: rows are read once per to
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
+// s_waitcnt immediates that wait only for the vector-memory counter to fall to
+// N (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8
+// left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kVmcntWait[3] = {vmcnt_imm(10), vmcnt_imm(5), vmcnt_imm(0)};
+
 __device__ __forceinline__ float gate_factor(const float* gate, int64_t idx) {
   if (!gate) return 1.0f;
   return 1.0f / (1.0f + expf(-gate[idx]));
@@ -202,15 +208,38 @@ __device__ __forceinline__ void finish(const AttnArgs& a, HeadState& st, int t, 
     for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db] * inv;
     if (a.lse && g == 0) a.lse[th] = l_tot > 0.0f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
   } else {
-    // partial layout [token][split][column block db][head][16 columns]: for one
-    // db the wave stores one contiguous 1 KiB block
-    const int64_t ts = (int64_t)t * a.splits + split;
-    float* dst = a.part_o + ts * kHeads * kDLatent + head * 16 + 4 * g;
+    // The split's output normalised by its exp-sum is a convex combination of
+    // value rows; divided by its largest magnitude it lies in [-1, 1] and is
+    // stored as fp16 (relative rounding 2^-11), with the scale kept in fp32.
+    // Layout [token][split][column block db][head][16 columns]: for one db the
+    // wave stores one contiguous 512-byte block.
+    const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+    float amax = 0.0f;
 #pragma unroll
-    for (int db = 0; db < 32; ++db) *reinterpret_cast<f32x4*>(dst + db * (kHeads * 16)) = st.o[db];
+    for (int db = 0; db < 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(st.o[db][r]));
+    amax = fmaxf(amax, __shfl_xor(amax, 16));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    amax *= inv_l;
+    const float scale = amax > 0.0f ? amax : 1.0f;
+    const float k = inv_l / scale;
+    const int64_t ts = (int64_t)t * a.splits + split;
+    uint16_t* dst = a.part_o + ts * kHeads * kDLatent + head * 16 + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 32; ++db) {
+      const f32x4 v = st.o[db] * k;
+      u32x2 packed;
+      packed.x = pack_f16x2(v[0], v[1]);
+      packed.y = pack_f16x2(v[2], v[3]);
+      *reinterpret_cast<u32x2*>(dst + db * (kHeads * 16)) = packed;
+    }
     if (g == 0) {
-      a.part_ml[2 * (ts * kHeads + head)] = st.m_run;
-      a.part_ml[2 * (ts * kHeads + head) + 1] = l_tot;
+      float* ml = a.part_ml + 4 * (ts * kHeads + head);
+      ml[0] = st.m_run;
+      ml[1] = l_tot;
+      ml[2] = scale;
+      ml[3] = scale;
     }
   }
 }
@@ -303,6 +332,254 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_direct_kernel(AttnArgs a) 
   finish(a, st, t, split, head, lane);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 rows, 8 waves in pairs. Wave w owns heads 16*(w%4) .. +15 and one half
+// h = w/4 of the work:
+//   logits: dims 288h .. 288h+287 (9 of the 18 k-steps); the two waves of a
+//           pair swap their partial logits through LDS and add them (fp32
+//           addition commutes, so both hold identical logits);
+//   output: latent columns 256h .. 256h+255.
+// So each wave holds 9 query k-steps (36 VGPRs) and 16 output blocks (64),
+// two waves run per SIMD, and the LDS traffic and MFMA count per tile are the
+// same as with four whole waves.
+// Rows stream straight from HBM into LDS (buffer_load ... lds): a super-tile
+// of three 32-row tiles is requested at once, and each tile is consumed as
+// soon as its own loads have landed. Every wave issues exactly five 1 KiB
+// loads per tile (units past the 32 rows read zeros into the region's tail),
+// so the per-tile waits are fixed counts.
+constexpr int kPairThreads = 512;
+constexpr int kPairWaves = kPairThreads / 64;
+constexpr int kPairTiles = 3;                                     // tiles per super-tile
+constexpr int kPairRows = kPairTiles * kAttnTileRows;             // 96
+constexpr int kPairLoads = 5;                                     // 1 KiB loads per wave per tile
+constexpr int kPairRegion = kPairWaves * kPairLoads * 1024;       // 40960 B per tile
+static_assert(kPairWaves * kPairLoads * 64 >= kAttnTileRows * kUnitsPerRow, "tile fits its loads");
+
+struct HalfState {
+  float m_run, l_run;
+  f32x4 o[16];
+};
+
+__device__ __forceinline__ void attend_tile_half(const uint16_t* __restrict__ tile,
+                                                 const float* __restrict__ rscale,
+                                                 float* __restrict__ xbuf, HalfState& st,
+                                                 const u32x4 (&qb)[9], float zscale, int lane,
+                                                 int wave, int half) {
+  const int n16 = lane & 15, g = lane >> 4;
+  // partial logits^T over this half's 9 k-steps; two chains per row block
+  f32x4 acc[2][2] = {};
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint16_t* rowp = tile + (16 * b + n16) * kRowStride + 8 * g + 288 * half;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) {
+      u32x4 av = *reinterpret_cast<const u32x4*>(rowp + 32 * s);
+      acc[b][s & 1] = mfma16x16x32(av, qb[s], acc[b][s & 1]);
+    }
+  }
+  f32x4 part0 = acc[0][0] + acc[0][1], part1 = acc[1][0] + acc[1][1];
+  f32x4* mine = reinterpret_cast<f32x4*>(xbuf + (wave * 64 + lane) * 8);
+  mine[0] = part0;
+  mine[1] = part1;
+  __syncthreads();
+  const f32x4* other = reinterpret_cast<const f32x4*>(xbuf + ((wave ^ 4) * 64 + lane) * 8);
+  const f32x4 full[2] = {part0 + other[0], part1 + other[1]};
+
+  float z[2][4];
+  float tmax = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float rs = rscale[16 * b + 4 * g + r];
+      z[b][r] = rs < 0.0f ? -INFINITY : full[b][r] * zscale;
+      tmax = fmaxf(tmax, z[b][r]);
+    }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+  const float m_new = fmaxf(st.m_run, tmax);
+  const float alpha = (st.m_run == -INFINITY) ? (m_new == -INFINITY ? 1.0f : 0.0f)
+                                              : __builtin_amdgcn_exp2f(st.m_run - m_new);
+  float p[2][4];
+  float psum = 0.0f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float e = (z[b][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[b][r] - m_new);
+      psum += e;
+      p[b][r] = e;
+    }
+  st.l_run = st.l_run * alpha + psum;
+  st.m_run = m_new;
+  if (__any(alpha != 1.0f)) {
+#pragma unroll
+    for (int db = 0; db < 16; ++db) st.o[db] *= alpha;
+  }
+  uint32_t hi_b[8], lo_b[8];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t h = f32_to_bf16_rne(p[b][r]);
+      hi_b[4 * b + r] = h;
+      lo_b[4 * b + r] = f32_to_bf16_rne(p[b][r] - __uint_as_float(h << 16));
+    }
+  const u32x4 phi = {hi_b[0] | (hi_b[1] << 16), hi_b[2] | (hi_b[3] << 16),
+                     hi_b[4] | (hi_b[5] << 16), hi_b[6] | (hi_b[7] << 16)};
+  const u32x4 plo = {lo_b[0] | (lo_b[1] << 16), lo_b[2] | (lo_b[3] << 16),
+                     lo_b[4] | (lo_b[5] << 16), lo_b[6] | (lo_b[7] << 16)};
+  const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
+  const int tr_col = 4 * (lane & 3) + 256 * half;
+  const uint16_t* tr0 = tile + tr_row * kRowStride + tr_col;
+  const uint16_t* tr1 = tr0 + 16 * kRowStride;
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+    s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr0 + 16 * db));
+    s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(tr1 + 16 * db));
+    u32x2 w0 = __builtin_bit_cast(u32x2, v0), w1 = __builtin_bit_cast(u32x2, v1);
+    const u32x4 vt = {w0.x, w0.y, w1.x, w1.y};
+    st.o[db] = mfma16x16x32(vt, phi, st.o[db]);
+    st.o[db] = mfma16x16x32(vt, plo, st.o[db]);
+  }
+}
+
+__device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, int t, int split,
+                                            int head, int lane, int half) {
+  const int g = lane >> 4;
+  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const int64_t th = (int64_t)t * kHeads + head;
+  if (a.splits == 1) {
+    const float gs = gate_factor(a.gate, th);
+    const float inv = l_tot > 0.0f ? gs / l_tot : 0.0f;
+    float* dst = a.out + th * kDLatent + 256 * half + 4 * g;
+#pragma unroll
+    for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(dst + 16 * db) = st.o[db] * inv;
+    if (a.lse && g == 0 && half == 0)
+      a.lse[th] = l_tot > 0.0f ? (st.m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    return;
+  }
+  // normalised, scaled fp16 partial (see finish); one scale per half
+  const float inv_l = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+  float amax = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(st.o[db][r]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax *= inv_l;
+  const float scale = amax > 0.0f ? amax : 1.0f;
+  const float k = inv_l / scale;
+  const int64_t ts = (int64_t)t * a.splits + split;
+  uint16_t* dst = a.part_o + ts * kHeads * kDLatent + 16 * half * (kHeads * 16) + head * 16 + 4 * g;
+#pragma unroll
+  for (int db = 0; db < 16; ++db) {
+    const f32x4 v = st.o[db] * k;
+    u32x2 packed;
+    packed.x = pack_f16x2(v[0], v[1]);
+    packed.y = pack_f16x2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(dst + db * (kHeads * 16)) = packed;
+  }
+  if (g == 0) {
+    float* ml = a.part_ml + 4 * (ts * kHeads + head);
+    if (half == 0) {
+      ml[0] = st.m_run;
+      ml[1] = l_tot;
+    }
+    ml[2 + half] = scale;
+  }
+}
+
+__global__ __launch_bounds__(kPairThreads) void attn_bf16_pair_kernel(AttnArgs a) {
+  // one LDS object per tile, so the compiler's waits for a tile's direct loads
+  // cover that tile only
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t0[kPairRegion];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t1[kPairRegion];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_t2[kPairRegion];
+  static_assert(kPairTiles == 3, "three tile objects");
+  __shared__ __attribute__((aligned(16))) float xbuf[kPairWaves * 64 * 8];
+  __shared__ int32_t lds_idx[kPairRows];
+  __shared__ float lds_rscale[kPairRows];
+  const int t = blockIdx.y, split = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = wave >> 2;
+  const int head = 16 * (wave & 3) + (lane & 15);
+  const int g = lane >> 4;
+  int64_t base;
+  int n;
+  a.batch.token(t, base, n);
+  const int32_t* idx_row = a.indices + (int64_t)t * a.k;
+  const int j_begin = split * a.rows_per_split;
+  const int j_end = min(a.k, j_begin + a.rows_per_split);
+
+  u32x4 qb[9];
+  {
+    const uint16_t* q = a.q_abs + ((int64_t)t * kHeads + head) * kDQK + 288 * half + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 9; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
+  }
+  HalfState st;
+  st.m_run = -INFINITY;
+  st.l_run = 0.0f;
+#pragma unroll
+  for (int db = 0; db < 16; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float zscale = a.sm_scale * kLog2e;
+  const uint32_t seq_bytes = (uint32_t)max(n, 0) * (2u * kDQK);
+  const __amdgpu_buffer_rsrc_t rows = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.kv + base * 2 * kDQK), (short)0, (int)seq_bytes, 0x00020000);
+
+  for (int j0 = j_begin; j0 < j_end; j0 += kPairRows) {
+    const int ntiles = min(kPairTiles, (j_end - j0 + kAttnTileRows - 1) / kAttnTileRows);
+    __syncthreads();  // the previous super-tile is fully consumed
+    if (threadIdx.x < kPairRows) {
+      const int j = j0 + threadIdx.x;
+      const int idx = j < j_end ? idx_row[j] : -1;
+      const bool ok = idx >= 0 && idx < n;
+      lds_idx[threadIdx.x] = ok ? idx : -1;
+      lds_rscale[threadIdx.x] = ok ? 1.0f : -1.0f;
+    }
+    __syncthreads();
+    // every wave issues kPairLoads loads for each of the kPairTiles tiles
+#pragma unroll
+    for (int i = 0; i < kPairTiles; ++i) {
+      int offs[kPairLoads];
+#pragma unroll
+      for (int q = 0; q < kPairLoads; ++q) {
+        const int u = (wave + q * kPairWaves) * 64 + lane;
+        const int r = u / kUnitsPerRow, c = u - r * kUnitsPerRow;
+        int off = (int)seq_bytes;  // out of range: zeros
+        if (r < kAttnTileRows && c < kUnitsPerRow - 1) {
+          const int idx = lds_idx[i * kAttnTileRows + r];
+          if (idx >= 0) off = idx * (2 * kDQK) + c * 16;
+        }
+        offs[q] = off;
+      }
+      uint8_t* region = i == 0 ? lds_t0 : (i == 1 ? lds_t1 : lds_t2);
+#pragma unroll
+      for (int q = 0; q < kPairLoads; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rows,
+            (__attribute__((address_space(3))) void*)(region + (wave + q * kPairWaves) * 1024),
+            16, offs[q], 0, 0, kNonTemporal);
+    }
+    // consume each tile once its own loads have landed
+#pragma unroll
+    for (int i = 0; i < kPairTiles; ++i) {
+      if (i >= ntiles) break;
+      if (i == 0) __builtin_amdgcn_s_waitcnt(kVmcntWait[0]);
+      else if (i == 1) __builtin_amdgcn_s_waitcnt(kVmcntWait[1]);
+      else __builtin_amdgcn_s_waitcnt(kVmcntWait[2]);
+      __syncthreads();
+      const uint8_t* region = i == 0 ? lds_t0 : (i == 1 ? lds_t1 : lds_t2);
+      attend_tile_half(reinterpret_cast<const uint16_t*>(region), lds_rscale + i * kAttnTileRows,
+                       xbuf, st, qb, zscale, lane, wave, half);
+    }
+  }
+  finish_half(a, st, t, split, head, lane, half);
+}
+
 // Rows staged through registers one tile ahead (fp8 rows are widened to bf16
 // on the way into LDS).
 template <bool kFp8>
@@ -349,39 +626,38 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
 
 // Merges the split partials by log-sum-exp, then gates. One workgroup per
 // (column block db, token): thread j takes head j/4 and columns
-// 16*db + 4*(j%4) .. +3; for each split it reads one contiguous 4 KiB block.
-constexpr int kMaxCombine = 64;
+// 16*db + 4*(j%4) .. +3; for each split it reads one contiguous 2 KiB block.
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   const int db = blockIdx.x, t = blockIdx.y;
   const int h = threadIdx.x >> 2, q = threadIdx.x & 3;
   const int S = a.splits;
   const int64_t th = (int64_t)t * kHeads + h;
-  const float* ml = a.part_ml + 2 * ((int64_t)t * S * kHeads + h);   // stride 2*kHeads per split
+  const float* ml = a.part_ml + 4 * ((int64_t)t * S * kHeads + h);   // stride 4*kHeads per split
+  const int sc = 2 + (db >= 16);                                       // scale of this column half
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[2 * kHeads * s]);
-  const float* po = a.part_o + (int64_t)t * S * kHeads * kDLatent + db * (kHeads * 16) + h * 16 + 4 * q;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, ml[4 * kHeads * s]);
+  const uint16_t* po = a.part_o + (int64_t)t * S * kHeads * kDLatent + db * (kHeads * 16) + h * 16 + 4 * q;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.0f;
   if (M != -INFINITY) {
-    int s = 0;
-    for (; s + 4 <= S; s += 4) {
-      f32x4 v[4];
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      u32x2 v[4];
       float wv[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        v[u] = *reinterpret_cast<const f32x4*>(po + (int64_t)(s + u) * kHeads * kDLatent);
-        const float ms = ml[2 * kHeads * (s + u)];
-        wv[u] = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        L += ml[2 * kHeads * (s + u) + 1] * wv[u];
+        const int s = min(s0 + u, S - 1);
+        v[u] = *reinterpret_cast<const u32x2*>(po + (int64_t)s * kHeads * kDLatent);
+        const float ms = ml[4 * kHeads * s];
+        const float w = (s0 + u >= S || ms == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        const float ls = ml[4 * kHeads * s + 1] * w;
+        L += ls;
+        wv[u] = ls * ml[4 * kHeads * s + sc];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc += v[u] * wv[u];
-    }
-    for (; s < S; ++s) {
-      const float ms = ml[2 * kHeads * s];
-      const float w = ms == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-      L += ml[2 * kHeads * s + 1] * w;
-      acc += *reinterpret_cast<const f32x4*>(po + (int64_t)s * kHeads * kDLatent) * w;
+      for (int u = 0; u < 4; ++u) {
+        const f32x2 lo = unpack_f16x2(v[u].x), hi = unpack_f16x2(v[u].y);
+        acc += f32x4{lo.x, lo.y, hi.x, hi.y} * wv[u];
+      }
     }
   }
   const float gs = gate_factor(a.gate, th);
@@ -396,7 +672,7 @@ hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid(a.splits, a.num_tokens);
   if (fp8) attn_kernel<true><<<grid, kThreads, 0, s>>>(a);
-  else attn_bf16_direct_kernel<<<grid, kThreads, 0, s>>>(a);
+  else attn_bf16_pair_kernel<<<grid, kPairThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

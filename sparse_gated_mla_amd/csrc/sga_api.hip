@@ -84,15 +84,15 @@ AttnPlan plan_attention(int32_t T, int32_t k) {
 }
 
 struct AttnLayout {
-  float* part_o;
+  uint16_t* part_o;
   float* part_ml;
 };
 
 AttnLayout carve_attn(Carver& c, int32_t T, const AttnPlan& p) {
   AttnLayout L{nullptr, nullptr};
   if (p.splits > 1) {
-    L.part_o = c.take<float>((size_t)T * p.splits * sga::kHeads * sga::kDLatent);
-    L.part_ml = c.take<float>((size_t)T * p.splits * sga::kHeads * 2);
+    L.part_o = c.take<uint16_t>((size_t)T * p.splits * sga::kHeads * sga::kDLatent);
+    L.part_ml = c.take<float>((size_t)T * p.splits * sga::kHeads * 4);
   }
   return L;
 }

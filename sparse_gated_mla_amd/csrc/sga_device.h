@@ -61,6 +61,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Two fp32 -> two IEEE fp16 (round to nearest even), packed low then high.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 h;
+  h.x = (_Float16)lo;
+  h.y = (_Float16)hi;
+  return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ f32x2 unpack_f16x2(uint32_t u) {
+  const f16x2 h = __builtin_bit_cast(f16x2, u);
+  return f32x2{(float)h.x, (float)h.y};
+}
+
 // ---------------------------------------------------------------- radix keys
 // Order-preserving map from fp32 scores to uint32 keys: a larger score gives a
 // larger key. -0.0 maps to the key of +0.0, so they tie.

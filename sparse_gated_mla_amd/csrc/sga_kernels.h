@@ -66,8 +66,9 @@ struct AttnArgs {
   float* lse;              // [T,64] or null
   int splits;              // row splits per token
   int rows_per_split;      // multiple of kAttnTileRows
-  float* part_o;           // [T,splits,64,512]
-  float* part_ml;          // [T,splits,64,2]
+  uint16_t* part_o;        // [T,splits,32 column blocks,64 heads,16] fp16, normalised
+  float* part_ml;          // [T,splits,64,4]: max logit (base 2), exp-sum, output scale of
+                           // columns 0..255 and of columns 256..511
 };
 
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
