@@ -13,7 +13,9 @@ Prints one JSON line with:
 - query-tokens/s;
 - roofline: the indexer kernel, timed with HIP events on the library's stream
   inside the timed steps, against the 8 TB/s HBM peak. The algorithmic bytes
-  are the indexer keys it must read plus its query inputs;
+  are the indexer keys it must read plus its query inputs. For a chunked
+  prefill, where thousands of tokens share one sequence's keys, the roof is
+  the 2.5 PFLOP/s dense bf16 MFMA peak instead;
 - cpu_baseline: the float64 CPU oracle, timed on this host over whole batches
   of the same workload.
 """
@@ -38,10 +40,16 @@ import sparse_gated_mla_amd as sga  # noqa: E402
 
 METRIC = "SGA decode query-tokens/sec at 128K ctx, k=2048; achieved HBM GB/s vs peak"
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+COPY_BYTES = 1 << 30                # calibration copy size
 WORKLOADS = {"tiny_decode_4k": 0, "batched_decode_ragged_16k_32k": 1, "long_decode_128k": 2,
+             "chunked_prefill_128k": 3,
              "extended_decode_256k_fp8": 4}
+PMC_WORKLOAD = "long_decode_128k"
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_long_decode_128k_pmc.json")
-INDEXER_SRC = os.path.join(ROOT, "sparse_gated_mla_amd", "csrc", "indexer.hip")
+# the sources the indexer kernel is built from
+INDEXER_SRC = [os.path.join(ROOT, "sparse_gated_mla_amd", "csrc", f)
+               for f in ("indexer.hip", "sga_kernels.h", "sga_device.h", "sga_block.h")]
 
 
 # ---------------------------------------------------------------- HIP events
@@ -102,6 +110,13 @@ def indexer_bytes(wl) -> int:
     return rows * per_row + wl.num_tokens * (64 * 128 * 2 + 64 * 4)
 
 
+def indexer_flops(wl) -> int:
+    """Multiply-add work of one indexer launch: 2*64*128 flops per (token,
+    visible position) for the logits; the ReLU and head weighting are not
+    counted."""
+    return int(visible(wl).astype(np.int64).sum()) * 2 * 64 * 128
+
+
 def step_bytes(wl) -> int:
     """Algorithmic bytes of one whole step: the indexer's bytes plus, per token,
     its min(k, visible) selected latent rows (576 elements, plus a scale for fp8),
@@ -115,8 +130,11 @@ def step_bytes(wl) -> int:
 
 # ---------------------------------------------------------------- traffic
 def src_digest() -> str:
-    with open(INDEXER_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for p in INDEXER_SRC:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():
@@ -130,6 +148,56 @@ def measured_traffic():
     if d.get("indexer_source_sha256_16") != src_digest():
         return None
     return d.get("traffic_bytes_per_launch")
+
+
+def summarize_pmc(root: str) -> dict:
+    """Writes the indexer's HBM traffic summary from rocprofv3 counter runs.
+
+    `root` holds one rocprofv3 output folder per pass: a FETCH_SIZE pass and a
+    WRITE_SIZE pass over a short bench run, and the same two counters over
+    `--copy-calibration` (five copies of 1 GiB). Both counters read KiB per
+    dispatch; each is scaled by the bytes a known copy moves over what the
+    counter reads for that copy."""
+    import csv
+    import glob
+    per = {}                        # (run, kernel, counter) -> values per dispatch
+    for f in glob.glob(os.path.join(root, "*", "*counter_collection.csv")):
+        for row in csv.DictReader(open(f)):
+            per.setdefault((f, row["Kernel_Name"], row["Counter_Name"]), []).append(
+                float(row["Counter_Value"]))
+    mean = lambda v: sum(v) / len(v)
+    copy_kib = COPY_BYTES / 1024.0
+    out = {"indexer_source_sha256_16": src_digest(), "workload": PMC_WORKLOAD,
+           "copy_bytes": COPY_BYTES,
+           "commands": [
+               "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/fetch -o run "
+               "-- python3 bench.py --steps 3 --warmup 1 --copies 1 --no-cpu-baseline",
+               "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/write -o run "
+               "-- python3 bench.py --steps 3 --warmup 1 --copies 1 --no-cpu-baseline",
+               "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/copy_fetch "
+               "-o run -- python3 bench.py --copy-calibration",
+               "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/copy_write "
+               "-o run -- python3 bench.py --copy-calibration",
+               "python3 bench.py --summarize-pmc <dir>"]}
+    total = 0.0
+    for ctr, name in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        copies = [mean(v) for (_, k, c), v in per.items() if c == ctr and "copyBuffer" in k]
+        idx = [v for (_, k, c), v in per.items() if c == ctr and "indexer_kernel" in k]
+        if not copies or not idx:
+            raise SystemExit(f"no {ctr} rows for the copy or the indexer under {root}")
+        # the calibration copy moves the largest amount of any copy in the runs
+        factor = copy_kib / max(copies)
+        kib = mean(idx[0])
+        out[f"{name}_kib_per_dispatch"] = kib
+        out[f"{name}_copy_kib_per_dispatch"] = max(copies)
+        out[f"{name}_scale"] = factor
+        out[f"{name}_bytes_per_launch"] = kib * 1024.0 * factor
+        total += kib * 1024.0 * factor
+    out["traffic_bytes_per_launch"] = total
+    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
+    with open(PMC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
 
 
 # ---------------------------------------------------------------- CPU oracle
@@ -173,7 +241,12 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="input sets alternated between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--summarize-pmc", metavar="DIR",
+                    help="write the indexer traffic summary from rocprofv3 counter runs under DIR")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        print(json.dumps(summarize_pmc(args.summarize_pmc)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the path runs on one GPU with no collectives)", file=sys.stderr)
@@ -185,7 +258,7 @@ def main():
     torch.cuda.set_device(dev)
 
     if args.copy_calibration:
-        n = 1 << 30
+        n = COPY_BYTES
         a = torch.ones(n, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(5):
@@ -237,19 +310,29 @@ def main():
     value = T * K / wall
     ib = indexer_bytes(wl)
     idx_avg_s = float(np.mean(idx_ms)) / 1e3
-    achieved = ib / idx_avg_s / 1e9
     sb = step_bytes(wl)
-    traffic = measured_traffic()
+    # the indexer's roof: HBM for decode; the MFMA when many tokens share one
+    # sequence's keys (chunked prefill), whichever takes longer at peak
+    flops = indexer_flops(wl)
+    if flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > ib / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "mfma", "kernel": "indexer_kernel",
+                "achieved": round(flops / idx_avg_s / 1e12, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(flops / idx_avg_s / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": None, "algorithmic_flops_per_launch": flops}
+    else:
+        achieved = ib / idx_avg_s / 1e9
+        roof = {"bound": "hbm", "kernel": "indexer_kernel", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": measured_traffic() if wl.name == PMC_WORKLOAD else None,
+                "algorithmic_bytes_per_launch": ib}
+    roof["avg_launch_us"] = round(idx_avg_s * 1e6, 2)
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if wl.fp8 else "bf16",
         "data": "synthetic",
         "config": dict(si.describe(wl), parallelism="single GPU"),
-        "roofline": {"bound": "hbm", "kernel": "indexer_kernel", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ib,
-                     "avg_launch_us": round(idx_avg_s * 1e6, 2)},
+        "roofline": roof,
         "extra": {"step_algorithmic_bytes": sb,
                   "step_gbps": round(sb / (ms_per_step / 1e3) / 1e9, 1),
                   "step_frac_of_hbm_peak": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
