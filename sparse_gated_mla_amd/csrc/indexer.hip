@@ -7,7 +7,7 @@
 // - Streaming. A workgroup streams kIndexerChunk positions of one token's key
 //   cache; its four waves take 32-position tiles in turn. Every load
 //   instruction reads 1 KiB of contiguous keys (16 B per lane), so each wave
-//   instruction covers whole cache lines. Each wave keeps two tiles of loads
+//   instruction covers whole cache lines. Each wave keeps three tiles of loads
 //   in flight.
 // - Re-layout. A wave writes its tile into a private 8 KiB LDS region. The
 //   16-byte slots of each row are XOR-swizzled by row, so the 16 lanes of a
@@ -20,11 +20,12 @@
 //   The dims are visited in a permuted order, the same in A and B: lane group
 //   g of step s covers dims 64g + 8s .. 64g + 8s + 7.
 // - Epilogue, per lane: ReLU, times w, summed over the lane's 32 heads. One
-//   cross-half shuffle then gives each position's score.
+//   cross-half shuffle then gives each position's score, which is stored at
+//   once (and counted, see below) while the wave's next tiles are in flight.
 // - fp8. Keys are widened to bf16 exactly on the LDS read. The row scale
 //   multiplies each head's dot product before the ReLU.
 // - Fused top-k. The variant used by the whole forward pass also counts the
-//   top 11 key bits of every score into a per-token histogram (the first radix
+//   top 12 key bits of every score into a per-token histogram (the first radix
 //   level of the top-k).
 #include "sga_block.h"
 #include "sga_kernels.h"
@@ -35,7 +36,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;
-constexpr int kStages = 3;   // key tiles in flight per wave
+// key tiles in flight per wave (more did not help the fp8 variant)
+template <bool kFp8> constexpr int kStages = 3;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
@@ -120,13 +122,13 @@ struct KeyTile {
   }
 };
 
-// Scores one staged tile: writes each position's score into lds_scores.
-// lds_w holds the token's 64 head weights; each lane reads the 32 that match
-// its accumulator rows (4 consecutive heads per b128 read).
+// Scores one staged tile. Returns, in lanes 0..31, the score of tile row
+// `lane` (lanes 32..63 hold the same values). lds_w holds the token's 64 head
+// weights; each lane reads the 32 that match its accumulator rows (4
+// consecutive heads per b128 read).
 template <bool kFp8>
-__device__ __forceinline__ void score_tile(const uint8_t* lds, float kscale, int lane,
-                                           const u32x4 (&qa)[2][8], const float* lds_w,
-                                           int grp, int w, float* lds_scores) {
+__device__ __forceinline__ float score_tile(const uint8_t* lds, float kscale, int lane,
+                                            const u32x4 (&qa)[2][8], const float* lds_w) {
   u32x4 b[8];
   KeyTile<kFp8>::operands(lds, lane, b);
   f32x16 acc0 = {}, acc1 = {};
@@ -150,20 +152,27 @@ __device__ __forceinline__ void score_tile(const uint8_t* lds, float kscale, int
       sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
     }
   }
-  sc += __shfl_xor(sc, 32);
-  if (lane < 32) lds_scores[KeyTile<kFp8>::position(grp, w, lane)] = sc;
+  return sc + __shfl_xor(sc, 32);
+}
+
+// query heads as MFMA A operands: qa[mb][s] = q[32mb + l%32][64g + 8s .. +7]
+__device__ __forceinline__ void load_query(const uint16_t* q, int lane, u32x4 (&qa)[2][8]) {
+  const int nidx = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qa[mb][s] = *reinterpret_cast<const u32x4*>(q + (32 * mb + nidx) * kIdxDim + 64 * g + 8 * s);
 }
 
 template <bool kFp8, bool kHist>
 __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   constexpr int kTileBytes = KeyTile<kFp8>::kRowBytes * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
-  __shared__ float lds_scores[kIndexerChunk];
   __shared__ __attribute__((aligned(16))) float lds_w[kIdxHeads];
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nidx = lane & 31, g = lane >> 5;
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -178,43 +187,39 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   const int len = min(n - chunk0, kIndexerChunk);   // positions of this chunk (<= 0: none)
   if (len > 0) {
     uint8_t* lds = lds_tiles + wave * kTileBytes;
-    // query heads as MFMA A operands: qa[mb][s] = q[32mb + l%32][64g + 8s .. +7]
     u32x4 qa[2][8];
-    const uint16_t* q = a.q_idx + (int64_t)t * kIdxHeads * kIdxDim;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int s = 0; s < 8; ++s)
-        qa[mb][s] = *reinterpret_cast<const u32x4*>(q + (32 * mb + nidx) * kIdxDim + 64 * g + 8 * s);
+    load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
 
     const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * KeyTile<kFp8>::kRowBytes,
                                   (uint32_t)len * KeyTile<kFp8>::kRowBytes);
     const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + base + chunk0) : (const void*)a.k_idx,
                                     kFp8 ? (uint32_t)len * 4u : 0u);
     const int ngroups = (len + KeyTile<kFp8>::kGroupRows - 1) / KeyTile<kFp8>::kGroupRows;
+    float* srow = a.scores + (int64_t)t * a.ld + chunk0;
 
     // this wave's tile of every group; kStages groups in flight. Loads are
     // never skipped (past the chunk they read zeros), so each wait is exact.
-    KeyTile<kFp8> st[kStages];
+    constexpr int S = kStages<kFp8>;
+    KeyTile<kFp8> st[S];
 #pragma unroll
-    for (int j = 0; j < kStages; ++j) st[j].load(keys, scales, j, wave, lane);
-    for (int i = 0; i < ngroups; i += kStages) {
+    for (int j = 0; j < S; ++j) st[j].load(keys, scales, j, wave, lane);
+    for (int i = 0; i < ngroups; i += S) {
 #pragma unroll
-      for (int j = 0; j < kStages; ++j) {
+      for (int j = 0; j < S; ++j) {
         st[j].store(lds, lane);
         const float ks = st[j].scale;
-        st[j].load(keys, scales, i + j + kStages, wave, lane);
-        if (i + j < ngroups) score_tile<kFp8>(lds, ks, lane, qa, lds_w, i + j, wave, lds_scores);
+        st[j].load(keys, scales, i + j + S, wave, lane);
+        if (i + j < ngroups) {
+          // scores go out as they are made: each is stored and counted while
+          // the wave's later tiles are still in flight
+          const float sc = score_tile<kFp8>(lds, ks, lane, qa, lds_w);
+          const int p = KeyTile<kFp8>::position(i + j, wave, lane);
+          if (lane < 32 && p < len) {
+            srow[p] = sc;
+            if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
+          }
+        }
       }
-    }
-  }
-  __syncthreads();
-  if (len > 0) {
-    float* srow = a.scores + (int64_t)t * a.ld + chunk0;
-    for (int i = threadIdx.x; i < len; i += kThreads) {
-      const float sc = lds_scores[i];
-      srow[i] = sc;
-      if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
     }
   }
   if constexpr (kHist) hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);

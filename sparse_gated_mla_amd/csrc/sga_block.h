@@ -72,13 +72,16 @@ __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
 
 // Adds a workgroup's LDS digit-1 histogram into the token's global histogram
 // (relaxed device-scope atomics; visible to the next kernel on the stream).
+// Two adjacent bins go in one 64-bit atomic: a bin counts at most one token's
+// positions (< 2^32), so the low half never carries into the high half.
 // No fence and no cross-workgroup hand-off: the cut is taken by the next kernel.
 template <int NT>
 __device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* ghist) {
   __syncthreads();
-  for (int b = threadIdx.x; b < kHist1; b += NT) {
-    uint32_t c = lds_hist[b];
-    if (c) atomicAdd(&ghist[b], c);
+  unsigned long long* g64 = reinterpret_cast<unsigned long long*>(ghist);
+  for (int b = threadIdx.x; b < kHist1 / 2; b += NT) {
+    const uint32_t c0 = lds_hist[2 * b], c1 = lds_hist[2 * b + 1];
+    if (c0 | c1) atomicAdd(g64 + b, (unsigned long long)c0 | ((unsigned long long)c1 << 32));
   }
 }
 

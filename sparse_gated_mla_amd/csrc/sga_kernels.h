@@ -10,8 +10,8 @@ namespace sga {
 
 // Per-token top-k control block in the workspace.
 struct TopkCtrl {
-  uint32_t digit1;      // top 11 key bits of the k-th largest score
-  uint32_t above1;      // scores whose top 11 key bits exceed digit1
+  uint32_t digit1;      // top 12 key bits of the k-th largest score
+  uint32_t above1;      // scores whose top 12 key bits exceed digit1
   uint32_t cand_count;  // candidates (top bits == digit1) appended so far
   uint32_t pad;
 };
@@ -30,7 +30,7 @@ struct IndexerArgs {
   float* scores;           // [T,ld]
   int64_t ld;
   // top-k first level, filled by the fused variant
-  uint32_t* hist;          // [T,2048]
+  uint32_t* hist;          // [T,4096]
   TopkCtrl* ctrl;          // [T]
   int k;
 };
@@ -42,7 +42,7 @@ struct TopkArgs {
   int64_t ld;
   int k;
   int32_t* indices;        // [T,k]
-  uint32_t* hist;          // [T,2048]
+  uint32_t* hist;          // [T,4096]
   TopkCtrl* ctrl;          // [T]
   uint32_t* sel;           // [T,words]
   int64_t words;           // bitmap words per token
