@@ -34,31 +34,34 @@ struct Carver {
   }
 };
 
+static_assert((SGA_MAX_LEN + sga::kSelectChunk - 1) / sga::kSelectChunk <= sga::kMaxSelectWgs,
+              "the finalize kernel scans one slice count per select workgroup");
+
 int64_t bitmap_words(int32_t max_len) { return ((int64_t)max_len + 63) / 64 * 2; }
 
 // ---------------------------------------------------------------- top-k layout
 struct TopkLayout {
-  uint32_t* hist;
+  uint32_t* hist;   // digit-1 histograms, then the digit-2 ones
   TopkCtrl* ctrl;
   uint32_t* sel;
   uint32_t* cand;
   uint32_t* cand_key;
+  uint32_t* wg_count;
   int64_t words, cand_cap;
-  size_t clear_words;  // hist + ctrl are contiguous and cleared per call
+  int max_select_wgs;
+  size_t clear_words;  // the histograms, cleared per call
 };
 
 TopkLayout carve_topk(Carver& c, int32_t T, int32_t max_len) {
   TopkLayout L;
   L.words = bitmap_words(max_len);
-  L.cand_cap = max_len;
-  // hist and ctrl are carved back to back and cleared by one fill kernel
-  size_t hist_bytes = (size_t)T * sga::kHist1 * sizeof(uint32_t);
-  size_t ctrl_bytes = (size_t)T * sizeof(TopkCtrl);
-  char* start = c.base ? c.base + c.used : nullptr;
-  c.used += align_up(hist_bytes + ctrl_bytes);
-  L.hist = reinterpret_cast<uint32_t*>(start);
-  L.ctrl = start ? reinterpret_cast<TopkCtrl*>(start + hist_bytes) : nullptr;
-  L.clear_words = (hist_bytes + ctrl_bytes) / sizeof(uint32_t);
+  L.max_select_wgs = (max_len + sga::kSelectChunk - 1) / sga::kSelectChunk;
+  L.cand_cap = (int64_t)L.max_select_wgs * sga::kSelectChunk;
+  // both histogram levels, back to back, cleared by one fill kernel
+  L.hist = c.take<uint32_t>((size_t)T * (sga::kHist1 + sga::kHist2));
+  L.clear_words = (size_t)T * (sga::kHist1 + sga::kHist2);
+  L.ctrl = c.take<TopkCtrl>((size_t)T);
+  L.wg_count = c.take<uint32_t>((size_t)T * L.max_select_wgs);
   L.sel = c.take<uint32_t>((size_t)T * L.words);
   L.cand = c.take<uint32_t>((size_t)T * L.cand_cap);
   L.cand_key = c.take<uint32_t>((size_t)T * L.cand_cap);
@@ -154,12 +157,15 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
   a.k = k;
   a.indices = indices;
   a.hist = L.hist;
+  a.hist2 = L.hist + (size_t)batch->num_tokens * sga::kHist1;
   a.ctrl = L.ctrl;
   a.sel = L.sel;
   a.words = L.words;
   a.cand = L.cand;
   a.cand_key = L.cand_key;
   a.cand_cap = L.cand_cap;
+  a.wg_count = L.wg_count;
+  a.max_select_wgs = L.max_select_wgs;
   if (!hist_ready) {
     SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
     SGA_HIP(sga::launch_topk_hist(a, stream));

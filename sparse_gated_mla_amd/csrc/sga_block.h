@@ -65,6 +65,80 @@ __device__ __forceinline__ void block_find_cut(const uint32_t* h, int nbins, uin
   __syncthreads();
 }
 
+// Radix cut with two workgroup barriers: h[0..nbins) in LDS, ranked from the
+// top, 1 <= r <= S(0). Finds d with S(d+1) < r <= S(d), S(d) = sum of h[b]
+// for b >= d, and returns d and S(d+1) to every thread. Thread j owns a run
+// of bins from the top; a wave scan gives each thread its running total and
+// each wave adds the totals of the waves before it. scratch: NT/64 + 2
+// words of LDS, free again once the function returns.
+template <int NT>
+__device__ __forceinline__ void block_cut(const uint32_t* h, int nbins, uint32_t r, uint32_t* scratch,
+                                          uint32_t& d, uint32_t& above) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int per = (nbins + NT - 1) / NT;
+  const int top = nbins - (int)threadIdx.x * per;
+  const int cnt = top <= 0 ? 0 : (top < per ? top : per);
+  uint32_t sum = 0;
+  for (int i = 1; i <= cnt; ++i) sum += h[top - i];
+  uint32_t x = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) scratch[wid] = x;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w < wid) before += scratch[w];
+  const uint32_t incl = before + x, excl = incl - sum;
+  if (excl < r && r <= incl) {
+    uint32_t acc = excl;
+    for (int i = 1; i <= cnt; ++i) {
+      const uint32_t c = h[top - i];
+      if (acc + c >= r) {
+        scratch[kWaves] = (uint32_t)(top - i);
+        scratch[kWaves + 1] = acc;
+        break;
+      }
+      acc += c;
+    }
+  }
+  __syncthreads();
+  d = scratch[kWaves];
+  above = scratch[kWaves + 1];
+  __syncthreads();
+}
+
+// Exclusive prefix sums of two counters per thread over a workgroup, in one
+// pass (the pair travels as one 64-bit value; neither total may reach 2^32).
+// scratch: 2 * (NT/64) words of LDS, free again once the function returns.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t* scratch,
+                                                 uint32_t& a_before, uint32_t& b_before) {
+  constexpr int kWaves = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  unsigned long long v = (unsigned long long)a | ((unsigned long long)b << 32), x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const unsigned long long y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  unsigned long long* s64 = reinterpret_cast<unsigned long long*>(scratch);
+  if (lane == 63) s64[wid] = x;
+  __syncthreads();
+  unsigned long long before = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    if (w < wid) before += s64[w];
+  const unsigned long long e = before + x - v;
+  a_before = (uint32_t)e;
+  b_before = (uint32_t)(e >> 32);
+  __syncthreads();
+}
+
 // Device-scope relaxed load that bypasses the non-coherent vector L1.
 __device__ __forceinline__ uint32_t load_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -88,7 +162,7 @@ __device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* 
 // First radix cut of a token from its global digit-1 histogram: the digit of
 // the k-th largest score and the count of scores with a larger digit.
 // Every thread of the workgroup gets the result. lds_hist: kHist1 words;
-// scratch: at least NT/64 + 3 words.
+// scratch: at least NT/64 + 2 words.
 template <int NT>
 __device__ __forceinline__ void hist1_cut(const uint32_t* ghist, uint32_t* lds_hist, uint32_t k,
                                           uint32_t* scratch, uint32_t& digit1, uint32_t& above1) {
@@ -99,11 +173,7 @@ __device__ __forceinline__ void hist1_cut(const uint32_t* ghist, uint32_t* lds_h
 #pragma unroll
   for (int u = 0; u < kHist1 / NT; ++u) lds_hist[u * NT + threadIdx.x] = h[u];
   __syncthreads();
-  uint32_t* res = scratch + NT / 64 + 1;
-  block_find_cut<NT>(lds_hist, kHist1, k, scratch, res);
-  digit1 = res[0];
-  above1 = res[1];
-  __syncthreads();
+  block_cut<NT>(lds_hist, kHist1, k, scratch, digit1, above1);
 }
 
 }  // namespace sga

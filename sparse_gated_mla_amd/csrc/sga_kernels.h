@@ -8,16 +8,16 @@
 
 namespace sga {
 
-// Per-token top-k control block in the workspace.
+// Per-token top-k control block in the workspace, written by the first select
+// workgroup of the token.
 struct TopkCtrl {
   uint32_t digit1;      // top 12 key bits of the k-th largest score
   uint32_t above1;      // scores whose top 12 key bits exceed digit1
-  uint32_t cand_count;  // candidates (top bits == digit1) appended so far
-  uint32_t pad;
 };
 
 constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup
 constexpr int kSelectChunk = 4096;    // positions per select workgroup
+constexpr int kMaxSelectWgs = 128;    // select workgroups of the longest context (512K)
 constexpr int kAttnTileRows = 32;     // latent rows per attention tile
 
 struct IndexerArgs {
@@ -42,13 +42,17 @@ struct TopkArgs {
   int64_t ld;
   int k;
   int32_t* indices;        // [T,k]
-  uint32_t* hist;          // [T,4096]
+  uint32_t* hist;          // [T,4096] digit-1 histogram (zeroed per call)
+  uint32_t* hist2;         // [T,4096] digit-2 histogram of the candidates (zeroed per call)
   TopkCtrl* ctrl;          // [T]
   uint32_t* sel;           // [T,words]
   int64_t words;           // bitmap words per token
-  uint32_t* cand;          // [T,cand_cap] candidate positions
+  uint32_t* cand;          // [T,cand_cap] candidate positions; select workgroup x of a
+                           // token writes its candidates from slot x * kSelectChunk on
   uint32_t* cand_key;      // [T,cand_cap] their radix keys
-  int64_t cand_cap;
+  int64_t cand_cap;        // a multiple of kSelectChunk covering the longest context
+  uint32_t* wg_count;      // [T,max_select_wgs] candidates each select workgroup wrote
+  int max_select_wgs;
   int lds_cand_cap;        // candidates the finalize kernel can stage in LDS
 };
 
@@ -74,7 +78,6 @@ struct AttnArgs {
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
-hipError_t launch_topk_cut(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);
 constexpr size_t kFinalizeLds = 160 * 1024;  // dynamic LDS of the finalize kernels

@@ -6,22 +6,24 @@
 //
 // Exact radix select on order-preserving uint32 keys. For batches of many
 // tokens (contexts up to 256K), topk_token_kernel does stages 2-3 below in
-// one workgroup per token; otherwise they run as separate kernels over many
-// workgroups per token. The stages:
+// one workgroup per token; otherwise they run as two kernels. The stages:
 //   1. digit-1 histogram: the top 12 key bits of every score, built in the
 //      indexer epilogue (fused path) or by topk_hist_kernel.
-//   2. topk_select_kernel (many workgroups per token): every workgroup first
-//      finds digit1, the top-12-bit value of the k-th largest score, from the
-//      histogram (the kernel boundary orders it after every histogram update,
-//      so no cross-workgroup hand-off or device-scope fence is needed).
-//      Positions whose digit is above digit1 go straight into a selection
-//      bitmap; one ballot gives 64 positions. Positions whose digit equals
-//      digit1 are appended, with their keys, to a candidate list.
-//   3. topk_finalize_kernel (one workgroup per token): two more radix levels
-//      (12 and 8 bits) over the candidates, staged in LDS when they fit, find
-//      the exact k-th key. Ties at that key are kept lowest position first,
-//      using a prefix count over a tie bitmap. An ordered compaction of the
-//      bitmaps then writes the kept positions in ascending order.
+//   2. topk_select_kernel (one workgroup per 4096 positions of a token):
+//      every workgroup first finds digit1, the top-12-bit value of the k-th
+//      largest score, from the histogram (the kernel boundary orders it after
+//      every histogram update, so no cross-workgroup hand-off or device-scope
+//      fence is needed). Positions whose digit is above digit1 go straight
+//      into a selection bitmap; one ballot gives 64 positions. Positions whose
+//      digit equals digit1 are written, with their keys, to the workgroup's
+//      own slice of the candidate list, the workgroup records how many, and
+//      their next 12 key bits are counted into the token's digit-2 histogram.
+//   3. topk_finalize_kernel (one workgroup per token): the digit-2 cut from
+//      that histogram, then the last 8 bits, over the candidates (staged in LDS
+//      when they fit) that share both digits, find the exact k-th key: a wave
+//      ranks them directly when they are few, else an 8-bit histogram does.
+//      One ordered pass over the selection and tie bitmaps then writes the kept
+//      positions in ascending order, ties at the k-th key lowest position first.
 // Every decision depends only on the score values, so the result is exact.
 #include "sga_block.h"
 #include "sga_kernels.h"
@@ -32,7 +34,6 @@ namespace {
 constexpr int kHistThreads = 256;
 constexpr int kSelThreads = 256;
 constexpr int kFinThreads = 1024;
-constexpr int kCutThreads = 1024;
 
 __global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
@@ -56,30 +57,10 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
   hist1_flush<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
 }
 
-// First radix cut of each token: digit1 and above1 from its histogram.
-__global__ __launch_bounds__(kCutThreads) void topk_cut_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[kHist1];
-  __shared__ uint32_t scratch[32];
-  const int t = blockIdx.x;
-  int64_t base;
-  int n;
-  a.batch.token(t, base, n);
-  if (n <= a.k) return;  // every visible position is kept
-  uint32_t d1, above1;
-  hist1_cut<kCutThreads>(a.hist + (int64_t)t * kHist1, hist, (uint32_t)a.k, scratch, d1, above1);
-  if (threadIdx.x == 0) {
-    a.ctrl[t].digit1 = d1;
-    a.ctrl[t].above1 = above1;
-  }
-}
-
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t stage_pos[kSelectChunk];   // also holds the histogram for the cut
-  __shared__ uint32_t stage_key[kSelectChunk];
+  __shared__ uint32_t lds_hist[kHist1];
   __shared__ uint32_t scratch[32];
-  __shared__ uint32_t stage_count;
-  __shared__ uint32_t stage_base;
-  static_assert(kHist1 <= kSelectChunk, "the cut histogram lives in stage_pos");
+  __shared__ uint32_t lds_count;
   constexpr int kSteps = kSelectChunk / kSelThreads;   // 64-position steps per wave
   const int t = blockIdx.y;
   int64_t base;
@@ -95,77 +76,74 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   float v[kSteps];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) v[i] = srow[min(c0 + i * kSelThreads + wave * 64 + lane, c1 - 1)];
+  if (threadIdx.x == 0) lds_count = 0;
   // first radix cut, taken redundantly by every workgroup of the token from the
   // histogram the previous kernel completed (no cross-workgroup hand-off)
   uint32_t d1, above1;
-  hist1_cut<kSelThreads>(a.hist + (int64_t)t * kHist1, stage_pos, (uint32_t)a.k, scratch, d1, above1);
+  hist1_cut<kSelThreads>(a.hist + (int64_t)t * kHist1, lds_hist, (uint32_t)a.k, scratch, d1, above1);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.ctrl[t].digit1 = d1;
     a.ctrl[t].above1 = above1;
   }
-  if (threadIdx.x == 0) stage_count = 0;
-  __syncthreads();
+  // classify: bitmap words for the digits above the cut, candidate masks kept
   uint32_t* sel = a.sel + (int64_t)t * a.words;
+  uint64_t cmask[kSteps];
+  uint32_t total = 0;
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) {
     const int p0 = c0 + i * kSelThreads + wave * 64;
-    if (p0 >= c1) break;
     const int p = p0 + lane;
     const bool valid = p < c1;
-    const uint32_t key = score_key(v[i]);
-    const uint32_t dig = key >> (32 - kDigit1Bits);
+    const uint32_t dig = score_key(v[i]) >> (32 - kDigit1Bits);
     const uint64_t above = __ballot(valid && dig > d1);
-    const uint64_t cand = __ballot(valid && dig == d1);
-    if (lane == 0) {
+    cmask[i] = __ballot(valid && dig == d1);
+    total += (uint32_t)__popcll(cmask[i]);
+    if (lane == 0 && p0 < c1) {
       sel[p0 >> 5] = (uint32_t)above;
       sel[(p0 >> 5) + 1] = (uint32_t)(above >> 32);
     }
-    if (cand) {
-      uint32_t off = 0;
-      if (lane == 0) off = atomicAdd(&stage_count, (uint32_t)__popcll(cand));
-      off = __shfl(off, 0);
-      if (valid && dig == d1) {
-        const uint32_t rank = (uint32_t)__popcll(cand & ((1ull << lane) - 1ull));
-        stage_pos[off + rank] = (uint32_t)p;
-        stage_key[off + rank] = key;
-      }
+  }
+  // one LDS atomic per wave reserves its run of the workgroup's candidate slice
+  uint32_t off = 0;
+  if (lane == 0 && total) off = atomicAdd(&lds_count, total);
+  off = __shfl(off, 0);
+  uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap + c0;
+  uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap + c0;
+  const uint64_t lower = (1ull << lane) - 1ull;
+  uint32_t* h2 = a.hist2 + (int64_t)t * kHist2;   // level 2 of the cut, counted here
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    if ((cmask[i] >> lane) & 1ull) {
+      const uint32_t j = off + (uint32_t)__popcll(cmask[i] & lower);
+      const uint32_t key = score_key(v[i]);
+      gpos[j] = (uint32_t)(c0 + i * kSelThreads + wave * 64 + lane);
+      gkey[j] = key;
+      atomicAdd(h2 + ((key >> kDigit3Bits) & (kHist2 - 1)), 1u);
     }
+    off += (uint32_t)__popcll(cmask[i]);
   }
   __syncthreads();
-  const uint32_t cnt = stage_count;
-  if (cnt == 0) return;
-  if (threadIdx.x == 0) stage_base = atomicAdd(&a.ctrl[t].cand_count, cnt);
-  __syncthreads();
-  uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap + stage_base;
-  uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap + stage_base;
-  for (uint32_t i = threadIdx.x; i < cnt; i += kSelThreads) {
-    gpos[i] = stage_pos[i];
-    gkey[i] = stage_key[i];
-  }
+  if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
 }
 
-// Candidate i of the finalize kernel: from LDS when staged there, else global.
-struct Cands {
-  const uint32_t* pos;
-  const uint32_t* key;
-  __device__ __forceinline__ uint32_t p(uint32_t i) const { return pos[i]; }
-  __device__ __forceinline__ uint32_t k(uint32_t i) const { return key[i]; }
-};
-
-// Dynamic LDS: level-2 histogram (4096) | level-3 histogram (256) | scratch
-// (32) | tie bitmap (words) | selection bitmap (words) | staged candidate
-// positions (lds_cand_cap) | their keys (lds_cand_cap).
+// Dynamic LDS: level-2 histogram (4096; then the staged output) | level-3
+// histogram or short key list (256) | scratch (64) | slice offsets
+// (kMaxSelectWgs + 1) | tie bitmap (words) | selection bitmap (words) |
+// staged candidate positions (lds_cand_cap) | their keys (lds_cand_cap).
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
+  constexpr int kFinWaves = kFinThreads / 64;
   uint32_t* hist2 = lds;
   uint32_t* hist3 = hist2 + kHist2;
   uint32_t* scratch = hist3 + kHist3;
-  uint32_t* tie = scratch + 32;
+  uint32_t* offs = scratch + 64;
+  uint32_t* tie = offs + kMaxSelectWgs + 1;
   uint32_t* selL = tie + a.words;
   uint32_t* lpos = selL + a.words;
   uint32_t* lkey = lpos + a.lds_cand_cap;
-  uint32_t* res = scratch + 24;
+  uint32_t* n_few = scratch + 40;   // short-list length, then the k-th key and ties kept
   const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -174,13 +152,19 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
     for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const uint32_t m = a.ctrl[t].cand_count;
-  const uint32_t d1 = a.ctrl[t].digit1;
-  const uint32_t r1 = (uint32_t)a.k - a.ctrl[t].above1;  // still needed, 1 <= r1 <= m
-  Cands c{a.cand + (int64_t)t * a.cand_cap, a.cand_key + (int64_t)t * a.cand_cap};
+  const int nsel = (n + kSelectChunk - 1) / kSelectChunk;
   const int words = (n + 31) >> 5;
-  // stage: selection bitmap and candidates into LDS (four loads of each in
-  // flight per thread); clear the histograms and the two candidate bitmaps
+  // one round of loads: the cut, the slice counts, the digit-2 histogram and
+  // the selection bitmap
+  const uint32_t d1 = a.ctrl[t].digit1;
+  const uint32_t r1 = (uint32_t)a.k - a.ctrl[t].above1;  // still needed from the candidates
+  uint32_t cnt = 0;
+  if (threadIdx.x < nsel) cnt = a.wg_count[(int64_t)t * a.max_select_wgs + threadIdx.x];
+  static_assert(kHist2 % kFinThreads == 0, "whole bins per thread");
+  uint32_t hv[kHist2 / kFinThreads];
+#pragma unroll
+  for (int u = 0; u < kHist2 / kFinThreads; ++u)
+    hv[u] = a.hist2[(int64_t)t * kHist2 + u * kFinThreads + threadIdx.x];
   {
     const uint32_t* sel = a.sel + (int64_t)t * a.words;
     for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
@@ -196,99 +180,158 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
         }
       }
     }
-    if (m <= (uint32_t)a.lds_cand_cap) {
-      for (uint32_t i0 = 0; i0 < m; i0 += 4 * kFinThreads) {
-        uint32_t pp[4], kk[4];
+  }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t i = min(i0 + u * kFinThreads + threadIdx.x, m - 1);
-          pp[u] = c.pos[i];
-          kk[u] = c.key[i];
-        }
+  for (int u = 0; u < kHist2 / kFinThreads; ++u) hist2[u * kFinThreads + threadIdx.x] = hv[u];
+  for (int b = threadIdx.x; b < kHist3; b += kFinThreads) hist3[b] = 0;
+  if (threadIdx.x == 0) *n_few = 0;
+  // slice offsets: an inclusive scan of the counts by the first waves
+  static_assert(kMaxSelectWgs <= kFinThreads, "one count per thread");
+  {
+    uint32_t x = cnt;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t i = i0 + u * kFinThreads + threadIdx.x;
-          if (i < m) {
-            lpos[i] = pp[u];
-            lkey[i] = kk[u];
-          }
-        }
-      }
-      c = Cands{lpos, lkey};
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(x, o);
+      if (lane >= o) x += y;
     }
-    for (int b = threadIdx.x; b < kHist2 + kHist3; b += kFinThreads) hist2[b] = 0;
+    uint32_t* wsum = scratch + 48;   // apart from what block_cut uses next
+    if (lane == 63 && wave < (kMaxSelectWgs + 63) / 64) wsum[wave] = x;
+    __syncthreads();
+    if (threadIdx.x < kMaxSelectWgs) {
+      uint32_t before = 0;
+      for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
+      offs[threadIdx.x + 1] = before + x;
+    }
+    if (threadIdx.x == 0) offs[0] = 0;
   }
-  __syncthreads();
+  // level 2, from the histogram the select kernel counted
+  uint32_t d2, above2;
+  block_cut<kFinThreads>(hist2, kHist2, r1, scratch, d2, above2);
+  const uint32_t r2 = r1 - above2;
+  const uint32_t n3 = hist2[d2];   // candidates with digit d2: usually a handful
+  const uint32_t m = offs[nsel];
+  const bool staged = m <= (uint32_t)a.lds_cand_cap;
+  const uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap;
+  const uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap;
 
-  // level 2: key bits 19..8 of the candidates
-  for (uint32_t i = threadIdx.x; i < m; i += kFinThreads)
-    atomicAdd(&hist2[(c.k(i) >> kDigit3Bits) & (kHist2 - 1)], 1u);
-  __syncthreads();
-  block_find_cut<kFinThreads>(hist2, kHist2, r1, scratch, res);
-  const uint32_t d2 = res[0];
-  const uint32_t r2 = r1 - res[1];
-  // level 3: key bits 7..0 of the candidates that match digit 2
-  for (uint32_t i = threadIdx.x; i < m; i += kFinThreads) {
-    const uint32_t key = c.k(i);
-    if (((key >> kDigit3Bits) & (kHist2 - 1)) == d2) atomicAdd(&hist3[key & (kHist3 - 1)], 1u);
+  // one pass over the slices: stage the candidates in LDS (when they fit) and
+  // gather level 3: the keys with digit d2 into a short list (at most 64) or
+  // their low 8 bits into a histogram
+  auto level3 = [&](uint32_t key) {
+    if (((key >> kDigit3Bits) & (kHist2 - 1)) != d2) return;
+    if (n3 <= 64) hist3[atomicAdd(n_few, 1u)] = key;
+    else atomicAdd(&hist3[key & (kHist3 - 1)], 1u);
+  };
+  for (int x = wave; x < nsel; x += kFinWaves) {
+    const uint32_t o = offs[x], len = offs[x + 1] - o;
+    const uint32_t* sp = gpos + (int64_t)x * kSelectChunk;
+    const uint32_t* sk = gkey + (int64_t)x * kSelectChunk;
+    for (uint32_t j0 = 0; j0 < len; j0 += 128) {
+      const uint32_t ja = j0 + lane, jb = j0 + 64 + lane;
+      const uint32_t pa = sp[min(ja, len - 1)], ka = sk[min(ja, len - 1)];
+      const uint32_t pb = sp[min(jb, len - 1)], kb = sk[min(jb, len - 1)];
+      if (ja < len) {
+        if (staged) {
+          lpos[o + ja] = pa;
+          lkey[o + ja] = ka;
+        }
+        level3(ka);
+      }
+      if (jb < len) {
+        if (staged) {
+          lpos[o + jb] = pb;
+          lkey[o + jb] = kb;
+        }
+        level3(kb);
+      }
+    }
   }
   __syncthreads();
-  block_find_cut<kFinThreads>(hist3, kHist3, r2, scratch, res);
-  const uint32_t d3 = res[0];
-  const uint32_t ties_kept = r2 - res[1];  // positions with key == kth to keep
-  const uint32_t kth = (d1 << (32 - kDigit1Bits)) | (d2 << kDigit3Bits) | d3;
+  uint32_t kth, ties_kept;   // the k-th key and how many positions holding it to keep
+  if (n3 <= 64) {
+    if (wave == 0) {
+      // lane l holds key l; it counts the keys above it and those not below it
+      const uint32_t mine = lane < (int)n3 ? hist3[lane] : 0u;
+      uint32_t gt = 0, ge = 0;
+      for (int j = 0; j < (int)n3; ++j) {
+        const uint32_t other = __builtin_amdgcn_readlane(mine, j);
+        gt += other > mine;
+        ge += other >= mine;
+      }
+      if (lane < (int)n3 && gt < r2 && r2 <= ge) {   // the lanes holding the k-th key agree
+        n_few[1] = mine;
+        n_few[2] = r2 - gt;
+      }
+    }
+    __syncthreads();
+    kth = n_few[1];
+    ties_kept = n_few[2];
+  } else {
+    uint32_t d3, above3;
+    block_cut<kFinThreads>(hist3, kHist3, r2, scratch, d3, above3);
+    ties_kept = r2 - above3;
+    kth = (d1 << (32 - kDigit1Bits)) | (d2 << kDigit3Bits) | d3;
+  }
 
   // candidates above the k-th key join the selection; ties at it are marked apart
-  for (uint32_t i = threadIdx.x; i < m; i += kFinThreads) {
-    const uint32_t key = c.k(i);
-    if (key >= kth) {
-      const uint32_t p = c.p(i);
-      atomicOr(key > kth ? &selL[p >> 5] : &tie[p >> 5], 1u << (p & 31));
+  auto mark = [&](uint32_t p, uint32_t key) {
+    if (key >= kth) atomicOr(key > kth ? &selL[p >> 5] : &tie[p >> 5], 1u << (p & 31));
+  };
+  if (staged) {
+    for (uint32_t i = threadIdx.x; i < m; i += kFinThreads) mark(lpos[i], lkey[i]);
+  } else {
+    for (int x = wave; x < nsel; x += kFinWaves) {
+      const uint32_t len = offs[x + 1] - offs[x];
+      for (uint32_t j = lane; j < len; j += 64)
+        mark(gpos[(int64_t)x * kSelectChunk + j], gkey[(int64_t)x * kSelectChunk + j]);
     }
   }
   __syncthreads();
-  // keep the ties_kept lowest-position ties: thread j owns a contiguous run of words
+  // one ordered pass: thread j owns a run of words; it keeps every selected
+  // position and the ties while fewer than ties_kept lower ties were kept
   const int per = (words + kFinThreads - 1) / kFinThreads;
   const int w0 = min(words, (int)threadIdx.x * per), w1 = min(words, w0 + per);
-  {
-    uint32_t cnt = 0;
-    for (int i = w0; i < w1; ++i) cnt += __popc(tie[i]);
-    uint32_t total;
-    uint32_t before = block_excl_scan<kFinThreads>(cnt, scratch, &total);
-    for (int i = w0; i < w1; ++i) {
-      uint32_t bits = tie[i];
-      const uint32_t pc = __popc(bits);
-      if (before >= ties_kept) {
-        bits = 0;
-      } else if (before + pc > ties_kept) {
-        const uint32_t keep = ties_kept - before;  // keep the lowest `keep` set bits
-        uint32_t nb = 0;
-        for (uint32_t kept = 0; kept < keep; ++kept) {
-          const uint32_t low = bits & (0u - bits);
-          nb |= low;
-          bits ^= low;
-        }
-        bits = nb;
-      }
-      before += pc;
-      tie[i] = bits;   // only this thread reads these words below
-    }
-  }
-  // ordered compaction of the selection and the kept ties
-  uint32_t cnt = 0;
-  for (int i = w0; i < w1; ++i) cnt += __popc(selL[i] | tie[i]);
-  uint32_t total;
-  uint32_t off = block_excl_scan<kFinThreads>(cnt, scratch, &total);
+  uint32_t ns = 0, nt = 0;
   for (int i = w0; i < w1; ++i) {
-    uint32_t bits = selL[i] | tie[i];
+    ns += __popc(selL[i]);
+    nt += __popc(tie[i]);
+  }
+  uint32_t s_before, t_before;
+  block_excl_scan2<kFinThreads>(ns, nt, scratch, s_before, t_before);
+  uint32_t o = s_before + min(t_before, ties_kept);
+  uint32_t ties_seen = t_before;
+  int32_t* staged_out = reinterpret_cast<int32_t*>(hist2);   // k <= kHist2: the output goes out coalesced
+  const bool stage_out = a.k <= kHist2;
+  for (int i = w0; i < w1; ++i) {
+    const uint32_t sbits = selL[i];
+    uint32_t tbits = tie[i];
+    if (ties_seen >= ties_kept) {
+      tbits = 0;
+    } else if (ties_seen + __popc(tbits) > ties_kept) {
+      uint32_t keep = ties_kept - ties_seen, nb = 0;   // the lowest `keep` ties of this word
+      for (; keep; --keep) {
+        const uint32_t low = tbits & (0u - tbits);
+        nb |= low;
+        tbits ^= low;
+      }
+      tbits = nb;
+    }
+    ties_seen += __popc(tie[i]);
+    uint32_t bits = sbits | tbits;
     while (bits) {
       const int b = __ffs(bits) - 1;
       bits &= bits - 1;
-      if (off < (uint32_t)a.k) out[off] = (i << 5) + b;
-      ++off;
+      if (o < (uint32_t)a.k) {
+        if (stage_out) staged_out[o] = (i << 5) + b;
+        else out[o] = (i << 5) + b;
+      }
+      ++o;
     }
   }
-  for (int i = (int)total + threadIdx.x; i < a.k; i += kFinThreads) out[i] = -1;
+  if (stage_out) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = staged_out[i];
+  }
 }
 
 // The whole selection of one token in one workgroup, for contexts whose two
@@ -499,21 +542,11 @@ int topk_token_lds_cap(int64_t words) {
 
 hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_token_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  hipError_t e = hipFuncSetAttribute((const void*)topk_token_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
+  if (e != hipSuccess) return e;
   const size_t lds = (size_t)(kHist1 + 32 + 2 * a.words + 2 * (int64_t)a.lds_cand_cap) * sizeof(uint32_t);
   topk_token_kernel<<<a.num_tokens, kTokThreads, lds, s>>>(a);
-  return hipGetLastError();
-}
-
-hipError_t launch_topk_cut(const TopkArgs& a, hipStream_t s) {
-  if (a.num_tokens == 0) return hipSuccess;
-  topk_cut_kernel<<<a.num_tokens, kCutThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -525,22 +558,18 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
 }
 
 int topk_finalize_lds_cap(int64_t words) {
-  const int64_t fixed = (int64_t)(kHist2 + kHist3 + 32 + 2 * words) * (int64_t)sizeof(uint32_t);
+  const int64_t fixed = (int64_t)(kHist2 + kHist3 + 64 + kMaxSelectWgs + 1 + 2 * words) * (int64_t)sizeof(uint32_t);
   const int64_t cap = ((int64_t)kFinalizeLds - fixed) / (2 * (int64_t)sizeof(uint32_t));
   return cap > 0 ? (int)cap : 0;
 }
 
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)topk_finalize_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  const size_t lds =
-      (size_t)(kHist2 + kHist3 + 32 + 2 * a.words + 2 * (int64_t)a.lds_cand_cap) * sizeof(uint32_t);
+  hipError_t e = hipFuncSetAttribute((const void*)topk_finalize_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
+  if (e != hipSuccess) return e;
+  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + kMaxSelectWgs + 1 + 2 * a.words +
+                              2 * (int64_t)a.lds_cand_cap) * sizeof(uint32_t);
   topk_finalize_kernel<<<a.num_tokens, kFinThreads, lds, s>>>(a);
   return hipGetLastError();
 }
