@@ -225,7 +225,146 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   if constexpr (kHist) hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
 }
 
+// ---------------------------------------------------------------------------
+// Many tokens over one sequence (chunked prefill). The kernel above would read
+// the keys once per token; here eight tokens share every key tile. A
+// workgroup of eight waves takes eight consecutive tokens, one per wave, each
+// with its query in registers. The 512 threads load each 32-position key tile
+// once (16 B apiece), through a ring of register stages into one of two LDS
+// slots, in the same swizzled layout as above; after one barrier every wave
+// scores the tile for its own token. The work is then bound by the MFMA
+// pipe, not by memory. Tokens of the eight that lie in different sequences
+// are taken one sequence at a time. Each token's digit-1 histogram lives in
+// LDS and, since one workgroup owns the token, goes out with plain stores.
+constexpr int kPfTokens = 8;                  // tokens per workgroup, one per wave
+constexpr int kPfThreads = kPfTokens * 64;
+constexpr int kPfStages = 4;                  // key tiles in flight per thread
+
+template <bool kFp8, bool kHist>
+__global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerArgs a) {
+  using Tile = KeyTile<kFp8>;
+  constexpr int kTileBytes = Tile::kRowBytes * kTile;
+  constexpr int kUnits = kTileBytes / 16;     // 16-byte units of a tile: 512 (bf16) or 256 (fp8)
+  constexpr int kUnitsPerRow = Tile::kRowBytes / 16;
+  static_assert(kUnits <= kPfThreads, "one unit per thread and tile");
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[2][kTileBytes];
+  __shared__ float lds_scale[2][kTile];
+  __shared__ __attribute__((aligned(16))) float lds_w[kPfTokens][kIdxHeads];
+  __shared__ uint32_t lds_hist[kHist ? kPfTokens : 1][kHist ? kHist1 : 1];
+  __shared__ int32_t lds_seq[kPfTokens];
+  __shared__ int32_t lds_n[kPfTokens];
+  __shared__ int64_t lds_base[kPfTokens];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * kPfTokens + wave;
+  const bool live = t < a.num_tokens;
+  int64_t base = 0;
+  int n = 0;
+  if (live) a.batch.token(t, base, n);
+  if (lane == 0) {
+    const int b = live ? a.batch.token_seq[t] : -1;
+    lds_seq[wave] = (n > 0) ? b : -1;
+    lds_n[wave] = n;
+    lds_base[wave] = base;
+  }
+  if (lane < kIdxHeads / 4 && live)
+    reinterpret_cast<f32x4*>(lds_w[wave])[lane] = reinterpret_cast<const f32x4*>(a.w + (int64_t)t * kIdxHeads)[lane];
+  if constexpr (kHist)
+    for (int b = lane; b < kHist1; b += 64) lds_hist[wave][b] = 0;
+  __syncthreads();
+
+  // the unit this thread loads in every tile, and where it goes in LDS
+  const int u = threadIdx.x;
+  const int ur = u / kUnitsPerRow, uc = u % kUnitsPerRow;
+  const int lds_off = ur * Tile::kRowBytes + 16 * Tile::slot(ur, uc);
+  const bool loader = u < kUnits;
+  const bool scale_loader = kFp8 && threadIdx.x >= kUnits && threadIdx.x < kUnits + kTile;
+
+  uint32_t done = 0;
+  while (true) {
+    // the next sequence among the eight tokens, its tokens and their longest context
+    int lead = -1;
+    for (int g = 0; g < kPfTokens; ++g)
+      if (lead < 0 && !((done >> g) & 1u) && lds_seq[g] >= 0) lead = g;
+    if (lead < 0) break;
+    const int seq = lds_seq[lead];
+    uint32_t members = 0;
+    int N = 0;
+    for (int g = 0; g < kPfTokens; ++g)
+      if (lds_seq[g] == seq) {
+        members |= 1u << g;
+        N = max(N, lds_n[g]);
+      }
+    done |= members;
+    const bool mine = (members >> wave) & 1u;
+    const int64_t sbase = lds_base[lead];
+    const rsrc_t keys = make_rsrc(a.k_idx + sbase * Tile::kRowBytes, (uint32_t)N * Tile::kRowBytes);
+    const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + sbase) : (const void*)a.k_idx,
+                                    kFp8 ? (uint32_t)N * 4u : 0u);
+    u32x4 qa[2][8];
+    if (mine) load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
+    float* srow = a.scores + (int64_t)t * a.ld;
+    const int ntiles = (N + kTile - 1) / kTile;
+
+    // register stages: tile i's unit is loaded kPfStages tiles ahead
+    u32x4 stv[kPfStages];
+    float sts[kPfStages];
+    auto issue = [&](int j, int tile) {
+      // units past the sequence (or idle threads) read zeros
+      const int off = loader ? tile * kTileBytes + ur * Tile::kRowBytes + uc * 16 : (int)0x7ffffff0;
+      stv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off, 0, kNonTemporal));
+      if constexpr (kFp8)
+        sts[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+            scales, scale_loader ? (tile * kTile + (int)threadIdx.x - kUnits) * 4 : (int)0x7ffffff0, 0, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int j = 0; j < kPfStages; ++j) issue(j, j);
+    for (int i0 = 0; i0 < ntiles; i0 += kPfStages) {
+#pragma unroll
+      for (int j = 0; j < kPfStages; ++j) {
+        const int i = i0 + j;
+        // slot i & 1 was last read two tiles ago, before the previous barrier
+        if (loader) *reinterpret_cast<u32x4*>(&lds_tiles[i & 1][lds_off]) = stv[j];
+        if constexpr (kFp8)
+          if (scale_loader) lds_scale[i & 1][threadIdx.x - kUnits] = sts[j];
+        issue(j, i + kPfStages);
+        __syncthreads();
+        if (mine && i < ntiles) {
+          const float ks = kFp8 ? lds_scale[i & 1][lane & 31] : 1.0f;
+          const float sc = score_tile<kFp8>(lds_tiles[i & 1], ks, lane, qa, lds_w[wave]);
+          // tile row r is position 32i + r in this layout
+          const int p = i * kTile + lane;
+          if (lane < 32 && p < n) {
+            srow[p] = sc;
+            if constexpr (kHist) atomicAdd(&lds_hist[wave][score_key(sc) >> (32 - kDigit1Bits)], 1u);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (kHist) {
+    __syncthreads();
+    if (live) {
+      uint32_t* gh = a.hist + (int64_t)t * kHist1;
+      for (int b = lane; b < kHist1; b += 64) gh[b] = lds_hist[wave][b];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_indexer_prefill(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  const dim3 grid((a.num_tokens + kPfTokens - 1) / kPfTokens);
+  if (fp8) {
+    if (fused_hist) indexer_prefill_kernel<true, true><<<grid, kPfThreads, 0, s>>>(a);
+    else indexer_prefill_kernel<true, false><<<grid, kPfThreads, 0, s>>>(a);
+  } else {
+    if (fused_hist) indexer_prefill_kernel<false, true><<<grid, kPfThreads, 0, s>>>(a);
+    else indexer_prefill_kernel<false, false><<<grid, kPfThreads, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;

@@ -37,6 +37,12 @@ struct Carver {
 static_assert((SGA_MAX_LEN + sga::kSelectChunk - 1) / sga::kSelectChunk <= sga::kMaxSelectWgs,
               "the finalize kernel scans one slice count per select workgroup");
 
+// Chunked prefill: tokens share their sequence's keys, so the indexer that
+// reuses each key tile across eight tokens is the faster one.
+bool many_tokens_per_seq(const sga_batch* b) {
+  return (int64_t)b->num_tokens >= (int64_t)sga::kPrefillTokensPerSeq * b->num_seqs;
+}
+
 int64_t bitmap_words(int32_t max_len) { return ((int64_t)max_len + 63) / 64 * 2; }
 
 // ---------------------------------------------------------------- top-k layout
@@ -256,7 +262,9 @@ SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, c
   a.k_scale = k_idx_scale;
   a.scores = scores;
   a.ld = ld;
-  return hip_status(sga::launch_indexer(a, k_idx_dtype == SGA_FP8_E4M3, false, stream));
+  return hip_status(many_tokens_per_seq(batch)
+                        ? sga::launch_indexer_prefill(a, k_idx_dtype == SGA_FP8_E4M3, false, stream)
+                        : sga::launch_indexer(a, k_idx_dtype == SGA_FP8_E4M3, false, stream));
 }
 
 SGA_API size_t sga_topk_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k) {
@@ -357,7 +365,10 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   ia.ctrl = TL.ctrl;
   ia.k = k;
   if (trace) SGA_TRY(record(trace->indexer_begin, stream));
-  SGA_HIP(sga::launch_indexer(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
+  if (many_tokens_per_seq(batch))
+    SGA_HIP(sga::launch_indexer_prefill(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
+  else
+    SGA_HIP(sga::launch_indexer(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
   if (trace) SGA_TRY(record(trace->indexer_end, stream));
   SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
   if (trace) SGA_TRY(record(trace->topk_end, stream));

@@ -77,6 +77,11 @@ struct AttnArgs {
 
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
+// Eight tokens per workgroup sharing each key tile: for batches with many
+// tokens per sequence. With fused_hist it writes each token's digit-1
+// histogram with plain stores (it owns the token).
+hipError_t launch_indexer_prefill(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
+constexpr int kPrefillTokensPerSeq = 64;   // mean tokens per sequence from which it is used
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);

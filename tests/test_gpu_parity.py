@@ -201,3 +201,45 @@ def test_longest_supported_context():
     # 512K positions: the largest visible context the library accepts
     wl = si.build("len512k", [1 << 19], [(0, (1 << 19) - 1), (0, 70000)], seed=16)
     _check_forward(wl)
+
+
+def test_prefill_many_tokens_one_sequence():
+    # at least 64 tokens per sequence: the indexer that shares key tiles across
+    # eight tokens runs (its groups of eight hold one sequence here)
+    rng = np.random.default_rng(17)
+    pos = sorted(rng.choice(5000, size=72, replace=False).tolist())
+    wl = si.build("prefill_one_seq", [5000], [(0, p) for p in pos], seed=17)
+    _check_forward(wl)
+
+
+def test_prefill_mixed_sequences_in_a_group():
+    # tokens of two sequences interleaved: every group of eight spans both
+    rng = np.random.default_rng(18)
+    toks = []
+    for i in range(136):
+        b = i % 2
+        toks.append((b, int(rng.integers(0, [3000, 4500][b]))))
+    wl = si.build("prefill_mixed", [3000, 4500], toks, seed=18)
+    _check_forward(wl)
+
+
+def test_prefill_fp8():
+    rng = np.random.default_rng(19)
+    pos = sorted(rng.choice(4200, size=70, replace=False).tolist())
+    wl = si.build("prefill_fp8", [4200], [(0, p) for p in pos], seed=19, fp8=True)
+    _check_forward(wl)
+
+
+def test_prefill_index_scores_exact():
+    # the unfused scores of the prefill indexer, bit for bit, beyond the chunk of 8
+    rng = np.random.default_rng(20)
+    pos = sorted(rng.choice(3000, size=67, replace=False).tolist())
+    wl = si.build("prefill_scores", [3000], [(0, p) for p in pos], seed=20)
+    say("[index_scores] prefill path")
+    dev = Dev(wl)
+    s = dev.scores().cpu().numpy()
+    ref = run_oracle(wl, keep_scores=True)
+    for i, r in enumerate(ref["scores"]):
+        n = r.shape[0]
+        assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
+        assert np.all(np.isnan(s[i, n:])), "wrote beyond the visible rows"
