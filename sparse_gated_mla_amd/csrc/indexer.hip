@@ -4,7 +4,7 @@
 // of 64 ReLU-scored heads of width 128; cached indexer key width 128.
 //
 // Mapping onto gfx950:
-// - Streaming. A workgroup streams kIndexerChunk positions of one token's key
+// - Streaming. A workgroup streams indexer_chunk() positions of one token's key
 //   cache; its four waves take 32-position tiles in turn. Every load
 //   instruction reads 1 KiB of contiguous keys (16 B per lane), so each wave
 //   instruction covers whole cache lines. Each wave keeps three tiles of loads
@@ -183,8 +183,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   if (threadIdx.x < kIdxHeads) lds_w[threadIdx.x] = a.w[(int64_t)t * kIdxHeads + threadIdx.x];
   __syncthreads();
 
-  const int chunk0 = blockIdx.x * kIndexerChunk;
-  const int len = min(n - chunk0, kIndexerChunk);   // positions of this chunk (<= 0: none)
+  const int chunk0 = blockIdx.x * indexer_chunk(kFp8);
+  const int len = min(n - chunk0, indexer_chunk(kFp8));   // positions of this chunk (<= 0: none)
   if (len > 0) {
     uint8_t* lds = lds_tiles + wave * kTileBytes;
     u32x4 qa[2][8];
@@ -368,7 +368,7 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, bool fp8, bool fused_his
 
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
-  dim3 grid((a.batch.max_len + kIndexerChunk - 1) / kIndexerChunk, a.num_tokens);
+  dim3 grid((a.batch.max_len + indexer_chunk(fp8) - 1) / indexer_chunk(fp8), a.num_tokens);
   if (fp8) {
     if (fused_hist) indexer_kernel<true, true><<<grid, kThreads, 0, s>>>(a);
     else indexer_kernel<true, false><<<grid, kThreads, 0, s>>>(a);

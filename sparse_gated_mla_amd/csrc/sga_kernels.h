@@ -15,7 +15,10 @@ struct TopkCtrl {
   uint32_t above1;      // scores whose top 12 key bits exceed digit1
 };
 
-constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup
+constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup (bf16 keys)
+// fp8 keys are half the bytes: a workgroup takes twice the positions
+// (measured: one round of workgroups streams fp8 keys best)
+__host__ __device__ constexpr int indexer_chunk(bool fp8) { return fp8 ? 2 * kIndexerChunk : kIndexerChunk; }
 constexpr int kSelectChunk = 4096;    // positions per select workgroup
 constexpr int kMaxSelectWgs = 128;    // select workgroups of the longest context (512K)
 constexpr int kAttnTileRows = 32;     // latent rows per attention tile
