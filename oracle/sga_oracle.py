@@ -43,6 +43,15 @@ Storage formats decoded here from their bit-level definitions:
 - OCP E4M3FN: 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; a zero
   exponent field is subnormal; S.1111.111 is NaN; there is no infinity.
 An fp8 row's value is its decoded payload times its fp32 row scale.
+
+Cache append (the step just before the path in decode; FP8 model card
+(nlp.com.ai, "A.X K2 FP8"): FP8 with dynamic, per-row activation scaling).
+The new token's 576-wide latent row and 128-wide indexer key go into row
+seq_start[b] + p of their caches. For an fp8 cache the row scale is
+max|x| / 448 and each payload is x / scale rounded to the nearest E4M3FN value,
+ties to the even code, saturating at 448; both divisions are done in binary32,
+the precision the stored scale has. A row of zeros gets scale 1. -0 and
+negative values that round to zero keep the sign bit.
 """
 from __future__ import annotations
 
@@ -52,7 +61,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 __all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_scores",
-           "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT"]
+           "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT",
+           "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append"]
 
 D_LATENT = 512
 
@@ -81,6 +91,60 @@ def e4m3fn_table() -> np.ndarray:
 
 
 _E4M3 = e4m3fn_table()
+
+
+# the finite non-negative E4M3FN codes (0x00..0x7E) in increasing value
+_POS_CODES = np.arange(0x7F, dtype=np.uint8)
+_POS_VALS = _E4M3[:0x7F]
+
+
+def encode_e4m3fn(x: np.ndarray) -> np.ndarray:
+    """Each value to the nearest E4M3FN code, ties to the even code, |x| > 448
+    saturating to 448; the sign bit follows the sign of x (-0 included)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), _POS_VALS[-1])
+    hi = np.searchsorted(_POS_VALS, a, side="left")          # first value >= a
+    hi = np.minimum(hi, len(_POS_VALS) - 1)
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_VALS[lo]
+    d_hi = _POS_VALS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (_POS_CODES[hi] % 2 == 0))
+    code = np.where(pick_hi, _POS_CODES[hi], _POS_CODES[lo]).astype(np.uint8)
+    code = np.where(d_hi == 0, _POS_CODES[hi], code).astype(np.uint8)   # exact values
+    return code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+
+
+def quantize_rows_e4m3fn(x: np.ndarray):
+    """Rows [n, D] (binary32 values) -> (uint8 payloads [n, D], float32 scales [n]).
+    scale = max|x| / 448 in binary32 (1 for a zero row); payload = E4M3FN(x / scale)."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    q = (x / scale[:, None]).astype(np.float32)
+    return encode_e4m3fn(q), scale
+
+
+def cache_append(token_seq, token_pos, seq_start, seq_len, cache_rows: int, rows: np.ndarray,
+                 fmt: str):
+    """The rows the append writes: {cache row: (payload row, scale or None)}.
+    rows: [T, D] bf16 bit patterns (uint16). fmt: "bf16" (copied bits) or
+    "e4m3fn" (quantised per row). A token whose position lies outside its
+    sequence's rows, or whose row lies outside the cache, writes nothing."""
+    out = {}
+    vals = decode_bf16(rows).astype(np.float32)
+    for t in range(len(token_seq)):
+        b, p = int(token_seq[t]), int(token_pos[t])
+        if b < 0 or b >= len(seq_len) or p < 0 or p >= int(seq_len[b]):
+            continue
+        r = int(seq_start[b]) + p
+        if r < 0 or r >= cache_rows:
+            continue
+        if fmt == "bf16":
+            out[r] = (np.asarray(rows[t], dtype=np.uint16).copy(), None)
+        else:
+            pay, sc = quantize_rows_e4m3fn(vals[t:t + 1])
+            out[r] = (pay[0], np.float32(sc[0]))
+    return out
 
 
 def decode_e4m3fn(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:

@@ -50,6 +50,61 @@ def check_e4m3fn_table(orc):
     assert scaled.tolist() == [[0.25, 112.0]]
 
 
+def check_e4m3fn_encode(orc):
+    # against torch's float8_e4m3fn cast (round to nearest, ties to even): random
+    # values over many magnitudes, every midpoint between neighbours, every
+    # representable value, both signs
+    rng = np.random.default_rng(0)
+    x = rng.normal(size=20000) * rng.choice([1e-3, 0.1, 1.0, 100.0], size=20000)
+    x = np.clip(x, -448.0, 448.0).astype(np.float32)
+    vals = orc.e4m3fn_table()[:0x7F]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    x = np.concatenate([x, mids, -mids, vals.astype(np.float32), -vals.astype(np.float32)])
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = orc.encode_e4m3fn(x.astype(np.float64))
+    assert np.array_equal(got, ref), "E4M3FN encode disagrees with torch.float8_e4m3fn"
+    # the reading's saturation at 448, and the sign of zero
+    assert orc.encode_e4m3fn(np.array([500.0, -1e6, -0.0, 0.0])).tolist() == [0x7E, 0xFE, 0x80, 0x00]
+
+
+def check_quantize_rows(orc):
+    rng = np.random.default_rng(1)
+    x = (rng.normal(size=(64, 576)) / 24).astype(np.float32)
+    x[5] *= 1e-6              # small rows still use the full range
+    x[3] = 0.0
+    pay, sc = orc.quantize_rows_e4m3fn(x)
+    dec = orc.decode_e4m3fn(pay, sc)
+    table = orc.e4m3fn_table()
+    for i in range(len(x)):
+        if i == 3:
+            assert sc[i] == 1.0 and not pay[i].any(), "a zero row"
+            continue
+        # the row's largest magnitude lands on the largest code, 448
+        assert np.abs(table[pay[i]]).max() == 448.0
+        # round to nearest: the error is at most half the code spacing (1/8 of
+        # the binade, 2^-9 below the normals) times the scale
+        a = np.abs(x[i].astype(np.float64)) / float(sc[i])
+        spacing = np.where(a >= 2.0 ** -6, 2.0 ** (np.floor(np.log2(np.maximum(a, 2.0 ** -6))) - 3), 2.0 ** -9)
+        err = np.abs(dec[i] - x[i].astype(np.float64))
+        assert np.all(err <= 0.5 * spacing * float(sc[i]) * (1 + 1e-6)), i
+
+
+def check_cache_append(orc):
+    # sequence 0 at rows 0..4, sequence 1 at rows 10..12
+    token_seq = np.array([0, 1, 1, 2, 0], np.int32)
+    token_pos = np.array([4, 2, 3, 0, -1], np.int32)
+    seq_start = np.array([0, 10], np.int64)
+    seq_len = np.array([5, 3], np.int32)
+    rows = np.arange(5 * 8, dtype=np.uint16).reshape(5, 8) + 0x3F80
+    got = orc.cache_append(token_seq, token_pos, seq_start, seq_len, 13, rows, "bf16")
+    assert sorted(got) == [4, 12], sorted(got)
+    assert np.array_equal(got[4][0], rows[0]) and np.array_equal(got[12][0], rows[1])
+    q = orc.cache_append(token_seq, token_pos, seq_start, seq_len, 13, rows, "e4m3fn")
+    assert sorted(q) == [4, 12]
+    assert np.allclose(orc.decode_e4m3fn(q[4][0][None], np.array([q[4][1]]))[0],
+                       orc.decode_bf16(rows[0]), rtol=1 / 16, atol=0)
+
+
 # ---------------------------------------------------------------- indexer
 def check_indexer_worked_example(orc):
     g = _golden("indexer_worked_example.json")
@@ -313,4 +368,5 @@ ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_exampl
               check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
               check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
               check_attention_vs_sdpa, check_attention_special_cases, check_gate,
-              check_forward_dense_limit, check_forward_selects_by_indexer, check_forward_fp8_store]
+              check_forward_dense_limit, check_forward_selects_by_indexer, check_forward_fp8_store,
+              check_e4m3fn_encode, check_quantize_rows, check_cache_append]

@@ -86,6 +86,28 @@ def _bad_e4m3_table():
     return t
 
 
+def _encode_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = base.e4m3fn_table()[:0x7F]
+    a = np.minimum(np.abs(x), 448.0)
+    code = np.array([int(np.argmin(np.abs(vals - v) - 1e-12 * vals)) for v in a], np.uint8)
+    return code | np.where(np.signbit(x), np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+
+
+def _quantize_scale_240(x):
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.max(np.abs(x), axis=1).astype(np.float32)
+    scale = np.where(amax > 0, amax / np.float32(240.0), np.float32(1.0)).astype(np.float32)
+    return base.encode_e4m3fn((x / scale[:, None]).astype(np.float32)), scale
+
+
+def _append_row_plus_one(token_seq, token_pos, seq_start, seq_len, cache_rows, rows, fmt):
+    got = _ORIG_APPEND(token_seq, token_pos, seq_start, seq_len, cache_rows, rows, fmt)
+    return {r + 1: v for r, v in got.items()}
+
+
+_ORIG_APPEND = base.cache_append
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -96,6 +118,9 @@ MUTANTS = {
     "lse_in_base_2": dict(sparse_mla=_lse_log2),
     "gate_sign_flipped": dict(sigmoid_gate=_gate_sign),
     "e4m3_subnormals": dict(e4m3fn_table=_bad_e4m3_table),
+    "e4m3_encode_ties_away": dict(encode_e4m3fn=_encode_ties_away),
+    "quantize_scale_240": dict(quantize_rows_e4m3fn=_quantize_scale_240),
+    "append_row_off_by_one": dict(cache_append=_append_row_plus_one),
 }
 
 
