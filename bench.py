@@ -68,6 +68,7 @@ class HipEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.events = []
 
     def create(self) -> ctypes.c_void_p:
@@ -77,6 +78,11 @@ class HipEvents:
             raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
         self.events.append(e)
         return e
+
+    def record(self, e, stream: int):
+        rc = self.hip.hipEventRecord(e, ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
 
     def elapsed_ms(self, a, b) -> float:
         ms = ctypes.c_float()
@@ -126,6 +132,48 @@ def step_bytes(wl) -> int:
     sel_rows = int(np.minimum(visible(wl), wl.k).sum())
     per_tok = 64 * 576 * 2 + 64 * 4 + 64 * 512 * 4 + 64 * 4
     return indexer_bytes(wl) + sel_rows * per_row + wl.num_tokens * per_tok
+
+
+def append_bytes(wl) -> int:
+    """Algorithmic bytes of one cache append of every token's new rows: the
+    bf16 latent (576) and indexer key (128) read, the token's metadata
+    (sequence, position, start, length: 20 bytes) read, and the rows written
+    in the cache format (plus one fp32 scale per row for fp8)."""
+    out = (576 + 128 + 8) if wl.fp8 else (576 + 128) * 2
+    return wl.num_tokens * ((576 + 128) * 2 + 20 + out)
+
+
+def time_cache_append(wl, s, ev, reps: int) -> dict:
+    """Times sga_cache_append of one new row per token into the step's caches
+    (the write that precedes a decode step), one event pair per launch."""
+    dev = s["kv"].device
+    lat, key = si.append_rows(wl.num_tokens, seed=99)
+    lat, key = lat.to(dev), key.to(dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    append = lambda: sga.sga_cache_append(s["batch"], lat, key, s["kv"], s["kv_scale"], s["k_idx"],
+                                          s["k_idx_scale"])
+    for _ in range(3):
+        append()
+    torch.cuda.synchronize()
+    # a spin kernel keeps the GPU busy while the host queues the timed launches,
+    # so each event pair brackets one kernel and not the host's call overhead
+    s0, s1 = ev.create(), ev.create()
+    ev.record(s0, stream)
+    torch.cuda._sleep(50_000_000)
+    ev.record(s1, stream)
+    t0 = time.perf_counter()
+    for a, b in pairs:
+        ev.record(a, stream)
+        append()
+        ev.record(b, stream)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    us = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    nb = append_bytes(wl)
+    return {"us": round(us, 2), "algorithmic_bytes": nb, "gbps": round(nb / (us * 1e-6) / 1e9, 1),
+            "tokens": wl.num_tokens, "spin_ms": round(ev.elapsed_ms(s0, s1), 3),
+            "host_enqueue_ms": round(host_ms, 3)}
 
 
 # ---------------------------------------------------------------- traffic
@@ -302,6 +350,7 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
+    append = time_cache_append(wl, sets[0], ev, reps=20)
     idx_ms = [ev.elapsed_ms(tr[i].indexer_begin, tr[i].indexer_end) for i in range(K)]
     topk_ms = [ev.elapsed_ms(tr[i].indexer_end, tr[i].topk_end) for i in range(K)]
     attn_ms = [ev.elapsed_ms(tr[i].topk_end, tr[i].attn_end) for i in range(K)]
@@ -339,7 +388,8 @@ def main():
                   "indexer_us": round(float(np.mean(idx_ms)) * 1e3, 2),
                   "topk_us": round(float(np.mean(topk_ms)) * 1e3, 2),
                   "attention_us": round(float(np.mean(attn_ms)) * 1e3, 2),
-                  "input_copies": len(sets)},
+                  "input_copies": len(sets),
+                  "cache_append": append},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

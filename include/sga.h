@@ -196,6 +196,36 @@ SGA_API sga_status sga_forward(const sga_batch* batch,
                                const sga_trace* trace, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
+/*
+ * sga_cache_append: writes each token's new cached rows (the step just before
+ * the path in decode).
+ * Source: the FP8 model card (nlp.com.ai, "A.X K2 FP8": FP8 with dynamic
+ * per-row scaling) and the fact sheet's per-token cache row (512 latent + 64
+ * RoPE, 128-wide indexer key).
+ *
+ * Token t of sequence b at position p writes flat row r = seq_start[b] + p:
+ *   kv[r]    <- latent[t]  (576 values),  when latent and kv are non-NULL;
+ *   k_idx[r] <- idx_key[t] (128 values),  when idx_key and k_idx are non-NULL.
+ *   latent  [T,576] bf16, idx_key [T,128] bf16, row-major, 16-byte aligned.
+ * Each pair is given whole or left out whole (both NULL): one NULL and one
+ * non-NULL is SGA_ERR_INVALID_ARG. Caches are 16-byte aligned, scale arrays
+ * 4-byte aligned; the caller owns every buffer and the call only writes the
+ * rows (and scales) named above, asynchronously on `stream`.
+ * A bf16 cache gets the bits copied. An SGA_FP8_E4M3 cache gets, per row,
+ *   scale = max|x| / 448 (binary32 division; 1 for a row of zeros), stored in
+ *   kv_scale[r] / k_idx_scale[r], and payload = x / scale (binary32) rounded to
+ *   the nearest E4M3FN value, ties to the even code, saturating at 448; the
+ *   sign bit follows x (so -0 gives 0x80).
+ * The scale arrays must be NULL for a bf16 cache and non-NULL for fp8.
+ * A token with b outside [0, num_seqs), p outside [0, seq_len[b]) or r outside
+ * [0, cache_rows) writes nothing. Tokens writing the same row race; the
+ * caller keeps rows distinct. max_len is checked as for the other calls but
+ * not otherwise used. Inputs must be finite.
+ */
+SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,
+                                    void* kv, float* kv_scale, sga_dtype kv_dtype, void* k_idx,
+                                    float* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream);
+
 SGA_API const char* sga_status_string(sga_status status);
 /* Library version as major*10000 + minor*100 + patch. */
 SGA_API int sga_version(void);

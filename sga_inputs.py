@@ -175,6 +175,20 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
                     k=k, sm_scale=sm_scale, meta={"seed": seed, "fp8": fp8})
 
 
+def append_rows(num_tokens: int, seed: int, *, kv_sigma: float = 1.0 / 24.0, key_sigma: float = 1.0,
+                spread: int = 8):
+    """New cache rows for a cache append: latent rows [T, 576] and indexer keys
+    [T, 128], both bf16. Each row is N(0, sigma^2) times 2**u with u drawn
+    uniformly from [-spread, spread], so the per-row fp8 scales span a wide
+    range. Draw order: latent normals, latent exponents, key normals, key exponents."""
+    rng = np.random.default_rng(seed)
+    lat = rng.standard_normal(size=(num_tokens, D_QK), dtype=np.float32) * np.float32(kv_sigma)
+    lat *= np.ldexp(np.float32(1.0), rng.integers(-spread, spread + 1, size=(num_tokens, 1))).astype(np.float32)
+    key = rng.standard_normal(size=(num_tokens, IDX_DIM), dtype=np.float32) * np.float32(key_sigma)
+    key *= np.ldexp(np.float32(1.0), rng.integers(-spread, spread + 1, size=(num_tokens, 1))).astype(np.float32)
+    return _bf16(lat), _bf16(key)
+
+
 def config(i: int, seed: Optional[int] = None) -> Workload:
     """The five workloads: seed defaults to the workload's number."""
     s = i if seed is None else seed

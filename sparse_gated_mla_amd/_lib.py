@@ -23,7 +23,7 @@ HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK = 64, 64, 128, 512, 576
 
 EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_workspace_size",
            "sga_sparse_mla_attn", "sga_forward_workspace_size", "sga_forward",
-           "sga_status_string", "sga_version")
+           "sga_cache_append", "sga_status_string", "sga_version")
 
 
 class SgaBatch(ctypes.Structure):
@@ -71,6 +71,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "sga_forward_workspace_size": ([i32, i32, i32], sz),
         "sga_forward": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, f32, vp, vp,
                          vp, vp, vp, sz, tp, vp], ctypes.c_int),
+        "sga_cache_append": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp], ctypes.c_int),
         "sga_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sga_version": ([], ctypes.c_int),
     }
@@ -245,3 +246,26 @@ def sga_forward(batch: Batch, q_idx, w, k_idx, k_idx_scale, q_abs, kv, kv_scale,
         _ptr(kv), _ptr(kv_scale), vdt, k, float(sm_scale), _ptr(gate), _ptr(out), _ptr(lse),
         _ptr(indices_out), _ptr(ws), ws.numel(), None if trace is None else ctypes.byref(trace),
         _stream(q_abs)))
+
+
+def sga_cache_append(batch: Batch, latent=None, idx_key=None, kv=None, kv_scale=None,
+                     k_idx=None, k_idx_scale=None) -> None:
+    """Writes token t's latent row into kv[seq_start[b] + p] and its indexer key into
+    k_idx[seq_start[b] + p]; an fp8 cache (float8_e4m3fn) gets one fp32 scale per row."""
+    T = batch.num_tokens
+    kdt = vdt = SGA_BF16
+    if latent is not None:
+        _check(latent, "latent", (torch.bfloat16,), (T, D_QK))
+    if idx_key is not None:
+        _check(idx_key, "idx_key", (torch.bfloat16,), (T, IDX_DIM))
+    if kv is not None:
+        _check(kv, "kv", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, D_QK))
+        vdt = _store_dtype(kv, kv_scale, "kv")
+    if k_idx is not None:
+        _check(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, IDX_DIM))
+        kdt = _store_dtype(k_idx, k_idx_scale, "k_idx")
+    ref = next((t for t in (latent, idx_key, kv, k_idx) if t is not None), batch.token_seq)
+    b = batch.c()
+    _raise("sga_cache_append", load().sga_cache_append(
+        ctypes.byref(b), _ptr(latent), _ptr(idx_key), _ptr(kv), _ptr(kv_scale), vdt, _ptr(k_idx),
+        _ptr(k_idx_scale), kdt, _stream(ref)))

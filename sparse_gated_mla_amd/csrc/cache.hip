@@ -1,0 +1,115 @@
+// Cache append: the step just before the path in decode. Each token's new
+// 576-wide latent row and 128-wide indexer key are written into row
+// seq_start[b] + p of their caches, as bf16 (copied) or as OCP E4M3FN with one
+// fp32 scale per row.
+// Source: FP8 model card (nlp.com.ai, "A.X K2 FP8"): FP8 with dynamic, per-row
+// activation scaling; fact sheet (archdb, "A.X K2"): per token the cache holds
+// the 512 latent + 64 RoPE values and the 128-wide indexer key.
+//
+// fp8: scale = max|x| / 448 (binary32 division; 1 for a row of zeros), and each
+// payload is x / scale rounded to the nearest E4M3FN value, ties to the even
+// code, saturating at 448, the sign bit following x. The rounding is done from
+// the format's definition: a value in binade [2^e, 2^(e+1)) (e >= -6) has code
+// spacing 2^(e-3), below 2^-6 the spacing is 2^-9; scaling by the spacing is
+// exact, rintf rounds to nearest even, and the result is re-encoded.
+//
+// Mapping: one workgroup of two waves per token; wave 0 writes the latent row
+// (72 16-byte units, one or two per lane), wave 1 the indexer key (16 units).
+#include "sga_kernels.h"
+
+namespace sga {
+namespace {
+
+__device__ __forceinline__ uint32_t e4m3fn_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fminf(fabsf(x), 448.0f);
+  int ea;
+  frexpf(a, &ea);                       // a = f * 2^ea, f in [0.5, 1)
+  const int eb = max(ea - 1, -6);       // binade exponent, subnormals share -6
+  const float v = ldexpf(rintf(ldexpf(a, 3 - eb)), eb - 3);   // nearest code value
+  if (v == 0.0f) return sign;
+  int ev;
+  frexpf(v, &ev);
+  ev -= 1;                              // floor(log2 v)
+  if (ev < -6) return sign | (uint32_t)ldexpf(v, 9);          // subnormal: v / 2^-9
+  const uint32_t m = (uint32_t)ldexpf(v, 3 - ev) - 8u;        // v / 2^(ev-3) in [8, 16)
+  return sign | ((uint32_t)(ev + 7) << 3) | m;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// One row of `units` 16-byte units (8 bf16 each), lane l taking units l and l + 64.
+template <int kUnits>
+__device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                           float* __restrict__ scale_out, bool fp8, int lane) {
+  constexpr int kPer = (kUnits + 63) / 64;
+  u32x4 v[kPer];
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int u = lane + 64 * j;
+    v[j] = u32x4{0u, 0u, 0u, 0u};
+    if (u < kUnits) v[j] = *reinterpret_cast<const u32x4*>(src + 8 * u);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[j][c])), fabsf(bf16_hi(v[j][c]))));
+  }
+  if (!fp8) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int u = lane + 64 * j;
+      if (u < kUnits) *reinterpret_cast<u32x4*>(dst + 16 * u) = v[j];
+    }
+    return;
+  }
+  amax = wave_max(amax);
+  const float scale = amax > 0.0f ? amax / 448.0f : 1.0f;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int u = lane + 64 * j;
+    if (u < kUnits) {
+      u32x2 out;
+      uint32_t b[8];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        b[2 * c] = e4m3fn_encode(bf16_lo(v[j][c]) / scale);
+        b[2 * c + 1] = e4m3fn_encode(bf16_hi(v[j][c]) / scale);
+      }
+      out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+      out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+      *reinterpret_cast<u32x2*>(dst + 8 * u) = out;
+    }
+  }
+  if (lane == 0) *scale_out = scale;
+}
+
+__global__ __launch_bounds__(128) void cache_append_kernel(CacheArgs a) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int b = a.batch.token_seq[t];
+  if (b < 0 || b >= a.batch.num_seqs) return;
+  const int p = a.batch.token_pos[t];
+  if (p < 0 || p >= a.batch.seq_len[b]) return;
+  const int64_t row = a.batch.seq_start[b] + p;
+  if (row < 0 || row >= a.batch.cache_rows) return;
+  if (wave == 0) {
+    if (!a.latent || !a.kv) return;
+    append_row<kDQK / 8>(a.latent + (int64_t)t * kDQK, a.kv + row * (a.kv_fp8 ? kDQK : 2 * kDQK),
+                         a.kv_fp8 ? a.kv_scale + row : nullptr, a.kv_fp8, lane);
+  } else {
+    if (!a.key || !a.k_idx) return;
+    append_row<kIdxDim / 8>(a.key + (int64_t)t * kIdxDim,
+                            a.k_idx + row * (a.k_idx_fp8 ? kIdxDim : 2 * kIdxDim),
+                            a.k_idx_fp8 ? a.k_idx_scale + row : nullptr, a.k_idx_fp8, lane);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cache_append(const CacheArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  cache_append_kernel<<<a.num_tokens, 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sga

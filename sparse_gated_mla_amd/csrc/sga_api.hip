@@ -11,6 +11,7 @@ namespace {
 
 using sga::AttnArgs;
 using sga::BatchView;
+using sga::CacheArgs;
 using sga::IndexerArgs;
 using sga::TopkArgs;
 using sga::TopkCtrl;
@@ -119,6 +120,7 @@ sga_status check_batch(const sga_batch* b) {
 
 sga_status check_store(const void* data, const float* scale, sga_dtype dt) {
   if (!data || !aligned16(data)) return SGA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(scale) % alignof(float) != 0) return SGA_ERR_INVALID_ARG;
   if (dt == SGA_BF16) return scale ? SGA_ERR_INVALID_ARG : SGA_OK;
   if (dt == SGA_FP8_E4M3) return scale ? SGA_OK : SGA_ERR_INVALID_ARG;
   return SGA_ERR_UNSUPPORTED;
@@ -376,6 +378,35 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
                         out, lse, plan, AL, stream));
   if (trace) SGA_TRY(record(trace->attn_end, stream));
   return SGA_OK;
+}
+
+SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,
+                                    void* kv, float* kv_scale, sga_dtype kv_dtype, void* k_idx,
+                                    float* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (!latent != !kv || !idx_key != !k_idx) return SGA_ERR_INVALID_ARG;
+  const bool do_kv = latent != nullptr, do_key = idx_key != nullptr;
+  if (do_kv) {
+    if (!aligned16(latent)) return SGA_ERR_INVALID_ARG;
+    SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+  }
+  if (do_key) {
+    if (!aligned16(idx_key)) return SGA_ERR_INVALID_ARG;
+    SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
+  }
+  if (batch->num_tokens == 0 || (!do_kv && !do_key)) return SGA_OK;
+  CacheArgs a;
+  a.batch = view_of(batch);
+  a.num_tokens = batch->num_tokens;
+  a.latent = do_kv ? static_cast<const uint16_t*>(latent) : nullptr;
+  a.key = do_key ? static_cast<const uint16_t*>(idx_key) : nullptr;
+  a.kv = do_kv ? static_cast<uint8_t*>(kv) : nullptr;
+  a.kv_scale = do_kv ? kv_scale : nullptr;
+  a.kv_fp8 = do_kv && kv_dtype == SGA_FP8_E4M3;
+  a.k_idx = do_key ? static_cast<uint8_t*>(k_idx) : nullptr;
+  a.k_idx_scale = do_key ? k_idx_scale : nullptr;
+  a.k_idx_fp8 = do_key && k_idx_dtype == SGA_FP8_E4M3;
+  return hip_status(sga::launch_cache_append(a, stream));
 }
 
 }  // extern "C"

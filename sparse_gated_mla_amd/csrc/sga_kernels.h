@@ -78,7 +78,22 @@ struct AttnArgs {
                            // columns 0..255 and of columns 256..511
 };
 
+// Cache append: token t writes row seq_start[b] + p of each given cache.
+struct CacheArgs {
+  BatchView batch;
+  int num_tokens;
+  const uint16_t* latent;  // [T,576] bf16, or null
+  const uint16_t* key;     // [T,128] bf16, or null
+  uint8_t* kv;             // [rows,576] bf16 or fp8 payload
+  float* kv_scale;         // [rows] for fp8
+  bool kv_fp8;
+  uint8_t* k_idx;          // [rows,128] bf16 or fp8 payload
+  float* k_idx_scale;      // [rows] for fp8
+  bool k_idx_fp8;
+};
+
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
+hipError_t launch_cache_append(const CacheArgs& a, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
 // Eight tokens per workgroup sharing each key tile: for batches with many
 // tokens per sequence. With fused_hist it writes each token's digit-1

@@ -25,9 +25,9 @@ def declared_functions():
     return re.findall(r"SGA_API\s+[\w\s\*]+?\b(sga_\w+)\s*\(", text)
 
 
-def test_header_declares_the_four_entry_points():
+def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("sga_index_scores", "sga_topk", "sga_sparse_mla_attn", "sga_forward"):
+    for n in ("sga_index_scores", "sga_topk", "sga_sparse_mla_attn", "sga_forward", "sga_cache_append"):
         assert n in names
 
 
@@ -123,6 +123,32 @@ def test_forward_rejects_bad_arguments(lib):
     assert call(tau=math.inf) == 1
     assert call(k=0) == 1
     assert call(kdt=1) == 1
+
+
+def test_cache_append_rejects_bad_arguments(lib):
+    b = _batch()
+
+    def call(bb=b, lat=FAKE, kv=FAKE, kvs=None, kvdt=0, key=FAKE, kidx=FAKE, ks=None, kdt=0):
+        return lib.sga_cache_append(ctypes.byref(bb), lat, key, kv, kvs, kvdt, kidx, ks, kdt, None)
+    assert call(lat=None) == 1                 # half a pair
+    assert call(kv=None) == 1
+    assert call(key=None) == 1
+    assert call(kidx=None) == 1
+    assert call(lat=FAKE_ODD) == 1
+    assert call(key=FAKE_ODD) == 1
+    assert call(kv=FAKE_ODD) == 1
+    assert call(kidx=FAKE_ODD) == 1
+    assert call(kvdt=1) == 1                   # fp8 cache without scales
+    assert call(kdt=1) == 1
+    assert call(kvs=FAKE) == 1                 # bf16 cache with scales
+    assert call(kvdt=1, kvs=ctypes.c_void_p(0x10002)) == 1   # misaligned scales
+    assert call(kvdt=5) == 2
+    assert call(_batch(T=-1)) == 1
+    assert call(_batch(ptr=0)) == 1
+    assert call(_batch(max_len=(1 << 19) + 1)) == 2
+    assert call(_batch(T=0, ptr=0), lat=None, kv=None, key=None, kidx=None) == 0
+    assert call(_batch(T=0, ptr=0)) == 0       # empty batch: nothing launched
+    assert call(lat=None, kv=None, key=None, kidx=None) == 0   # nothing to write
 
 
 def test_workspace_sizes_grow_with_the_problem(lib):
