@@ -7,6 +7,27 @@
 
 namespace sga {
 
+// DPP source of a row shift or row broadcast; lanes with no source (or in a
+// row the mask leaves out) read 0, the identity of the sums below.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ uint32_t dpp_shifted(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, kRowMask, 0xf, false);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, in registers: shifts by
+// 1, 2, 4 and 8 lanes inside each 16-lane row (DPP row_shr), then the last
+// lane of rows 0 and 2 added into rows 1 and 3 (row_bcast:15), then the last
+// lane of row 1 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_shifted<0x111, 0xf>(x);
+  x += dpp_shifted<0x112, 0xf>(x);
+  x += dpp_shifted<0x114, 0xf>(x);
+  x += dpp_shifted<0x118, 0xf>(x);
+  x += dpp_shifted<0x142, 0xa>(x);
+  x += dpp_shifted<0x143, 0xc>(x);
+  return x;
+}
+
 // Exclusive prefix sum of one uint32 per thread over a workgroup of NT threads
 // (NT a multiple of 64). scratch: NT/64 + 1 words of LDS. All threads must call.
 template <int NT>
@@ -81,12 +102,7 @@ __device__ __forceinline__ void block_cut(const uint32_t* h, int nbins, uint32_t
   const int cnt = top <= 0 ? 0 : (top < per ? top : per);
   uint32_t sum = 0;
   for (int i = 1; i <= cnt; ++i) sum += h[top - i];
-  uint32_t x = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
+  const uint32_t x = wave_incl_scan(sum);
   if (lane == 63) scratch[wid] = x;
   __syncthreads();
   uint32_t before = 0;
@@ -120,22 +136,21 @@ __device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_
                                                  uint32_t& a_before, uint32_t& b_before) {
   constexpr int kWaves = NT / 64;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  unsigned long long v = (unsigned long long)a | ((unsigned long long)b << 32), x = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const unsigned long long y = __shfl_up(x, off);
-    if (lane >= off) x += y;
+  const uint32_t xa = wave_incl_scan(a), xb = wave_incl_scan(b);
+  if (lane == 63) {
+    scratch[wid] = xa;
+    scratch[kWaves + wid] = xb;
   }
-  unsigned long long* s64 = reinterpret_cast<unsigned long long*>(scratch);
-  if (lane == 63) s64[wid] = x;
   __syncthreads();
-  unsigned long long before = 0;
+  uint32_t ba = 0, bb = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w)
-    if (w < wid) before += s64[w];
-  const unsigned long long e = before + x - v;
-  a_before = (uint32_t)e;
-  b_before = (uint32_t)(e >> 32);
+    if (w < wid) {
+      ba += scratch[w];
+      bb += scratch[kWaves + w];
+    }
+  a_before = ba + xa - a;
+  b_before = bb + xb - b;
   __syncthreads();
 }
 
@@ -159,21 +174,62 @@ __device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* 
   }
 }
 
-// First radix cut of a token from its global digit-1 histogram: the digit of
-// the k-th largest score and the count of scores with a larger digit.
-// Every thread of the workgroup gets the result. lds_hist: kHist1 words;
-// scratch: at least NT/64 + 2 words.
-template <int NT>
-__device__ __forceinline__ void hist1_cut(const uint32_t* ghist, uint32_t* lds_hist, uint32_t k,
-                                          uint32_t* scratch, uint32_t& digit1, uint32_t& above1) {
-  static_assert(kHist1 % NT == 0, "whole bins per thread");
-  uint32_t h[kHist1 / NT];   // every load in flight before the first LDS store
+// A radix cut straight from a histogram in global memory, with no LDS copy.
+// Thread j holds bins [nbins - P(j+1), nbins - Pj) in registers (P = nbins/NT,
+// a multiple of 4), so thread 0 holds the top bins. load() issues the loads;
+// cut() waits for them and finds d with S(d+1) < r <= S(d), where S(d) is the
+// sum of the bins >= d, for 1 <= r <= S(0). Every thread gets d, S(d+1) and
+// the count of bin d. scratch: NT/64 + 3 words of LDS, free again on return.
+template <int NT, int NBINS>
+struct HistRun {
+  static constexpr int P = NBINS / NT;
+  static_assert(P % 4 == 0 && P * NT == NBINS, "whole 16-byte runs per thread");
+  u32x4 v[P / 4];
+
+  __device__ __forceinline__ void load(const uint32_t* ghist) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(ghist + NBINS - P * ((int)threadIdx.x + 1));
 #pragma unroll
-  for (int u = 0; u < kHist1 / NT; ++u) h[u] = ghist[u * NT + threadIdx.x];
+    for (int q = 0; q < P / 4; ++q) v[q] = src[q];
+  }
+
+  __device__ __forceinline__ void cut(uint32_t r, uint32_t* scratch, uint32_t& d, uint32_t& above,
+                                      uint32_t& count) const {
+    constexpr int kWaves = NT / 64;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    uint32_t sum = 0;
 #pragma unroll
-  for (int u = 0; u < kHist1 / NT; ++u) lds_hist[u * NT + threadIdx.x] = h[u];
-  __syncthreads();
-  block_cut<NT>(lds_hist, kHist1, k, scratch, digit1, above1);
-}
+    for (int q = 0; q < P / 4; ++q) sum += v[q].x + v[q].y + v[q].z + v[q].w;
+    const uint32_t x = wave_incl_scan(sum);
+    if (lane == 63) scratch[wid] = x;
+    __syncthreads();
+    uint32_t before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (w < wid) before += scratch[w];
+    const uint32_t incl = before + x, excl = incl - sum;
+    if (excl < r && r <= incl) {
+      // bins from the top of this run down: element e of v[q] is bin base + 4q + e
+      const int base = NBINS - P * ((int)threadIdx.x + 1);
+      uint32_t acc = excl;
+      bool found = false;
+#pragma unroll
+      for (int i = P - 1; i >= 0; --i) {
+        const uint32_t c = v[i / 4][i % 4];
+        if (!found && acc + c >= r) {
+          scratch[kWaves] = (uint32_t)(base + i);
+          scratch[kWaves + 1] = acc;
+          scratch[kWaves + 2] = c;
+          found = true;
+        }
+        acc += c;
+      }
+    }
+    __syncthreads();
+    d = scratch[kWaves];
+    above = scratch[kWaves + 1];
+    count = scratch[kWaves + 2];
+    __syncthreads();
+  }
+};
 
 }  // namespace sga

@@ -58,7 +58,6 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
-  __shared__ uint32_t lds_hist[kHist1];
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t lds_count;
   constexpr int kSteps = kSelectChunk / kSelThreads;   // 64-position steps per wave
@@ -72,15 +71,18 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   const int c1 = min(n, c0 + kSelectChunk);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* srow = a.scores + (int64_t)t * a.ld;
-  // issue every score load of this workgroup at once
+  // the histogram first, then every score load of this workgroup: the cut is
+  // taken while the scores are still in flight
+  HistRun<kSelThreads, kHist1> h1;
+  h1.load(a.hist + (int64_t)t * kHist1);
   float v[kSteps];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i) v[i] = srow[min(c0 + i * kSelThreads + wave * 64 + lane, c1 - 1)];
   if (threadIdx.x == 0) lds_count = 0;
   // first radix cut, taken redundantly by every workgroup of the token from the
   // histogram the previous kernel completed (no cross-workgroup hand-off)
-  uint32_t d1, above1;
-  hist1_cut<kSelThreads>(a.hist + (int64_t)t * kHist1, lds_hist, (uint32_t)a.k, scratch, d1, above1);
+  uint32_t d1, above1, n1;
+  h1.cut((uint32_t)a.k, scratch, d1, above1, n1);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.ctrl[t].digit1 = d1;
     a.ctrl[t].above1 = above1;
@@ -126,15 +128,15 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
 }
 
-// Dynamic LDS: level-2 histogram (4096; then the staged output) | level-3
+// Dynamic LDS: staged output (4096 words) | level-3
 // histogram or short key list (256) | scratch (64) | slice offsets
 // (kMaxSelectWgs + 1) | tie bitmap (words) | selection bitmap (words) |
 // staged candidate positions (lds_cand_cap) | their keys (lds_cand_cap).
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
   constexpr int kFinWaves = kFinThreads / 64;
-  uint32_t* hist2 = lds;
-  uint32_t* hist3 = hist2 + kHist2;
+  uint32_t* out_stage = lds;
+  uint32_t* hist3 = out_stage + kHist2;
   uint32_t* scratch = hist3 + kHist3;
   uint32_t* offs = scratch + 64;
   uint32_t* tie = offs + kMaxSelectWgs + 1;
@@ -160,11 +162,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   const uint32_t r1 = (uint32_t)a.k - a.ctrl[t].above1;  // still needed from the candidates
   uint32_t cnt = 0;
   if (threadIdx.x < nsel) cnt = a.wg_count[(int64_t)t * a.max_select_wgs + threadIdx.x];
-  static_assert(kHist2 % kFinThreads == 0, "whole bins per thread");
-  uint32_t hv[kHist2 / kFinThreads];
-#pragma unroll
-  for (int u = 0; u < kHist2 / kFinThreads; ++u)
-    hv[u] = a.hist2[(int64_t)t * kHist2 + u * kFinThreads + threadIdx.x];
+  HistRun<kFinThreads, kHist2> h2;
+  h2.load(a.hist2 + (int64_t)t * kHist2);
   {
     const uint32_t* sel = a.sel + (int64_t)t * a.words;
     for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
@@ -181,20 +180,13 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
       }
     }
   }
-#pragma unroll
-  for (int u = 0; u < kHist2 / kFinThreads; ++u) hist2[u * kFinThreads + threadIdx.x] = hv[u];
   for (int b = threadIdx.x; b < kHist3; b += kFinThreads) hist3[b] = 0;
   if (threadIdx.x == 0) *n_few = 0;
   // slice offsets: an inclusive scan of the counts by the first waves
   static_assert(kMaxSelectWgs <= kFinThreads, "one count per thread");
   {
-    uint32_t x = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(x, o);
-      if (lane >= o) x += y;
-    }
-    uint32_t* wsum = scratch + 48;   // apart from what block_cut uses next
+    const uint32_t x = wave_incl_scan(cnt);
+    uint32_t* wsum = scratch + 48;   // apart from what the cut uses next
     if (lane == 63 && wave < (kMaxSelectWgs + 63) / 64) wsum[wave] = x;
     __syncthreads();
     if (threadIdx.x < kMaxSelectWgs) {
@@ -205,10 +197,9 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
     if (threadIdx.x == 0) offs[0] = 0;
   }
   // level 2, from the histogram the select kernel counted
-  uint32_t d2, above2;
-  block_cut<kFinThreads>(hist2, kHist2, r1, scratch, d2, above2);
+  uint32_t d2, above2, n3;   // n3: candidates with digit d2, usually a handful
+  h2.cut(r1, scratch, d2, above2, n3);
   const uint32_t r2 = r1 - above2;
-  const uint32_t n3 = hist2[d2];   // candidates with digit d2: usually a handful
   const uint32_t m = offs[nsel];
   const bool staged = m <= (uint32_t)a.lds_cand_cap;
   const uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap;
@@ -300,7 +291,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   block_excl_scan2<kFinThreads>(ns, nt, scratch, s_before, t_before);
   uint32_t o = s_before + min(t_before, ties_kept);
   uint32_t ties_seen = t_before;
-  int32_t* staged_out = reinterpret_cast<int32_t*>(hist2);   // k <= kHist2: the output goes out coalesced
+  int32_t* staged_out = reinterpret_cast<int32_t*>(out_stage);   // k <= kHist2: the output goes out coalesced
   const bool stage_out = a.k <= kHist2;
   for (int i = w0; i < w1; ++i) {
     const uint32_t sbits = selL[i];
