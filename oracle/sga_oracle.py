@@ -52,6 +52,17 @@ max|x| / 448 and each payload is x / scale rounded to the nearest E4M3FN value,
 ties to the even code, saturating at 448; both divisions are done in binary32,
 the precision the stored scale has. A row of zeros gets scale 1. -0 and
 negative values that round to zero keep the sign bit.
+
+MX block-32 cache (fact sheet, Training: MXFP8 E4M3 with one scale per 32
+consecutive elements). The pages give only the granularity; the block rule
+taken here is the Open Compute Project MX format's: each run of 32 elements
+shares one E8M0 scale 2^(e - 127) (e = 0..254; e = 255 is NaN), with
+e - 127 = floor(log2(max|x|)) - 8, 8 being the exponent of E4M3FN's largest
+normal (448 = 1.75 * 2^8), clamped to [-127, 127]; a block of zeros gets
+e = 0. Each element is x / 2^(e - 127) rounded to the nearest E4M3FN value,
+ties to the even code, saturating at 448 (a block whose maximum lies in
+(448, 512) * 2^(e - 127) has its largest elements clamped). The value of a
+stored element is its payload times its block's scale.
 """
 from __future__ import annotations
 
@@ -62,7 +73,8 @@ import numpy as np
 
 __all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_scores",
            "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT",
-           "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append"]
+           "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append", "e8m0_table", "MX_BLOCK",
+           "quantize_blocks_mxfp8", "decode_mxfp8"]
 
 D_LATENT = 512
 
@@ -124,12 +136,51 @@ def quantize_rows_e4m3fn(x: np.ndarray):
     return encode_e4m3fn(q), scale
 
 
+MX_BLOCK = 32
+
+
+def e8m0_table() -> np.ndarray:
+    """The 256 values of E8M0 (an unsigned power-of-two exponent, bias 127; 255 is NaN)."""
+    t = np.ldexp(1.0, np.arange(256) - 127)
+    t[255] = np.nan
+    return t
+
+
+_E8M0 = e8m0_table()
+
+
+def quantize_blocks_mxfp8(x: np.ndarray):
+    """Rows [n, D] (D a multiple of 32) -> (uint8 E4M3FN payloads [n, D], uint8
+    E8M0 block exponents [n, D/32]), one exponent per 32 consecutive elements."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    blocks = x.reshape(n, d // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    exps = np.zeros(amax.shape, dtype=np.uint8)
+    nz = amax > 0
+    _, e2 = np.frexp(amax[nz])                        # amax = f * 2^e2, f in [0.5, 1)
+    exps[nz] = np.clip(e2 - 1 - 8, -127, 127) + 127   # floor(log2 amax) - 8, biased
+    scale = _E8M0[exps]                               # 2^(e - 127)
+    payload = encode_e4m3fn(blocks / scale[:, :, None]).reshape(n, d)
+    return payload, exps
+
+
+def decode_mxfp8(payload: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """uint8 payload rows [n, D] and E8M0 block exponents [n, D/32] -> float64 [n, D]."""
+    p = np.asarray(payload, dtype=np.uint8)
+    n, d = p.shape
+    vals = _E4M3[p].reshape(n, d // MX_BLOCK, MX_BLOCK)
+    return (vals * _E8M0[np.asarray(exps, dtype=np.uint8)][:, :, None]).reshape(n, d)
+
+
 def cache_append(token_seq, token_pos, seq_start, seq_len, cache_rows: int, rows: np.ndarray,
                  fmt: str):
     """The rows the append writes: {cache row: (payload row, scale or None)}.
-    rows: [T, D] bf16 bit patterns (uint16). fmt: "bf16" (copied bits) or
-    "e4m3fn" (quantised per row). A token whose position lies outside its
-    sequence's rows, or whose row lies outside the cache, writes nothing."""
+    rows: [T, D] bf16 bit patterns (uint16). fmt: "bf16" (copied bits),
+    "e4m3fn" (quantised per row; the scale is a float32) or "mxfp8" (quantised
+    per 32-element block; the scale is the row's uint8 E8M0 exponents). A token
+    whose position lies outside its sequence's rows, or whose row lies outside
+    the cache, writes nothing."""
     out = {}
     vals = decode_bf16(rows).astype(np.float32)
     for t in range(len(token_seq)):
@@ -141,6 +192,9 @@ def cache_append(token_seq, token_pos, seq_start, seq_len, cache_rows: int, rows
             continue
         if fmt == "bf16":
             out[r] = (np.asarray(rows[t], dtype=np.uint16).copy(), None)
+        elif fmt == "mxfp8":
+            pay, ex = quantize_blocks_mxfp8(vals[t:t + 1])
+            out[r] = (pay[0], ex[0])
         else:
             pay, sc = quantize_rows_e4m3fn(vals[t:t + 1])
             out[r] = (pay[0], np.float32(sc[0]))
@@ -155,16 +209,18 @@ def decode_e4m3fn(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Store:
-    """A flat cache: raw bits per row plus the format ('bf16' or 'e4m3fn')."""
-    bits: np.ndarray                  # uint16 [rows, D] (bf16) or uint8 [rows, D] (e4m3fn)
+    """A flat cache: raw bits per row plus the format ('bf16', 'e4m3fn' or 'mxfp8')."""
+    bits: np.ndarray                  # uint16 [rows, D] (bf16) or uint8 [rows, D] (e4m3fn, mxfp8)
     fmt: str
-    scale: Optional[np.ndarray] = None  # float32 [rows] for e4m3fn
+    scale: Optional[np.ndarray] = None  # float32 [rows] (e4m3fn) or uint8 [rows, D/32] (mxfp8)
 
     def rows(self, idx) -> np.ndarray:
         if self.fmt == "bf16":
             return decode_bf16(self.bits[idx])
         if self.fmt == "e4m3fn":
             return decode_e4m3fn(self.bits[idx], self.scale[idx])
+        if self.fmt == "mxfp8":
+            return decode_mxfp8(self.bits[idx], self.scale[idx])
         raise ValueError(self.fmt)
 
 

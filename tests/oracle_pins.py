@@ -103,6 +103,82 @@ def check_cache_append(orc):
     assert sorted(q) == [4, 12]
     assert np.allclose(orc.decode_e4m3fn(q[4][0][None], np.array([q[4][1]]))[0],
                        orc.decode_bf16(rows[0]), rtol=1 / 16, atol=0)
+    m = orc.cache_append(token_seq, token_pos, seq_start, seq_len, 13,
+                         np.tile(rows, (1, 4)), "mxfp8")
+    assert sorted(m) == [4, 12] and m[4][1].shape == (1,)
+    assert np.allclose(orc.decode_mxfp8(m[12][0][None], m[12][1][None])[0],
+                       orc.decode_bf16(np.tile(rows[1], 4)), rtol=1 / 16, atol=0)
+
+
+def check_e8m0_table(orc):
+    # against torch's float8_e8m0fnu -> float32 for every code (255 is NaN)
+    ref = torch.arange(256, dtype=torch.uint8).view(torch.float8_e8m0fnu).to(torch.float32).numpy()
+    got = orc.e8m0_table()
+    assert np.isnan(got[255]) and np.isnan(ref[255])
+    assert np.array_equal(got[:255], ref[:255].astype(np.float64)), "E8M0 table disagrees with torch"
+
+
+def check_mxfp8_worked_example(orc):
+    g = _golden("mxfp8_worked_example.json")
+    x = np.zeros((1, 96))
+    for blk, off in (("block0", 0), ("block1", 32)):
+        for i, v in g[blk]["values"].items():
+            x[0, off + int(i)] = v
+    pay, ex = orc.quantize_blocks_mxfp8(x)
+    assert ex.tolist() == [[g["block0"]["exp"], g["block1"]["exp"], g["zero_block"]["exp"]]], ex
+    for blk, off in (("block0", 0), ("block1", 32)):
+        for i, c in g[blk]["codes"].items():
+            assert int(pay[0, off + int(i)]) == c, (blk, i, int(pay[0, off + int(i)]), c)
+    assert not pay[0, 64:].any()
+
+
+def check_mxfp8_brute_force(orc):
+    # every element is the nearest of all finite E4M3FN values times its block's
+    # scale (ties to the even code, beyond 448 the largest), and the block's
+    # exponent is floor(log2 max|x|) - 8, found by search over powers of two
+    rng = np.random.default_rng(3)
+    x = rng.normal(size=(6, 128)) * np.ldexp(1.0, rng.integers(-20, 20, size=(6, 1)))
+    x[2, 32:64] = 0.0
+    x[4, :32] = 0.0                                  # max 1: scale 2^-8, ties among subnormals
+    x[4, 0] = 1.0
+    x[4, 1:4] = np.array([1.5, 0.5, 2.5]) * 2.0 ** -17
+    pay, ex = orc.quantize_blocks_mxfp8(x)
+    table = orc.e4m3fn_table()
+    codes = np.array([c for c in range(256) if not np.isnan(table[c])])
+    for r in range(x.shape[0]):
+        for b in range(4):
+            blk = x[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert ex[r, b] == 0 and not pay[r, 32 * b:32 * b + 32].any()
+                continue
+            e = 0
+            while 2.0 ** (e + 1) <= amax:
+                e += 1
+            while 2.0 ** e > amax:
+                e -= 1
+            assert int(ex[r, b]) == e - 8 + 127, (r, b)
+            sc = 2.0 ** (e - 8)
+            for j, v in enumerate(blk):
+                a = min(abs(v) / sc, 448.0)
+                d = np.abs(np.abs(table[codes]) - a)
+                best = codes[(d == d.min()) & (codes < 0x80)]
+                want = best[best % 2 == 0][0] if len(best) > 1 else best[0]
+                if v < 0 or (v == 0 and np.signbit(v)):
+                    want |= 0x80
+                assert int(pay[r, 32 * b + j]) == int(want), (r, b, j, v)
+
+
+def check_mxfp8_scale_invariance(orc):
+    # scaling a block by 2^k keeps its payload and moves its exponent by k
+    rng = np.random.default_rng(4)
+    x = rng.normal(size=(3, 64))
+    p0, e0 = orc.quantize_blocks_mxfp8(x)
+    for k in (-9, 1, 17):
+        p1, e1 = orc.quantize_blocks_mxfp8(np.ldexp(x, k))
+        assert np.array_equal(p0, p1) and np.array_equal(e1.astype(int), e0.astype(int) + k)
+    dec = orc.decode_mxfp8(p0, e0)
+    assert np.allclose(dec, x, rtol=1 / 16, atol=0)
 
 
 # ---------------------------------------------------------------- indexer
@@ -364,9 +440,40 @@ def check_forward_fp8_store(orc):
     assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
 
 
+def check_forward_mxfp8_store(orc):
+    """An MX block-32 cache holds payload times block scale: the path over an MX
+    store equals the path over the same values stored exactly in bf16."""
+    rng = np.random.default_rng(11)
+    n = 24
+    codes = rng.integers(0, 256, (n, 576)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x38
+    exps = rng.integers(120, 130, (n, 18)).astype(np.uint8)
+    vals = (torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+            * torch.from_numpy(np.ldexp(1.0, exps.astype(int) - 127).astype(np.float32)).repeat_interleave(32, 1))
+    vals_bits = vals.to(torch.bfloat16)
+    assert torch.equal(vals_bits.to(torch.float32), vals)
+    kcodes = rng.integers(-3, 4, (n, 128)).astype(np.float32)
+    kexps = rng.integers(125, 130, (n, 4)).astype(np.uint8)
+    kpay = torch.from_numpy(kcodes).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    kvals = torch.from_numpy(kcodes * np.ldexp(1.0, kexps.astype(int) - 127).repeat(32, 1)).to(torch.bfloat16)
+    q_idx = rng.integers(-3, 4, (1, 64, 128)).astype(float)
+    w = rng.integers(0, 5, (1, 64)).astype(float)
+    q_abs = rng.standard_normal((1, 64, 576))
+    tau = 1 / math.sqrt(192)
+    args = (np.zeros(1, np.int32), np.array([n - 1], np.int32), np.zeros(1, np.int64), np.array([n], np.int32))
+    a = orc.forward(*args, q_idx, w, orc.Store(kpay, "mxfp8", kexps), q_abs,
+                    orc.Store(codes, "mxfp8", exps), None, 5, tau)
+    b = orc.forward(*args, q_idx, w, orc.Store(kvals.view(torch.int16).numpy().view(np.uint16), "bf16"), q_abs,
+                    orc.Store(vals_bits.view(torch.int16).numpy().view(np.uint16), "bf16"), None, 5, tau)
+    assert np.array_equal(a["indices"], b["indices"])
+    assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
+
+
 ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_example,
               check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
               check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
               check_attention_vs_sdpa, check_attention_special_cases, check_gate,
               check_forward_dense_limit, check_forward_selects_by_indexer, check_forward_fp8_store,
-              check_e4m3fn_encode, check_quantize_rows, check_cache_append]
+              check_e4m3fn_encode, check_quantize_rows, check_cache_append, check_e8m0_table,
+              check_mxfp8_worked_example, check_mxfp8_brute_force, check_mxfp8_scale_invariance,
+              check_forward_mxfp8_store]

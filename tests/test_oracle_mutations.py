@@ -108,6 +108,30 @@ def _append_row_plus_one(token_seq, token_pos, seq_start, seq_len, cache_rows, r
 
 _ORIG_APPEND = base.cache_append
 
+
+def _mx_quantize(x, shift=8, block=32, ceil=False):
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    blocks = x.reshape(n, d // block, block)
+    amax = np.max(np.abs(blocks), axis=2)
+    exps = np.zeros(amax.shape, dtype=np.uint8)
+    nz = amax > 0
+    lg = np.ceil(np.log2(amax[nz])) if ceil else np.floor(np.log2(amax[nz]))
+    exps[nz] = np.clip(lg - shift, -127, 127) + 127
+    scale = np.ldexp(1.0, exps.astype(int) - 127)
+    pay = base.encode_e4m3fn(blocks / scale[:, :, None]).reshape(n, d)
+    if block != 32:          # report one exponent per 32 as the format stores
+        exps = exps[:, ::32 // block]
+    return pay, exps
+
+
+def _mx_decode_bias_128(payload, exps):
+    p = np.asarray(payload, dtype=np.uint8)
+    n, d = p.shape
+    vals = base.e4m3fn_table()[p].reshape(n, d // 32, 32)
+    return (vals * np.ldexp(1.0, np.asarray(exps, int) - 128)[:, :, None]).reshape(n, d)
+
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -121,6 +145,10 @@ MUTANTS = {
     "e4m3_encode_ties_away": dict(encode_e4m3fn=_encode_ties_away),
     "quantize_scale_240": dict(quantize_rows_e4m3fn=_quantize_scale_240),
     "append_row_off_by_one": dict(cache_append=_append_row_plus_one),
+    "mx_exponent_off_by_one": dict(quantize_blocks_mxfp8=lambda x: _mx_quantize(x, shift=7)),
+    "mx_exponent_from_ceil": dict(quantize_blocks_mxfp8=lambda x: _mx_quantize(x, ceil=True)),
+    "mx_blocks_of_16": dict(quantize_blocks_mxfp8=lambda x: _mx_quantize(x, block=16)),
+    "mx_decode_bias_128": dict(decode_mxfp8=_mx_decode_bias_128),
 }
 
 
