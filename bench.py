@@ -44,7 +44,7 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 COPY_BYTES = 1 << 30                # calibration copy size
 WORKLOADS = {"tiny_decode_4k": 0, "batched_decode_ragged_16k_32k": 1, "long_decode_128k": 2,
              "chunked_prefill_128k": 3,
-             "extended_decode_256k_fp8": 4}
+             "extended_decode_256k_fp8": 4, "extended_decode_256k_mxfp8": 5}
 PMC_WORKLOAD = "long_decode_128k"
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_long_decode_128k_pmc.json")
 # the sources the indexer kernel is built from
@@ -107,7 +107,7 @@ def indexer_bytes(wl) -> int:
     (128 elements, plus a 4-byte scale for fp8) and each token's 64x128 bf16
     query and 64 fp32 head weights. Keys shared by several tokens of one
     sequence count once."""
-    per_row = 128 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)
+    per_row = 128 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)   # MX: 4 one-byte exponents
     rows = 0
     for b in range(wl.num_seqs):
         sel = wl.token_seq == b
@@ -128,7 +128,7 @@ def step_bytes(wl) -> int:
     its min(k, visible) selected latent rows (576 elements, plus a scale for fp8),
     its 64x576 bf16 absorbed query, 64 gate logits, and its fp32 output
     (64x512) and lse (64)."""
-    per_row = 576 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)
+    per_row = 576 * (1 if wl.fp8 else 2) + ((18 if wl.mx else 4) if wl.fp8 else 0)
     sel_rows = int(np.minimum(visible(wl), wl.k).sum())
     per_tok = 64 * 576 * 2 + 64 * 4 + 64 * 512 * 4 + 64 * 4
     return indexer_bytes(wl) + sel_rows * per_row + wl.num_tokens * per_tok
@@ -138,8 +138,9 @@ def append_bytes(wl) -> int:
     """Algorithmic bytes of one cache append of every token's new rows: the
     bf16 latent (576) and indexer key (128) read, the token's metadata
     (sequence, position, start, length: 20 bytes) read, and the rows written
-    in the cache format (plus one fp32 scale per row for fp8)."""
-    out = (576 + 128 + 8) if wl.fp8 else (576 + 128) * 2
+    in the cache format (plus one fp32 scale per row for fp8, one byte per
+    32 elements for MX)."""
+    out = ((576 + 128 + (22 if wl.mx else 8)) if wl.fp8 else (576 + 128) * 2)
     return wl.num_tokens * ((576 + 128) * 2 + 20 + out)
 
 
@@ -256,9 +257,9 @@ def cpu_baseline(wl, min_seconds: float):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # threadpoolctl missing: report the affinity size
         threads = len(os.sched_getaffinity(0))
-    ks = (oracle.Store(wl.k_idx.view(torch.uint8).numpy(), "e4m3fn", wl.k_idx_scale.numpy()) if wl.fp8
+    ks = (oracle.Store(wl.k_idx.view(torch.uint8).numpy(), wl.cache_fmt, wl.k_idx_scale.numpy()) if wl.fp8
           else oracle.Store(wl.k_idx.view(torch.int16).numpy().view(np.uint16), "bf16"))
-    vs = (oracle.Store(wl.kv.view(torch.uint8).numpy(), "e4m3fn", wl.kv_scale.numpy()) if wl.fp8
+    vs = (oracle.Store(wl.kv.view(torch.uint8).numpy(), wl.cache_fmt, wl.kv_scale.numpy()) if wl.fp8
           else oracle.Store(wl.kv.view(torch.int16).numpy().view(np.uint16), "bf16"))
     args = (wl.token_seq, wl.token_pos, wl.seq_start, wl.seq_len, wl.q_idx.double().numpy(),
             wl.w.double().numpy(), ks, wl.q_abs.double().numpy(), vs, wl.gate.double().numpy(),
@@ -378,7 +379,7 @@ def main():
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp8" if wl.fp8 else "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": dict(si.describe(wl), parallelism="single GPU"),
         "roofline": roof,

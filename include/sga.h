@@ -32,6 +32,15 @@
  * - Element types: bf16 is IEEE bfloat16. SGA_FP8_E4M3 is OCP E4M3FN (max 448,
  *   no infinities) with one fp32 scale per cached row. A row's value is
  *   payload * scale. Scales must be finite and positive.
+ * - SGA_MXFP8_E4M3 is the MX block-32 form (fact sheet, Training: MXFP8 E4M3
+ *   with one scale per 32 consecutive elements): E4M3FN payloads plus one
+ *   E8M0 byte e per 32 consecutive elements of a row, worth 2^(e - 127). The
+ *   scale array is uint8 [rows, D/32], row-major: 4 bytes per indexer key row
+ *   (read as one 32-bit word, so 4-byte aligned) and 18 per latent row.
+ *   e = 255 (NaN) is not a valid exponent. The kernels widen payload * 2^(e-127)
+ *   to bf16, which is exact while the products are bf16 normals or zero, so
+ *   every exponent of a nonzero block must be at least 10 (scale >= 2^-117);
+ *   below that the smallest values lose bits.
  */
 #ifndef SGA_H
 #define SGA_H
@@ -66,7 +75,8 @@ typedef enum sga_status {
 
 typedef enum sga_dtype {
   SGA_BF16 = 0,
-  SGA_FP8_E4M3 = 1          /* OCP E4M3FN payload + fp32 scale per row */
+  SGA_FP8_E4M3 = 1,         /* OCP E4M3FN payload + fp32 scale per row */
+  SGA_MXFP8_E4M3 = 2        /* OCP E4M3FN payload + E8M0 exponent per 32 elements */
 } sga_dtype;
 
 /*
@@ -115,11 +125,13 @@ typedef struct sga_trace {
  *
  * For each token t and each visible position s < n_t:
  *   scores[t*ld + s] = sum_h w[t*64+h] * max(0, sum_d q_idx[t,h,d] * key[row(s), d])
- * where key = k_idx (bf16), or payload * k_idx_scale[row] (fp8).
+ * where key = k_idx (bf16), payload * k_idx_scale[row] (fp8), or payload
+ * times its 32-element block's E8M0 scale (MX).
  *   q_idx       [T,64,128] bf16, row-major.
  *   w           [T,64] fp32 head weights.
- *   k_idx       [cache_rows,128] bf16 or fp8 payload, row-major (256 or 128 B per row).
- *   k_idx_scale [cache_rows] fp32 for fp8; must be NULL for bf16.
+ *   k_idx       [cache_rows,128] bf16 or E4M3FN payload, row-major (256 or 128 B per row).
+ *   k_idx_scale [cache_rows] fp32 (fp8), [cache_rows,4] uint8 E8M0 (MX, 4-byte
+ *               aligned); must be NULL for bf16.
  *   scores      [T, ld] fp32, ld >= max_len. Only entries s < n_t are written.
  * Accumulation is fp32 (bf16 products are exact in fp32). With integer-valued
  * inputs every partial sum is an integer, so the scores are exact whenever
@@ -127,7 +139,7 @@ typedef struct sga_trace {
  * payload and then multiplied by the row scale.
  */
 SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, const float* w,
-                                    const void* k_idx, const float* k_idx_scale,
+                                    const void* k_idx, const void* k_idx_scale,
                                     sga_dtype k_idx_dtype, float* scores, int64_t ld,
                                     hipStream_t stream);
 
@@ -164,16 +176,18 @@ SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t
  *   o     = sum_j softmax(z)_j * row_j[0:512]
  *   out[t,h,:] = o * sigmoid(gate_logits[t*64+h])   (o itself when gate_logits == NULL)
  *   lse[t*64+h] = log(sum_j exp(z_j))                (natural log)
- * An fp8 row is payload * kv_scale[row]. With J empty, out = 0 and lse = -inf.
- *   q_abs [T,64,576] bf16. kv [cache_rows,576] bf16 or fp8 payload.
- *   kv_scale [cache_rows] fp32 for fp8, NULL for bf16. indices [T,k] int32.
+ * An fp8 row is payload * kv_scale[row]; an MX row is each payload times its
+ * 32-column block's scale. With J empty, out = 0 and lse = -inf.
+ *   q_abs [T,64,576] bf16. kv [cache_rows,576] bf16 or E4M3FN payload.
+ *   kv_scale [cache_rows] fp32 (fp8), [cache_rows,18] uint8 E8M0 (MX), NULL
+ *   for bf16. indices [T,k] int32.
  *   out [T,64,512] fp32. lse [T,64] fp32 or NULL.
  * Logits and softmax are fp32. Probabilities enter the value product as
  * bf16, and accumulation is fp32.
  */
 SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k);
 SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs, const void* kv,
-                                       const float* kv_scale, sga_dtype kv_dtype,
+                                       const void* kv_scale, sga_dtype kv_dtype,
                                        const int32_t* indices, int32_t k, float sm_scale,
                                        const float* gate_logits, float* out, float* lse,
                                        void* ws, size_t ws_bytes, hipStream_t stream);
@@ -188,44 +202,49 @@ SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs
 SGA_API size_t sga_forward_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k);
 SGA_API sga_status sga_forward(const sga_batch* batch,
                                const void* q_idx, const float* w, const void* k_idx,
-                               const float* k_idx_scale, sga_dtype k_idx_dtype,
-                               const void* q_abs, const void* kv, const float* kv_scale,
+                               const void* k_idx_scale, sga_dtype k_idx_dtype,
+                               const void* q_abs, const void* kv, const void* kv_scale,
                                sga_dtype kv_dtype, int32_t k, float sm_scale,
                                const float* gate_logits, float* out, float* lse,
                                int32_t* indices_out, void* ws, size_t ws_bytes,
                                const sga_trace* trace, hipStream_t stream);
 
-/* Human-readable name of a status code (static string). */
 /*
  * sga_cache_append: writes each token's new cached rows (the step just before
  * the path in decode).
  * Source: the FP8 model card (nlp.com.ai, "A.X K2 FP8": FP8 with dynamic
- * per-row scaling) and the fact sheet's per-token cache row (512 latent + 64
- * RoPE, 128-wide indexer key).
+ * per-row scaling), the fact sheet's per-token cache row (512 latent + 64
+ * RoPE, 128-wide indexer key) and its Training section (MXFP8, one scale per
+ * 32 consecutive elements).
  *
  * Token t of sequence b at position p writes flat row r = seq_start[b] + p:
  *   kv[r]    <- latent[t]  (576 values),  when latent and kv are non-NULL;
  *   k_idx[r] <- idx_key[t] (128 values),  when idx_key and k_idx are non-NULL.
  *   latent  [T,576] bf16, idx_key [T,128] bf16, row-major, 16-byte aligned.
  * Each pair is given whole or left out whole (both NULL): one NULL and one
- * non-NULL is SGA_ERR_INVALID_ARG. Caches are 16-byte aligned, scale arrays
- * 4-byte aligned; the caller owns every buffer and the call only writes the
- * rows (and scales) named above, asynchronously on `stream`.
+ * non-NULL is SGA_ERR_INVALID_ARG. Caches are 16-byte aligned, fp32 scale
+ * arrays 4-byte aligned; the caller owns every buffer and the call only writes
+ * the rows (and scales) named above, asynchronously on `stream`.
  * A bf16 cache gets the bits copied. An SGA_FP8_E4M3 cache gets, per row,
  *   scale = max|x| / 448 (binary32 division; 1 for a row of zeros), stored in
  *   kv_scale[r] / k_idx_scale[r], and payload = x / scale (binary32) rounded to
  *   the nearest E4M3FN value, ties to the even code, saturating at 448; the
  *   sign bit follows x (so -0 gives 0x80).
- * The scale arrays must be NULL for a bf16 cache and non-NULL for fp8.
+ * An SGA_MXFP8_E4M3 cache gets, per run of 32 elements, the E8M0 exponent
+ *   e = clamp(floor(log2 max|x|) - 8, -127, 127) + 127 (e = 0 for a block of
+ *   zeros; 8 is the exponent of 448), stored in byte r*D/32 + block of the
+ *   scale array, and payload = x * 2^(127 - e) encoded as above.
+ * The scale arrays must be NULL for a bf16 cache and non-NULL otherwise.
  * A token with b outside [0, num_seqs), p outside [0, seq_len[b]) or r outside
  * [0, cache_rows) writes nothing. Tokens writing the same row race; the
  * caller keeps rows distinct. max_len is checked as for the other calls but
  * not otherwise used. Inputs must be finite.
  */
 SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,
-                                    void* kv, float* kv_scale, sga_dtype kv_dtype, void* k_idx,
-                                    float* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream);
+                                    void* kv, void* kv_scale, sga_dtype kv_dtype, void* k_idx,
+                                    void* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream);
 
+/* Human-readable name of a status code (static string). */
 SGA_API const char* sga_status_string(sga_status status);
 /* Library version as major*10000 + minor*100 + patch. */
 SGA_API int sga_version(void);

@@ -28,6 +28,14 @@ fp8 caches use OCP E4M3FN with one fp32 scale per cached row:
 - indexer keys: payload = the integer itself, scale = 2**u with u drawn
   uniformly from [-2, 2].
 Power-of-two scales keep the scores exact.
+
+MX block-32 caches (E4M3FN payloads, one E8M0 exponent per 32 elements) are
+drawn in their stored form:
+- latent rows: each block's exponent e is drawn uniformly from [118, 121]
+  (scales 2^-9 .. 2^-6) and its payload is the N(0,1)/24 draw divided by
+  2^(e - 127), cast to E4M3FN (nearest even, clamped to 448);
+- indexer keys: payload = the integer itself, each block's exponent 127 + u
+  with u drawn uniformly from [-2, 2].
 """
 from __future__ import annotations
 
@@ -49,7 +57,8 @@ SM_SCALE = 1.0 / math.sqrt(192.0)  # QK head dim 192 = 128 NoPE + 64 RoPE
 E4M3_MAX = 448.0
 
 CONFIG_NAMES = ("tiny_decode_4k", "batched_decode_ragged_16k_32k",
-                "long_decode_128k", "chunked_prefill_128k", "extended_decode_256k_fp8")
+                "long_decode_128k", "chunked_prefill_128k", "extended_decode_256k_fp8",
+                "extended_decode_256k_mxfp8")
 
 
 @dataclass
@@ -62,9 +71,9 @@ class Workload:
     q_idx: torch.Tensor      # bf16 [T, 64, 128]
     w: torch.Tensor          # fp32 [T, 64]
     k_idx: torch.Tensor      # bf16 or float8_e4m3fn [rows, 128]
-    k_idx_scale: Optional[torch.Tensor]  # fp32 [rows] for fp8, else None
+    k_idx_scale: Optional[torch.Tensor]  # fp32 [rows] (fp8), uint8 [rows, 4] (MX), else None
     kv: torch.Tensor         # bf16 or float8_e4m3fn [rows, 576]
-    kv_scale: Optional[torch.Tensor]     # fp32 [rows] for fp8, else None
+    kv_scale: Optional[torch.Tensor]     # fp32 [rows] (fp8), uint8 [rows, 18] (MX), else None
     q_abs: torch.Tensor      # bf16 [T, 64, 576]
     gate: torch.Tensor       # fp32 [T, 64]
     k: int = TOP_K
@@ -91,7 +100,17 @@ class Workload:
 
     @property
     def fp8(self) -> bool:
+        """One-byte E4M3FN payloads (per-row or MX block scales)."""
         return self.kv.dtype == torch.float8_e4m3fn
+
+    @property
+    def mx(self) -> bool:
+        return self.kv_scale is not None and self.kv_scale.dim() == 2
+
+    @property
+    def cache_fmt(self) -> str:
+        """The format name the oracle's Store uses."""
+        return "mxfp8" if self.mx else ("e4m3fn" if self.fp8 else "bf16")
 
 
 def _bf16(x: np.ndarray) -> torch.Tensor:
@@ -113,13 +132,17 @@ def _quantize_rows_e4m3(x: np.ndarray):
 def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int, *,
           fp8: bool = False, kv_sigma: float = 1.0 / 24.0, q_abs_mult: float = 1.0,
           idx_range: int = 3, w_range: tuple = (0, 4), gate_sigma: float = 2.0,
-          k: int = TOP_K, sm_scale: float = SM_SCALE, chunk_rows: int = 1 << 16) -> Workload:
+          k: int = TOP_K, sm_scale: float = SM_SCALE, chunk_rows: int = 1 << 16,
+          mx: bool = False) -> Workload:
     """Draw one workload.
 
     lengths: cached rows per sequence. tokens: (sequence, position) per query token.
     Draw order: lengths are given; then indexer keys, indexer queries, head
-    weights, latent cache, absorbed queries, gate logits, fp8 key-scale exponents.
+    weights, latent cache (with each chunk's block exponents for MX), absorbed
+    queries, gate logits, fp8 key-scale exponents. mx: MX block-32 caches
+    (implies fp8 payloads).
     """
+    fp8 = fp8 or mx
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
     B = int(lengths.shape[0])
@@ -145,7 +168,12 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
         r1 = min(rows, r0 + chunk_rows)
         x = rng.standard_normal(size=(r1 - r0, D_QK), dtype=np.float32)
         x *= np.float32(kv_sigma)
-        if fp8:
+        if mx:
+            e = rng.integers(118, 122, size=(r1 - r0, D_QK // 32))
+            inv = np.ldexp(np.float32(1.0), 127 - e).astype(np.float32)
+            kv_parts.append(_to_e4m3(x * np.repeat(inv, 32, axis=1)))
+            kv_scale_parts.append(torch.from_numpy(e.astype(np.uint8)))
+        elif fp8:
             p, s = _quantize_rows_e4m3(x)
             kv_parts.append(p)
             kv_scale_parts.append(s)
@@ -155,12 +183,19 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
         kv = torch.cat(kv_parts)
     else:
         kv = torch.zeros((0, D_QK), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16)
-    kv_scale = (torch.cat(kv_scale_parts) if kv_scale_parts else torch.zeros(0)) if fp8 else None
+    if mx:
+        kv_scale = torch.cat(kv_scale_parts) if kv_scale_parts else torch.zeros((0, D_QK // 32), dtype=torch.uint8)
+    else:
+        kv_scale = (torch.cat(kv_scale_parts) if kv_scale_parts else torch.zeros(0)) if fp8 else None
 
     q_abs = rng.standard_normal(size=(T, N_HEADS, D_QK), dtype=np.float32) * np.float32(q_abs_mult)
     gate = (rng.standard_normal(size=(T, N_HEADS)) * gate_sigma).astype(np.float32)
 
-    if fp8:
+    if mx:
+        u = rng.integers(-2, 3, size=(rows, IDX_DIM // 32))
+        k_idx = _to_e4m3(k_int.astype(np.float32))
+        k_idx_scale = torch.from_numpy((127 + u).astype(np.uint8))
+    elif fp8:
         u = rng.integers(-2, 3, size=rows)
         k_idx = _to_e4m3(k_int.astype(np.float32))
         k_idx_scale = torch.from_numpy(np.ldexp(np.float32(1.0), u).astype(np.float32))
@@ -172,7 +207,7 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
                     token_seq=token_seq, token_pos=token_pos, q_idx=_bf16(q_idx),
                     w=torch.from_numpy(w), k_idx=k_idx, k_idx_scale=k_idx_scale, kv=kv,
                     kv_scale=kv_scale, q_abs=_bf16(q_abs), gate=torch.from_numpy(gate),
-                    k=k, sm_scale=sm_scale, meta={"seed": seed, "fp8": fp8})
+                    k=k, sm_scale=sm_scale, meta={"seed": seed, "fp8": fp8, "mx": mx})
 
 
 def append_rows(num_tokens: int, seed: int, *, kv_sigma: float = 1.0 / 24.0, key_sigma: float = 1.0,
@@ -190,7 +225,8 @@ def append_rows(num_tokens: int, seed: int, *, kv_sigma: float = 1.0 / 24.0, key
 
 
 def config(i: int, seed: Optional[int] = None) -> Workload:
-    """The five workloads: seed defaults to the workload's number."""
+    """The five workloads, and a sixth: the 256K decode with MX block-32 caches.
+    The seed defaults to the workload's number."""
     s = i if seed is None else seed
     if i == 0:   # tiny decode: 1 sequence of 4096, tokens at 4092..4095
         return build(CONFIG_NAMES[0], [4096], [(0, p) for p in range(4092, 4096)], s)
@@ -204,9 +240,12 @@ def config(i: int, seed: Optional[int] = None) -> Workload:
         return build(CONFIG_NAMES[3], [131072], [(0, p) for p in range(122880, 131072)], s)
     if i == 4:   # extended decode with fp8 caches: 8 x 262144
         return build(CONFIG_NAMES[4], [262144] * 8, [(b, 262143) for b in range(8)], s, fp8=True)
+    if i == 5:   # the same shape with MX block-32 caches (the training recipe's format)
+        return build(CONFIG_NAMES[5], [262144] * 8, [(b, 262143) for b in range(8)], s, mx=True)
     raise ValueError(f"no workload {i}")
 
 
 def describe(wl: Workload) -> dict:
     return {"workload": wl.name, "batch": wl.num_seqs, "query_tokens": wl.num_tokens,
-            "max_context": wl.max_len, "top_k": wl.k, "cache": "fp8_e4m3" if wl.fp8 else "bf16"}
+            "max_context": wl.max_len, "top_k": wl.k,
+            "cache": "mxfp8_e4m3" if wl.mx else ("fp8_e4m3" if wl.fp8 else "bf16")}

@@ -18,7 +18,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsga.so")
 
 SGA_OK, SGA_ERR_INVALID_ARG, SGA_ERR_UNSUPPORTED, SGA_ERR_WORKSPACE, SGA_ERR_HIP = range(5)
-SGA_BF16, SGA_FP8_E4M3 = 0, 1
+SGA_BF16, SGA_FP8_E4M3, SGA_MXFP8_E4M3 = 0, 1, 2
+MX_BLOCK = 32
 HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK = 64, 64, 128, 512, 576
 
 EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_workspace_size",
@@ -115,15 +116,22 @@ def _check(t: torch.Tensor, name: str, dtypes, shape=None):
 
 
 def _store_dtype(t: torch.Tensor, scale: Optional[torch.Tensor], name: str) -> int:
+    """The cache format from the tensors: bf16 rows; float8_e4m3fn rows with one
+    fp32 scale per row; or float8_e4m3fn rows with one E8M0 exponent (uint8 or
+    float8_e8m0fnu) per 32 elements, [rows, width/32] (MX block-32)."""
     if t.dtype == torch.bfloat16:
         if scale is not None:
             raise ValueError(f"{name}: bf16 storage takes no scale")
         return SGA_BF16
     if t.dtype == torch.float8_e4m3fn:
         if scale is None:
-            raise ValueError(f"{name}: fp8 storage needs one fp32 scale per row")
-        _check(scale, name + "_scale", (torch.float32,), (t.shape[0],))
-        return SGA_FP8_E4M3
+            raise ValueError(f"{name}: fp8 storage needs scales")
+        if scale.dtype == torch.float32:
+            _check(scale, name + "_scale", (torch.float32,), (t.shape[0],))
+            return SGA_FP8_E4M3
+        _check(scale, name + "_scale", (torch.uint8, torch.float8_e8m0fnu),
+               (t.shape[0], t.shape[1] // MX_BLOCK))
+        return SGA_MXFP8_E4M3
     raise TypeError(f"{name} must be bfloat16 or float8_e4m3fn, got {t.dtype}")
 
 

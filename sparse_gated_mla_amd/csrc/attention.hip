@@ -28,7 +28,10 @@
 // never covers the loads of a later one. Two LDS regions alternate: one is
 // attended while the other is filled.
 // fp8 rows are widened to bf16 exactly on their way into LDS; the row scale
-// multiplies the row's logit and probability.
+// multiplies the row's logit and probability. MX block-32 rows (fact sheet,
+// Training: MXFP8, one scale per 32 consecutive elements) have each 32-column
+// block multiplied by its power-of-two scale as it is widened, which is exact
+// in bf16, and are then attended like bf16 rows.
 //
 // With several splits per token, each split writes its output normalised by
 // its own exp-sum, in fp16 with a per-half scale, plus (max, exp-sum);
@@ -61,14 +64,15 @@ __device__ __forceinline__ float gate_factor(const float* gate, int64_t idx) {
 
 // One tile's rows in registers: thread x holds 16-byte units x, x + 512, ...
 // of the tile (row u / kUnitsPerRow, unit u % kUnitsPerRow of that row).
-template <bool kFp8>
+template <int kFmt>
 struct RowStage {
+  static constexpr bool kFp8 = kFmt != kFmtBf16;                  // one-byte payloads
   static constexpr int kRowBytes = kFp8 ? kDQK : 2 * kDQK;       // cached bytes per row
   static constexpr int kUnitsPerRow = kRowBytes / 16;             // 36 or 72
   static constexpr int kUnits = kAttnTileRows * kUnitsPerRow;     // 1152 or 2304
   static constexpr int kPer = (kUnits + kAttnThreads - 1) / kAttnThreads;  // 3 or 5
   u32x4 v[kPer];
-  float s[kPer];        // fp8 row scales
+  uint32_t s[kPer];     // the unit's fp32 row scale (fp8) or its block's E8M0 exponent (MX)
   int32_t idx[kPer];    // row indices for the next load_rows
   uint32_t ok;          // bit q: unit q of the loaded tile is a real row
 
@@ -100,9 +104,11 @@ struct RowStage {
       const uint32_t skip = real ? 0u : 0x80000000u;
       v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                            rows, (int)(((uint32_t)id * kRowBytes + 16u * c) | skip), 0, kNonTemporal));
-      if constexpr (kFp8)
-        s[q] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                             scales, (int)(((uint32_t)id * 4u) | skip), 0, 0));
+      if constexpr (kFmt == kFmtFp8)
+        s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, (int)(((uint32_t)id * 4u) | skip), 0, 0);
+      if constexpr (kFmt == kFmtMx)   // 16 payload bytes = half of block c/2
+        s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
+            scales, (int)(((uint32_t)id * (kDQK / 32) + (uint32_t)(c >> 1)) | skip), 0, 0);
     }
     ok = m;
     // keep each tile's loads together, in program order
@@ -110,7 +116,7 @@ struct RowStage {
   }
 
   // Stores the tile into an LDS region (bf16 rows of kRowStride elements) and
-  // each row's flag: its scale (fp8), 1 (bf16), or -1 for a skipped row.
+  // each row's flag: its scale (fp8), 1 (bf16, MX), or -1 for a skipped row.
   __device__ __forceinline__ void store(uint8_t* region, float* flags) const {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -121,13 +127,24 @@ struct RowStage {
         if constexpr (!kFp8) {
           *reinterpret_cast<u32x4*>(row + 16 * c) = v[q];
         } else {
-          const u32x2 a0 = e4m3x4_to_bf16x4(v[q].x), a1 = e4m3x4_to_bf16x4(v[q].y);
-          const u32x2 a2 = e4m3x4_to_bf16x4(v[q].z), a3 = e4m3x4_to_bf16x4(v[q].w);
+          u32x2 a0, a1, a2, a3;
+          if constexpr (kFmt == kFmtMx) {
+            const float bs = e8m0_to_f32(s[q]);
+            a0 = e4m3x4_scaled_to_bf16x4(v[q].x, bs);
+            a1 = e4m3x4_scaled_to_bf16x4(v[q].y, bs);
+            a2 = e4m3x4_scaled_to_bf16x4(v[q].z, bs);
+            a3 = e4m3x4_scaled_to_bf16x4(v[q].w, bs);
+          } else {
+            a0 = e4m3x4_to_bf16x4(v[q].x);
+            a1 = e4m3x4_to_bf16x4(v[q].y);
+            a2 = e4m3x4_to_bf16x4(v[q].z);
+            a3 = e4m3x4_to_bf16x4(v[q].w);
+          }
           u32x4* dst = reinterpret_cast<u32x4*>(row + 32 * c);
           dst[0] = u32x4{a0.x, a0.y, a1.x, a1.y};
           dst[1] = u32x4{a2.x, a2.y, a3.x, a3.y};
         }
-        if (c == 0) flags[r] = (ok >> q) & 1u ? (kFp8 ? s[q] : 1.0f) : -1.0f;
+        if (c == 0) flags[r] = (ok >> q) & 1u ? (kFmt == kFmtFp8 ? __uint_as_float(s[q]) : 1.0f) : -1.0f;
       }
     }
   }
@@ -288,12 +305,13 @@ __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, in
   }
 }
 
-template <bool kFp8>
+template <int kFmt>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+  constexpr bool kRowScale = kFmt == kFmtFp8;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tile[2][kRegionBytes];
   __shared__ float lds_flags[2][kAttnTileRows];
   __shared__ __attribute__((aligned(16))) float xbuf[kAttnWaves * 64 * 8];
-  using Stage = RowStage<kFp8>;
+  using Stage = RowStage<kFmt>;
   const int t = blockIdx.y, split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = wave >> 2;
@@ -308,8 +326,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 
   const uint32_t rows_bytes = (uint32_t)max(n, 0) * Stage::kRowBytes;
   const rsrc_t rows = make_rsrc(a.kv + base * Stage::kRowBytes, rows_bytes);
-  const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.kv_scale + base) : (const void*)a.kv,
-                                  kFp8 ? (uint32_t)max(n, 0) * 4u : 0u);
+  const rsrc_t scales =
+      kFmt == kFmtFp8 ? make_rsrc(static_cast<const float*>(a.kv_scale) + base, (uint32_t)max(n, 0) * 4u)
+      : kFmt == kFmtMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
+                                   (uint32_t)max(n, 0) * (kDQK / 32))
+                       : make_rsrc(a.kv, 0u);
   const rsrc_t idx_rs = make_rsrc(a.indices + (int64_t)t * a.k + j_begin, (uint32_t)nrows * 4u);
 
   Stage s0, s1;
@@ -341,7 +362,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     sg.load_idx(idx_rs, i + 4);
     __syncthreads();
     if (i < ntiles)
-      attend_tile_half<kFp8>(reinterpret_cast<const uint16_t*>(lds_tile[slot]), lds_flags[slot],
+      attend_tile_half<kRowScale>(reinterpret_cast<const uint16_t*>(lds_tile[slot]), lds_flags[slot],
                              xbuf, st, qb, zscale, lane, wave, half);
   };
   for (int i = 0; i < ntiles; i += 2) {
@@ -403,11 +424,12 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s) {
+hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid(a.splits, a.num_tokens);
-  if (fp8) attn_kernel<true><<<grid, kAttnThreads, 0, s>>>(a);
-  else attn_kernel<false><<<grid, kAttnThreads, 0, s>>>(a);
+  if (fmt == kFmtFp8) attn_kernel<kFmtFp8><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx) attn_kernel<kFmtMx><<<grid, kAttnThreads, 0, s>>>(a);
+  else attn_kernel<kFmtBf16><<<grid, kAttnThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 

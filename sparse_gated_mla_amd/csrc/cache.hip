@@ -1,7 +1,8 @@
 // Cache append: the step just before the path in decode. Each token's new
 // 576-wide latent row and 128-wide indexer key are written into row
-// seq_start[b] + p of their caches, as bf16 (copied) or as OCP E4M3FN with one
-// fp32 scale per row.
+// seq_start[b] + p of their caches, as bf16 (copied), as OCP E4M3FN with one
+// fp32 scale per row, or as MX block-32 E4M3FN with one E8M0 exponent per 32
+// consecutive elements (fact sheet, Training: MXFP8 E4M3, one scale per 32).
 // Source: FP8 model card (nlp.com.ai, "A.X K2 FP8"): FP8 with dynamic, per-row
 // activation scaling; fact sheet (archdb, "A.X K2"): per token the cache holds
 // the 512 latent + 64 RoPE values and the 128-wide indexer key.
@@ -12,6 +13,11 @@
 // the format's definition: a value in binade [2^e, 2^(e+1)) (e >= -6) has code
 // spacing 2^(e-3), below 2^-6 the spacing is 2^-9; scaling by the spacing is
 // exact, rintf rounds to nearest even, and the result is re-encoded.
+//
+// MX: block exponent e - 127 = floor(log2 max|x|) - 8 (8 = exponent of 448),
+// clamped to [-127, 127], e = 0 for a block of zeros (the Open Compute
+// Project MX format's rule); each element is x * 2^(127 - e) (exact) encoded
+// as above.
 //
 // Mapping: one workgroup of two waves per token; wave 0 writes the latent row
 // (72 16-byte units, one or two per lane), wave 1 the indexer key (16 units).
@@ -40,9 +46,10 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
 // One row of `units` 16-byte units (8 bf16 each), lane l taking units l and l + 64.
+// scale_out: the row's fp32 scale (kFmtFp8) or its E8M0 block exponents (kFmtMx).
 template <int kUnits>
 __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uint8_t* __restrict__ dst,
-                                           float* __restrict__ scale_out, bool fp8, int lane) {
+                                           void* __restrict__ scale_out, int fmt, int lane) {
   constexpr int kPer = (kUnits + 63) / 64;
   u32x4 v[kPer];
   float amax = 0.0f;
@@ -54,11 +61,43 @@ __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uin
 #pragma unroll
     for (int c = 0; c < 4; ++c) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(v[j][c])), fabsf(bf16_hi(v[j][c]))));
   }
-  if (!fp8) {
+  if (fmt == kFmtBf16) {
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int u = lane + 64 * j;
       if (u < kUnits) *reinterpret_cast<u32x4*>(dst + 16 * u) = v[j];
+    }
+    return;
+  }
+  if (fmt == kFmtMx) {
+    // a block of 32 elements is units 4b .. 4b+3: four neighbouring lanes
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int u = lane + 64 * j;
+      float bmax = 0.0f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bmax = fmaxf(bmax, fmaxf(fabsf(bf16_lo(v[j][c])), fabsf(bf16_hi(v[j][c]))));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 1));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 2));
+      int e = 0;
+      if (bmax > 0.0f) {
+        int ea;
+        frexpf(bmax, &ea);                       // floor(log2 bmax) = ea - 1
+        e = min(max(ea - 1 - 8, -127), 127) + 127;
+      }
+      if (u < kUnits) {
+        uint32_t b[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          b[2 * c] = e4m3fn_encode(ldexpf(bf16_lo(v[j][c]), 127 - e));
+          b[2 * c + 1] = e4m3fn_encode(ldexpf(bf16_hi(v[j][c]), 127 - e));
+        }
+        u32x2 out;
+        out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+        out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+        *reinterpret_cast<u32x2*>(dst + 8 * u) = out;
+        if ((u & 3) == 0) static_cast<uint8_t*>(scale_out)[u >> 2] = (uint8_t)e;
+      }
     }
     return;
   }
@@ -80,7 +119,14 @@ __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uin
       *reinterpret_cast<u32x2*>(dst + 8 * u) = out;
     }
   }
-  if (lane == 0) *scale_out = scale;
+  if (lane == 0) *static_cast<float*>(scale_out) = scale;
+}
+
+// Where row `row`'s scale goes: an fp32 per row, or width/32 E8M0 bytes per row.
+__device__ __forceinline__ void* scale_row(void* base, int fmt, int64_t row, int width) {
+  if (fmt == kFmtFp8) return static_cast<float*>(base) + row;
+  if (fmt == kFmtMx) return static_cast<uint8_t*>(base) + row * (width / 32);
+  return nullptr;
 }
 
 __global__ __launch_bounds__(128) void cache_append_kernel(CacheArgs a) {
@@ -94,13 +140,13 @@ __global__ __launch_bounds__(128) void cache_append_kernel(CacheArgs a) {
   if (row < 0 || row >= a.batch.cache_rows) return;
   if (wave == 0) {
     if (!a.latent || !a.kv) return;
-    append_row<kDQK / 8>(a.latent + (int64_t)t * kDQK, a.kv + row * (a.kv_fp8 ? kDQK : 2 * kDQK),
-                         a.kv_fp8 ? a.kv_scale + row : nullptr, a.kv_fp8, lane);
+    append_row<kDQK / 8>(a.latent + (int64_t)t * kDQK, a.kv + row * (a.kv_fmt != kFmtBf16 ? kDQK : 2 * kDQK),
+                         scale_row(a.kv_scale, a.kv_fmt, row, kDQK), a.kv_fmt, lane);
   } else {
     if (!a.key || !a.k_idx) return;
     append_row<kIdxDim / 8>(a.key + (int64_t)t * kIdxDim,
-                            a.k_idx + row * (a.k_idx_fp8 ? kIdxDim : 2 * kIdxDim),
-                            a.k_idx_fp8 ? a.k_idx_scale + row : nullptr, a.k_idx_fp8, lane);
+                            a.k_idx + row * (a.k_idx_fmt != kFmtBf16 ? kIdxDim : 2 * kIdxDim),
+                            scale_row(a.k_idx_scale, a.k_idx_fmt, row, kIdxDim), a.k_idx_fmt, lane);
   }
 }
 

@@ -22,8 +22,11 @@
 // - Epilogue, per lane: ReLU, times w, summed over the lane's 32 heads. One
 //   cross-half shuffle then gives each position's score, which is stored at
 //   once (and counted, see below) while the wave's next tiles are in flight.
-// - fp8. Keys are widened to bf16 exactly on the LDS read. The row scale
-//   multiplies each head's dot product before the ReLU.
+// - fp8. Keys are widened to bf16 exactly on the LDS read. A per-row fp32
+//   scale multiplies each head's dot product before the ReLU. An MX block-32
+//   key (fact sheet, Training: MXFP8 with one scale per 32 consecutive
+//   elements) has four E8M0 exponents per row; each is applied to its 32 dims
+//   as they are widened (payload times a power of two is exact in bf16).
 // - Fused top-k. The variant used by the whole forward pass also counts the
 //   top 12 key bits of every score into a per-token histogram (the first radix
 //   level of the top-k).
@@ -37,7 +40,7 @@ constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;
 // key tiles in flight per wave (more did not help the fp8 variant)
-template <bool kFp8> constexpr int kStages = 3;
+constexpr int kStages = 3;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
@@ -54,18 +57,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 // the workgroup streams through contiguous memory. Tile row r (the MFMA
 // column) is group row (r / kRowsPerLoad) * 4 * kRowsPerLoad + w * kRowsPerLoad
 // + r % kRowsPerLoad.
-template <bool kFp8>
+template <int kFmt>
 struct KeyTile {
+  static constexpr bool kFp8 = kFmt != kFmtBf16;   // one-byte payloads
   // bf16 tile: 8 loads of 1 KiB (4 rows of 256 B each); load s, lane l -> tile
   //   row 4s + l/16, 16-byte chunk l%16.
   // fp8 tile:  4 loads of 1 KiB (8 rows of 128 B each); load s, lane l -> tile
-  //   row 8s + l/8, chunk l%8; plus the fp32 scale of tile row l%32.
+  //   row 8s + l/8, chunk l%8; plus the 32-bit scale word of tile row l%32
+  //   (the fp32 row scale, or the four E8M0 block exponents).
   static constexpr int kLoads = kFp8 ? 4 : 8;
   static constexpr int kRowBytes = kFp8 ? 128 : 256;
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;
   static constexpr int kGroupRows = kWaves * kTile;
   u32x4 v[kLoads];
-  float scale;
+  uint32_t scale;
 
   // chunk position of tile row r of wave w in group grp
   static __device__ __forceinline__ int position(int grp, int w, int r) {
@@ -80,8 +85,7 @@ struct KeyTile {
     for (int s = 0; s < kLoads; ++s)
       v[s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off + s * kWaves * 1024, 0, kNonTemporal));
     if constexpr (kFp8)
-      scale = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                            scales, position(grp, w, lane & 31) * 4, 0, 0));
+      scale = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, position(grp, w, lane & 31) * 4, 0, 0);
     // keep each tile's loads together and in program order, so the wait for
     // one tile never covers the loads of the tile issued after it
     __builtin_amdgcn_sched_barrier(0);
@@ -101,8 +105,10 @@ struct KeyTile {
     }
   }
 
-  // B operands for the 8 k-steps: row n = lane%32, dims 64g + 8s .. +7 (g = lane/32)
-  static __device__ __forceinline__ void operands(const uint8_t* lds, int lane, u32x4 (&b)[8]) {
+  // B operands for the 8 k-steps: row n = lane%32, dims 64g + 8s .. +7 (g = lane/32).
+  // sw: the row's scale word (MX: byte j is the exponent of dims 32j .. 32j+31).
+  static __device__ __forceinline__ void operands(const uint8_t* lds, int lane, uint32_t sw,
+                                                  u32x4 (&b)[8]) {
     const int n = lane & 31, g = lane >> 5;
     if constexpr (!kFp8) {
 #pragma unroll
@@ -113,8 +119,20 @@ struct KeyTile {
       for (int s = 0; s < 4; ++s) {
         // chunk 4g + s holds dims 64g + 16s .. +15 = steps 2s and 2s+1
         u32x4 raw = *reinterpret_cast<const u32x4*>(lds + n * 128 + 16 * slot(n, 4 * g + s));
-        u32x2 a = e4m3x4_to_bf16x4(raw.x), bb = e4m3x4_to_bf16x4(raw.y);
-        u32x2 c = e4m3x4_to_bf16x4(raw.z), d = e4m3x4_to_bf16x4(raw.w);
+        u32x2 a, bb, c, d;
+        if constexpr (kFmt == kFmtMx) {
+          // dims 64g + 16s .. +15 lie in block 2g + s/2
+          const float bs = e8m0_to_f32((sw >> (8 * (2 * g + (s >> 1)))) & 0xFFu);
+          a = e4m3x4_scaled_to_bf16x4(raw.x, bs);
+          bb = e4m3x4_scaled_to_bf16x4(raw.y, bs);
+          c = e4m3x4_scaled_to_bf16x4(raw.z, bs);
+          d = e4m3x4_scaled_to_bf16x4(raw.w, bs);
+        } else {
+          a = e4m3x4_to_bf16x4(raw.x);
+          bb = e4m3x4_to_bf16x4(raw.y);
+          c = e4m3x4_to_bf16x4(raw.z);
+          d = e4m3x4_to_bf16x4(raw.w);
+        }
         b[2 * s] = u32x4{a.x, a.y, bb.x, bb.y};
         b[2 * s + 1] = u32x4{c.x, c.y, d.x, d.y};
       }
@@ -125,12 +143,13 @@ struct KeyTile {
 // Scores one staged tile. Returns, in lanes 0..31, the score of tile row
 // `lane` (lanes 32..63 hold the same values). lds_w holds the token's 64 head
 // weights; each lane reads the 32 that match its accumulator rows (4
-// consecutive heads per b128 read).
-template <bool kFp8>
-__device__ __forceinline__ float score_tile(const uint8_t* lds, float kscale, int lane,
+// consecutive heads per b128 read). sw: the scale word of row lane % 32.
+template <int kFmt>
+__device__ __forceinline__ float score_tile(const uint8_t* lds, uint32_t sw, int lane,
                                             const u32x4 (&qa)[2][8], const float* lds_w) {
   u32x4 b[8];
-  KeyTile<kFp8>::operands(lds, lane, b);
+  KeyTile<kFmt>::operands(lds, lane, sw, b);
+  const float kscale = __uint_as_float(sw);
   f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
@@ -147,7 +166,7 @@ __device__ __forceinline__ float score_tile(const uint8_t* lds, float kscale, in
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float d0 = acc0[4 * q + j], d1 = acc1[4 * q + j];
-      if constexpr (kFp8) { d0 *= kscale; d1 *= kscale; }
+      if constexpr (kFmt == kFmtFp8) { d0 *= kscale; d1 *= kscale; }
       sc = fmaf(w0[j], fmaxf(d0, 0.0f), sc);
       sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
     }
@@ -165,9 +184,11 @@ __device__ __forceinline__ void load_query(const uint16_t* q, int lane, u32x4 (&
       qa[mb][s] = *reinterpret_cast<const u32x4*>(q + (32 * mb + nidx) * kIdxDim + 64 * g + 8 * s);
 }
 
-template <bool kFp8, bool kHist>
+template <int kFmt, bool kHist>
 __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
-  constexpr int kTileBytes = KeyTile<kFp8>::kRowBytes * kTile;
+  using Tile = KeyTile<kFmt>;
+  constexpr bool kFp8 = Tile::kFp8;
+  constexpr int kTileBytes = Tile::kRowBytes * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
   __shared__ __attribute__((aligned(16))) float lds_w[kIdxHeads];
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
@@ -190,30 +211,31 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
     u32x4 qa[2][8];
     load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
 
-    const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * KeyTile<kFp8>::kRowBytes,
-                                  (uint32_t)len * KeyTile<kFp8>::kRowBytes);
-    const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + base + chunk0) : (const void*)a.k_idx,
-                                    kFp8 ? (uint32_t)len * 4u : 0u);
-    const int ngroups = (len + KeyTile<kFp8>::kGroupRows - 1) / KeyTile<kFp8>::kGroupRows;
+    const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * Tile::kRowBytes,
+                                  (uint32_t)len * Tile::kRowBytes);
+    const rsrc_t scales = make_rsrc(
+        kFp8 ? (const void*)(static_cast<const uint32_t*>(a.k_scale) + base + chunk0) : (const void*)a.k_idx,
+        kFp8 ? (uint32_t)len * 4u : 0u);
+    const int ngroups = (len + Tile::kGroupRows - 1) / Tile::kGroupRows;
     float* srow = a.scores + (int64_t)t * a.ld + chunk0;
 
     // this wave's tile of every group; kStages groups in flight. Loads are
     // never skipped (past the chunk they read zeros), so each wait is exact.
-    constexpr int S = kStages<kFp8>;
-    KeyTile<kFp8> st[S];
+    constexpr int S = kStages;
+    Tile st[S];
 #pragma unroll
     for (int j = 0; j < S; ++j) st[j].load(keys, scales, j, wave, lane);
     for (int i = 0; i < ngroups; i += S) {
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         st[j].store(lds, lane);
-        const float ks = st[j].scale;
+        const uint32_t ks = st[j].scale;
         st[j].load(keys, scales, i + j + S, wave, lane);
         if (i + j < ngroups) {
           // scores go out as they are made: each is stored and counted while
           // the wave's later tiles are still in flight
-          const float sc = score_tile<kFp8>(lds, ks, lane, qa, lds_w);
-          const int p = KeyTile<kFp8>::position(i + j, wave, lane);
+          const float sc = score_tile<kFmt>(lds, ks, lane, qa, lds_w);
+          const int p = Tile::position(i + j, wave, lane);
           if (lane < 32 && p < len) {
             srow[p] = sc;
             if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
@@ -240,15 +262,16 @@ constexpr int kPfTokens = 8;                  // tokens per workgroup, one per w
 constexpr int kPfThreads = kPfTokens * 64;
 constexpr int kPfStages = 4;                  // key tiles in flight per thread
 
-template <bool kFp8, bool kHist>
+template <int kFmt, bool kHist>
 __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerArgs a) {
-  using Tile = KeyTile<kFp8>;
+  using Tile = KeyTile<kFmt>;
+  constexpr bool kFp8 = Tile::kFp8;
   constexpr int kTileBytes = Tile::kRowBytes * kTile;
   constexpr int kUnits = kTileBytes / 16;     // 16-byte units of a tile: 512 (bf16) or 256 (fp8)
   constexpr int kUnitsPerRow = Tile::kRowBytes / 16;
   static_assert(kUnits <= kPfThreads, "one unit per thread and tile");
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[2][kTileBytes];
-  __shared__ float lds_scale[2][kTile];
+  __shared__ uint32_t lds_scale[2][kTile];
   __shared__ __attribute__((aligned(16))) float lds_w[kPfTokens][kIdxHeads];
   __shared__ uint32_t lds_hist[kHist ? kPfTokens : 1][kHist ? kHist1 : 1];
   __shared__ int32_t lds_seq[kPfTokens];
@@ -298,8 +321,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
     const bool mine = (members >> wave) & 1u;
     const int64_t sbase = lds_base[lead];
     const rsrc_t keys = make_rsrc(a.k_idx + sbase * Tile::kRowBytes, (uint32_t)N * Tile::kRowBytes);
-    const rsrc_t scales = make_rsrc(kFp8 ? (const void*)(a.k_scale + sbase) : (const void*)a.k_idx,
-                                    kFp8 ? (uint32_t)N * 4u : 0u);
+    const rsrc_t scales = make_rsrc(
+        kFp8 ? (const void*)(static_cast<const uint32_t*>(a.k_scale) + sbase) : (const void*)a.k_idx,
+        kFp8 ? (uint32_t)N * 4u : 0u);
     u32x4 qa[2][8];
     if (mine) load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
     float* srow = a.scores + (int64_t)t * a.ld;
@@ -307,14 +331,14 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
 
     // register stages: tile i's unit is loaded kPfStages tiles ahead
     u32x4 stv[kPfStages];
-    float sts[kPfStages];
+    uint32_t sts[kPfStages];
     auto issue = [&](int j, int tile) {
       // units past the sequence (or idle threads) read zeros
       const int off = loader ? tile * kTileBytes + ur * Tile::kRowBytes + uc * 16 : (int)0x7ffffff0;
       stv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(keys, off, 0, kNonTemporal));
       if constexpr (kFp8)
-        sts[j] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-            scales, scale_loader ? (tile * kTile + (int)threadIdx.x - kUnits) * 4 : (int)0x7ffffff0, 0, 0));
+        sts[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+            scales, scale_loader ? (tile * kTile + (int)threadIdx.x - kUnits) * 4 : (int)0x7ffffff0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
@@ -330,8 +354,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
         issue(j, i + kPfStages);
         __syncthreads();
         if (mine && i < ntiles) {
-          const float ks = kFp8 ? lds_scale[i & 1][lane & 31] : 1.0f;
-          const float sc = score_tile<kFp8>(lds_tiles[i & 1], ks, lane, qa, lds_w[wave]);
+          const uint32_t ks = kFp8 ? lds_scale[i & 1][lane & 31] : 0u;
+          const float sc = score_tile<kFmt>(lds_tiles[i & 1], ks, lane, qa, lds_w[wave]);
           // tile row r is position 32i + r in this layout
           const int p = i * kTile + lane;
           if (lane < 32 && p < n) {
@@ -351,32 +375,37 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
   }
 }
 
-}  // namespace
-
-hipError_t launch_indexer_prefill(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s) {
-  if (a.num_tokens == 0) return hipSuccess;
+template <int kFmt>
+hipError_t launch_prefill_fmt(const IndexerArgs& a, bool fused_hist, hipStream_t s) {
   const dim3 grid((a.num_tokens + kPfTokens - 1) / kPfTokens);
-  if (fp8) {
-    if (fused_hist) indexer_prefill_kernel<true, true><<<grid, kPfThreads, 0, s>>>(a);
-    else indexer_prefill_kernel<true, false><<<grid, kPfThreads, 0, s>>>(a);
-  } else {
-    if (fused_hist) indexer_prefill_kernel<false, true><<<grid, kPfThreads, 0, s>>>(a);
-    else indexer_prefill_kernel<false, false><<<grid, kPfThreads, 0, s>>>(a);
-  }
+  if (fused_hist) indexer_prefill_kernel<kFmt, true><<<grid, kPfThreads, 0, s>>>(a);
+  else indexer_prefill_kernel<kFmt, false><<<grid, kPfThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s) {
-  if (a.num_tokens == 0) return hipSuccess;
-  dim3 grid((a.batch.max_len + indexer_chunk(fp8) - 1) / indexer_chunk(fp8), a.num_tokens);
-  if (fp8) {
-    if (fused_hist) indexer_kernel<true, true><<<grid, kThreads, 0, s>>>(a);
-    else indexer_kernel<true, false><<<grid, kThreads, 0, s>>>(a);
-  } else {
-    if (fused_hist) indexer_kernel<false, true><<<grid, kThreads, 0, s>>>(a);
-    else indexer_kernel<false, false><<<grid, kThreads, 0, s>>>(a);
-  }
+template <int kFmt>
+hipError_t launch_indexer_fmt(const IndexerArgs& a, bool fused_hist, hipStream_t s) {
+  const int chunk = indexer_chunk(kFmt != kFmtBf16);
+  const dim3 grid((a.batch.max_len + chunk - 1) / chunk, a.num_tokens);
+  if (fused_hist) indexer_kernel<kFmt, true><<<grid, kThreads, 0, s>>>(a);
+  else indexer_kernel<kFmt, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_prefill(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (fmt == kFmtFp8) return launch_prefill_fmt<kFmtFp8>(a, fused_hist, s);
+  if (fmt == kFmtMx) return launch_prefill_fmt<kFmtMx>(a, fused_hist, s);
+  return launch_prefill_fmt<kFmtBf16>(a, fused_hist, s);
+}
+
+hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  if (fmt == kFmtFp8) return launch_indexer_fmt<kFmtFp8>(a, fused_hist, s);
+  if (fmt == kFmtMx) return launch_indexer_fmt<kFmtMx>(a, fused_hist, s);
+  return launch_indexer_fmt<kFmtBf16>(a, fused_hist, s);
 }
 
 }  // namespace sga

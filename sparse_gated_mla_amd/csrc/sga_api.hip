@@ -118,11 +118,15 @@ sga_status check_batch(const sga_batch* b) {
   return SGA_OK;
 }
 
-sga_status check_store(const void* data, const float* scale, sga_dtype dt) {
+// A cache and its scales. mx_align: the alignment the kernels need of an MX
+// exponent array (4 for the indexer keys, read one 32-bit word per row; 1 for
+// the latent rows, read by byte).
+sga_status check_store(const void* data, const void* scale, sga_dtype dt, uintptr_t mx_align) {
   if (!data || !aligned16(data)) return SGA_ERR_INVALID_ARG;
-  if (reinterpret_cast<uintptr_t>(scale) % alignof(float) != 0) return SGA_ERR_INVALID_ARG;
+  const uintptr_t sa = reinterpret_cast<uintptr_t>(scale);
   if (dt == SGA_BF16) return scale ? SGA_ERR_INVALID_ARG : SGA_OK;
-  if (dt == SGA_FP8_E4M3) return scale ? SGA_OK : SGA_ERR_INVALID_ARG;
+  if (dt == SGA_FP8_E4M3) return scale && sa % alignof(float) == 0 ? SGA_OK : SGA_ERR_INVALID_ARG;
+  if (dt == SGA_MXFP8_E4M3) return scale && sa % mx_align == 0 ? SGA_OK : SGA_ERR_INVALID_ARG;
   return SGA_ERR_UNSUPPORTED;
 }
 
@@ -192,7 +196,7 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
 }
 
 sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* kv,
-                         const float* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
+                         const void* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
                          int32_t k, float sm_scale, const float* gate, float* out, float* lse,
                          const AttnPlan& plan, const AttnLayout& L, hipStream_t stream) {
   AttnArgs a;
@@ -211,7 +215,7 @@ sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* 
   a.rows_per_split = plan.rows_per_split;
   a.part_o = L.part_o;
   a.part_ml = L.part_ml;
-  SGA_HIP(sga::launch_attention(a, kv_dtype == SGA_FP8_E4M3, stream));
+  SGA_HIP(sga::launch_attention(a, (int)kv_dtype, stream));
   SGA_HIP(sga::launch_combine(a, stream));
   return SGA_OK;
 }
@@ -230,6 +234,10 @@ size_t attn_ws(int32_t T, int32_t k) {
 
 }  // namespace
 
+static_assert(SGA_BF16 == sga::kFmtBf16 && SGA_FP8_E4M3 == sga::kFmtFp8 &&
+                  SGA_MXFP8_E4M3 == sga::kFmtMx,
+              "cache formats are passed to the kernels as their sga_dtype values");
+
 extern "C" {
 
 SGA_API const char* sga_status_string(sga_status s) {
@@ -246,13 +254,13 @@ SGA_API const char* sga_status_string(sga_status s) {
 SGA_API int sga_version(void) { return 100; }
 
 SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, const float* w,
-                                    const void* k_idx, const float* k_idx_scale,
+                                    const void* k_idx, const void* k_idx_scale,
                                     sga_dtype k_idx_dtype, float* scores, int64_t ld,
                                     hipStream_t stream) {
   SGA_TRY(check_batch(batch));
   if (batch->num_tokens == 0) return SGA_OK;
   if (!q_idx || !w || !scores || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
-  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
+  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype, 4));
   if (ld < batch->max_len) return SGA_ERR_INVALID_ARG;
   IndexerArgs a;
   memset(&a, 0, sizeof(a));
@@ -265,8 +273,8 @@ SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, c
   a.scores = scores;
   a.ld = ld;
   return hip_status(many_tokens_per_seq(batch)
-                        ? sga::launch_indexer_prefill(a, k_idx_dtype == SGA_FP8_E4M3, false, stream)
-                        : sga::launch_indexer(a, k_idx_dtype == SGA_FP8_E4M3, false, stream));
+                        ? sga::launch_indexer_prefill(a, (int)k_idx_dtype, false, stream)
+                        : sga::launch_indexer(a, (int)k_idx_dtype, false, stream));
 }
 
 SGA_API size_t sga_topk_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k) {
@@ -295,7 +303,7 @@ SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k) {
 }
 
 SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs, const void* kv,
-                                       const float* kv_scale, sga_dtype kv_dtype,
+                                       const void* kv_scale, sga_dtype kv_dtype,
                                        const int32_t* indices, int32_t k, float sm_scale,
                                        const float* gate_logits, float* out, float* lse,
                                        void* ws, size_t ws_bytes, hipStream_t stream) {
@@ -305,7 +313,7 @@ SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs
   if (!isfinite(sm_scale)) return SGA_ERR_INVALID_ARG;
   if (batch->num_tokens == 0) return SGA_OK;
   if (!q_abs || !indices || !out || !aligned16(q_abs) || !aligned16(out)) return SGA_ERR_INVALID_ARG;
-  SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+  SGA_TRY(check_store(kv, kv_scale, kv_dtype, 1));
   AttnPlan plan = plan_attention(batch->num_tokens, k);
   size_t need = attn_ws(batch->num_tokens, k);
   if (need > 0 && (!ws || ws_bytes < need)) return SGA_ERR_WORKSPACE;
@@ -326,8 +334,8 @@ SGA_API size_t sga_forward_workspace_size(int32_t num_tokens, int32_t max_len, i
 }
 
 SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const float* w,
-                               const void* k_idx, const float* k_idx_scale, sga_dtype k_idx_dtype,
-                               const void* q_abs, const void* kv, const float* kv_scale,
+                               const void* k_idx, const void* k_idx_scale, sga_dtype k_idx_dtype,
+                               const void* q_abs, const void* kv, const void* kv_scale,
                                sga_dtype kv_dtype, int32_t k, float sm_scale,
                                const float* gate_logits, float* out, float* lse,
                                int32_t* indices_out, void* ws, size_t ws_bytes,
@@ -339,8 +347,8 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   if (batch->num_tokens == 0) return SGA_OK;
   if (!q_idx || !w || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
   if (!q_abs || !out || !aligned16(q_abs) || !aligned16(out)) return SGA_ERR_INVALID_ARG;
-  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
-  SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+  SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype, 4));
+  SGA_TRY(check_store(kv, kv_scale, kv_dtype, 1));
   const int32_t T = batch->num_tokens;
   size_t need = sga_forward_workspace_size(T, batch->max_len, k);
   if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
@@ -368,9 +376,9 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   ia.k = k;
   if (trace) SGA_TRY(record(trace->indexer_begin, stream));
   if (many_tokens_per_seq(batch))
-    SGA_HIP(sga::launch_indexer_prefill(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
+    SGA_HIP(sga::launch_indexer_prefill(ia, (int)k_idx_dtype, true, stream));
   else
-    SGA_HIP(sga::launch_indexer(ia, k_idx_dtype == SGA_FP8_E4M3, true, stream));
+    SGA_HIP(sga::launch_indexer(ia, (int)k_idx_dtype, true, stream));
   if (trace) SGA_TRY(record(trace->indexer_end, stream));
   SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
   if (trace) SGA_TRY(record(trace->topk_end, stream));
@@ -381,18 +389,18 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
 }
 
 SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,
-                                    void* kv, float* kv_scale, sga_dtype kv_dtype, void* k_idx,
-                                    float* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream) {
+                                    void* kv, void* kv_scale, sga_dtype kv_dtype, void* k_idx,
+                                    void* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream) {
   SGA_TRY(check_batch(batch));
   if (!latent != !kv || !idx_key != !k_idx) return SGA_ERR_INVALID_ARG;
   const bool do_kv = latent != nullptr, do_key = idx_key != nullptr;
   if (do_kv) {
     if (!aligned16(latent)) return SGA_ERR_INVALID_ARG;
-    SGA_TRY(check_store(kv, kv_scale, kv_dtype));
+    SGA_TRY(check_store(kv, kv_scale, kv_dtype, 1));
   }
   if (do_key) {
     if (!aligned16(idx_key)) return SGA_ERR_INVALID_ARG;
-    SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype));
+    SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype, 1));
   }
   if (batch->num_tokens == 0 || (!do_kv && !do_key)) return SGA_OK;
   CacheArgs a;
@@ -402,10 +410,10 @@ SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, 
   a.key = do_key ? static_cast<const uint16_t*>(idx_key) : nullptr;
   a.kv = do_kv ? static_cast<uint8_t*>(kv) : nullptr;
   a.kv_scale = do_kv ? kv_scale : nullptr;
-  a.kv_fp8 = do_kv && kv_dtype == SGA_FP8_E4M3;
+  a.kv_fmt = do_kv ? (int)kv_dtype : sga::kFmtBf16;
   a.k_idx = do_key ? static_cast<uint8_t*>(k_idx) : nullptr;
   a.k_idx_scale = do_key ? k_idx_scale : nullptr;
-  a.k_idx_fp8 = do_key && k_idx_dtype == SGA_FP8_E4M3;
+  a.k_idx_fmt = do_key ? (int)k_idx_dtype : sga::kFmtBf16;
   return hip_status(sga::launch_cache_append(a, stream));
 }
 

@@ -51,6 +51,28 @@ __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t packed) {
   return r;
 }
 
+// The fp32 value of an E8M0 block exponent e: 2^(e - 127) (e = 0 is the
+// subnormal 2^-127). e = 255 (NaN) is not a valid input.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// Four OCP E4M3FN bytes times a power-of-two block scale -> four bf16, packed
+// two per dword. The products are exact in fp32; keeping the upper 16 bits is
+// exact whenever they are bf16 normals or zero (block scale >= 2^-117).
+__device__ __forceinline__ u32x2 e4m3x4_scaled_to_bf16x4(uint32_t packed, float scale) {
+  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, false);
+  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, true);
+  lo.x *= scale;
+  lo.y *= scale;
+  hi.x *= scale;
+  hi.y *= scale;
+  u32x2 r;
+  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
+  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  return r;
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);

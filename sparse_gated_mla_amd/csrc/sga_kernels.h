@@ -15,6 +15,11 @@ struct TopkCtrl {
   uint32_t above1;      // scores whose top 12 key bits exceed digit1
 };
 
+// Cache element formats (the values of sga_dtype).
+constexpr int kFmtBf16 = 0;    // bf16 rows
+constexpr int kFmtFp8 = 1;     // E4M3FN rows, one fp32 scale per row
+constexpr int kFmtMx = 2;      // E4M3FN rows, one E8M0 exponent per 32 elements
+
 constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup (bf16 keys)
 // fp8 keys are half the bytes: a workgroup takes twice the positions
 // (measured: one round of workgroups streams fp8 keys best)
@@ -28,8 +33,9 @@ struct IndexerArgs {
   int num_tokens;
   const uint16_t* q_idx;   // [T,64,128] bf16
   const float* w;          // [T,64]
-  const uint8_t* k_idx;    // [rows,128] bf16 (256 B) or fp8 (128 B) rows
-  const float* k_scale;    // [rows] for fp8
+  const uint8_t* k_idx;    // [rows,128] bf16 (256 B) or E4M3FN (128 B) rows
+  const void* k_scale;     // one 32-bit word per row: the fp32 scale (kFmtFp8) or
+                           // the row's four E8M0 block exponents (kFmtMx)
   float* scores;           // [T,ld]
   int64_t ld;
   // top-k first level, filled by the fused variant
@@ -63,8 +69,8 @@ struct AttnArgs {
   BatchView batch;
   int num_tokens;
   const uint16_t* q_abs;   // [T,64,576] bf16
-  const uint8_t* kv;       // [rows,576] bf16 or fp8
-  const float* kv_scale;   // [rows] for fp8
+  const uint8_t* kv;       // [rows,576] bf16 or E4M3FN
+  const void* kv_scale;    // [rows] fp32 (kFmtFp8) or [rows,18] E8M0 bytes (kFmtMx)
   const int32_t* indices;  // [T,k]
   int k;
   float sm_scale;
@@ -84,21 +90,21 @@ struct CacheArgs {
   int num_tokens;
   const uint16_t* latent;  // [T,576] bf16, or null
   const uint16_t* key;     // [T,128] bf16, or null
-  uint8_t* kv;             // [rows,576] bf16 or fp8 payload
-  float* kv_scale;         // [rows] for fp8
-  bool kv_fp8;
-  uint8_t* k_idx;          // [rows,128] bf16 or fp8 payload
-  float* k_idx_scale;      // [rows] for fp8
-  bool k_idx_fp8;
+  uint8_t* kv;             // [rows,576] bf16 or E4M3FN payload
+  void* kv_scale;          // [rows] fp32 (kFmtFp8) or [rows,18] E8M0 bytes (kFmtMx)
+  int kv_fmt;
+  uint8_t* k_idx;          // [rows,128] bf16 or E4M3FN payload
+  void* k_idx_scale;       // [rows] fp32 (kFmtFp8) or [rows,4] E8M0 bytes (kFmtMx)
+  int k_idx_fmt;
 };
 
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
 hipError_t launch_cache_append(const CacheArgs& a, hipStream_t s);
-hipError_t launch_indexer(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
+hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s);
 // Eight tokens per workgroup sharing each key tile: for batches with many
 // tokens per sequence. With fused_hist it writes each token's digit-1
 // histogram with plain stores (it owns the token).
-hipError_t launch_indexer_prefill(const IndexerArgs& a, bool fp8, bool fused_hist, hipStream_t s);
+hipError_t launch_indexer_prefill(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s);
 constexpr int kPrefillTokensPerSeq = 64;   // mean tokens per sequence from which it is used
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
@@ -108,7 +114,7 @@ constexpr int64_t kMaxTokenWords = 8192;     // bitmap words for the one-kernel 
 int topk_finalize_lds_cap(int64_t words);
 int topk_token_lds_cap(int64_t words);       // 0: use the multi-kernel top-k
 hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s);
-hipError_t launch_attention(const AttnArgs& a, bool fp8, hipStream_t s);
+hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s);
 
 }  // namespace sga

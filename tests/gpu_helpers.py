@@ -74,8 +74,8 @@ class Dev:
 def stores(wl):
     """The oracle's views of the caches: raw bits plus format."""
     if wl.fp8:
-        ks = oracle.Store(wl.k_idx.view(torch.uint8).numpy(), "e4m3fn", wl.k_idx_scale.numpy())
-        vs = oracle.Store(wl.kv.view(torch.uint8).numpy(), "e4m3fn", wl.kv_scale.numpy())
+        ks = oracle.Store(wl.k_idx.view(torch.uint8).numpy(), wl.cache_fmt, wl.k_idx_scale.numpy())
+        vs = oracle.Store(wl.kv.view(torch.uint8).numpy(), wl.cache_fmt, wl.kv_scale.numpy())
     else:
         ks = oracle.Store(wl.k_idx.view(torch.int16).numpy().view(np.uint16), "bf16")
         vs = oracle.Store(wl.kv.view(torch.int16).numpy().view(np.uint16), "bf16")

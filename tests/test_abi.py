@@ -71,6 +71,8 @@ def test_index_scores_rejects_bad_arguments(lib):
     assert call(b, ks=FAKE, dt=0) == 1         # bf16 keys take no scale
     assert call(b, ks=None, dt=1) == 1         # fp8 keys need scales
     assert call(b, dt=7) == 2                  # unknown dtype
+    assert call(b, ks=None, dt=2) == 1         # MX keys need exponents
+    assert call(b, ks=ctypes.c_void_p(0x10002), dt=2) == 1   # read as 32-bit words: 4-byte aligned
     assert call(_batch(T=-1)) == 1
     assert call(_batch(B=0)) == 1
     assert call(_batch(max_len=(1 << 19) + 1)) == 2
@@ -108,6 +110,8 @@ def test_attention_rejects_bad_arguments(lib):
     assert call(b, out=FAKE_ODD) == 1
     assert call(b, kv=FAKE_ODD) == 1
     assert call(b, dt=1) == 1                  # fp8 without scales
+    assert call(b, dt=2) == 1                  # MX without exponents
+    assert call(b, dt=3) == 2
 
 
 def test_forward_rejects_bad_arguments(lib):
@@ -143,6 +147,8 @@ def test_cache_append_rejects_bad_arguments(lib):
     assert call(kvs=FAKE) == 1                 # bf16 cache with scales
     assert call(kvdt=1, kvs=ctypes.c_void_p(0x10002)) == 1   # misaligned scales
     assert call(kvdt=5) == 2
+    assert call(kvdt=2) == 1                   # MX cache without exponents
+    assert call(kdt=2) == 1
     assert call(_batch(T=-1)) == 1
     assert call(_batch(ptr=0)) == 1
     assert call(_batch(max_len=(1 << 19) + 1)) == 2

@@ -1,6 +1,6 @@
-"""GPU parity for sga_cache_append: the bytes it writes into bf16 and fp8 caches,
-and their row scales, against the oracle's cache append, bit for bit; rows it
-must not touch keep their contents."""
+"""GPU parity for sga_cache_append: the bytes it writes into bf16, fp8 (one
+scale per row) and MX block-32 caches, and their scales, against the oracle's
+cache append, bit for bit; rows it must not touch keep their contents."""
 import numpy as np
 import pytest
 import torch
@@ -14,7 +14,8 @@ pytestmark = pytest.mark.gpu
 
 SENT_BF16 = -0x5A5B          # int16 fill of untouched bf16 rows (0xA5A5)
 SENT_FP8 = 0xA5              # byte fill of untouched fp8 rows
-SENT_SCALE = -3.0            # fill of untouched row scales
+SENT_SCALE = -3.0            # fill of untouched fp32 row scales
+SENT_MX = 0xA5               # fill of untouched E8M0 exponents
 
 
 def _meta(lengths, tokens, starts=None):
@@ -31,6 +32,8 @@ def _cache(rows, width, fmt):
     if fmt == "bf16":
         return torch.full((rows, width), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16), None
     data = torch.full((rows, width), SENT_FP8, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
+    if fmt == "mx":
+        return data, torch.full((rows, width // 32), SENT_MX, dtype=torch.uint8, device="cuda")
     return data, torch.full((rows,), SENT_SCALE, dtype=torch.float32, device="cuda")
 
 
@@ -48,6 +51,15 @@ def _check_cache(data, scale, fmt, expect, rows_to_check=None):
     rows = list(range(data.shape[0])) if rows_to_check is None else list(rows_to_check)
     bits = _bits(data, None if rows_to_check is None else rows)
     sc = None if scale is None else scale.cpu().numpy()
+    if fmt == "mx":
+        for i, r in enumerate(rows):
+            if r in expect:
+                pay, ex = expect[r]
+                assert np.array_equal(bits[i], pay), f"row {r}: payload differs"
+                assert np.array_equal(sc[r], ex), f"row {r}: exponents {sc[r]} != {ex}"
+            else:
+                assert np.all(bits[i] == SENT_FP8) and np.all(sc[r] == SENT_MX), f"row {r} was written"
+        return
     fill = np.uint16(0xA5A5) if fmt == "bf16" else np.uint8(SENT_FP8)
     for i, r in enumerate(rows):
         if r in expect:
@@ -77,7 +89,8 @@ def _append(meta, cache_rows, latent, key, kv_fmt, key_fmt, max_len=None):
 def _oracle(meta, cache_rows, rows, fmt):
     seq, pos, starts, lens = meta
     bits = rows.view(torch.int16).numpy().view(np.uint16)
-    return oracle.cache_append(seq, pos, starts, lens, cache_rows, bits, "bf16" if fmt == "bf16" else "e4m3fn")
+    name = {"bf16": "bf16", "fp8": "e4m3fn", "mx": "mxfp8"}[fmt]
+    return oracle.cache_append(seq, pos, starts, lens, cache_rows, bits, name)
 
 
 def _run_and_check(meta, cache_rows, latent, key, kv_fmt, key_fmt, rows_to_check=None, what=""):
@@ -90,7 +103,8 @@ def _run_and_check(meta, cache_rows, latent, key, kv_fmt, key_fmt, rows_to_check
 
 
 @pytest.mark.parametrize("kv_fmt,key_fmt", [("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8"),
-                                            ("fp8", "bf16"), ("fp8", None), (None, "fp8")])
+                                            ("fp8", "bf16"), ("fp8", None), (None, "fp8"),
+                                            ("mx", "mx"), ("mx", "fp8"), ("bf16", "mx")])
 def test_ragged_batch(kv_fmt, key_fmt):
     lens = [37, 300, 5, 1000]
     toks = [(0, 0), (0, 36), (1, 299), (1, 150), (1, 0), (2, 4), (3, 999), (3, 998), (3, 500), (0, 17)]
@@ -105,7 +119,7 @@ def test_out_of_range_tokens_write_nothing():
     toks = [(0, 9), (-1, 3), (3, 0), (1, -1), (1, 20), (1, 19), (2, 14), (2, 15), (2, 29), (0, 0)]
     meta = _meta(lens, toks, starts)
     lat, key = si.append_rows(len(toks), seed=12)
-    for fmt in ("bf16", "fp8"):
+    for fmt in ("bf16", "fp8", "mx"):
         expect = _oracle(meta, 60, lat, fmt)
         assert sorted(expect) == [0, 9, 29, 59], sorted(expect)      # the oracle's skip rules
         _run_and_check(meta, 60, lat, key, fmt, fmt, what=f"skips {fmt}")
@@ -143,7 +157,7 @@ def test_edge_values():
     key = lat[:, :128].contiguous()
     T = lat.shape[0]
     meta = _meta([T], [(0, p) for p in range(T)])
-    for fmt in ("bf16", "fp8"):
+    for fmt in ("bf16", "fp8", "mx"):
         _run_and_check(meta, T, lat, key, fmt, fmt, what=f"edge {fmt}")
 
 
@@ -153,12 +167,13 @@ def test_prefill_chunk():
     lat, key = si.append_rows(4096, seed=13)
     _run_and_check(meta, 8192, lat, key, "fp8", "fp8", what="prefill fp8")
     _run_and_check(meta, 8192, lat, key, "bf16", "bf16", what="prefill bf16")
+    _run_and_check(meta, 8192, lat, key, "mx", "mx", what="prefill mx")
 
 
-@pytest.mark.parametrize("cfg", [2, 4])
+@pytest.mark.parametrize("cfg", [2, 4, 5])
 def test_full_size_decode(cfg):
-    # the long-context decode shapes: 16 x 131072 bf16, 8 x 262144 fp8; one new row per sequence
-    B, S, fmt = (16, 131072, "bf16") if cfg == 2 else (8, 262144, "fp8")
+    # the long-context decode shapes: 16 x 131072 bf16, 8 x 262144 fp8 or MX; one new row per sequence
+    B, S, fmt = {2: (16, 131072, "bf16"), 4: (8, 262144, "fp8"), 5: (8, 262144, "mx")}[cfg]
     meta = _meta([S] * B, [(b, S - 1) for b in range(B)])
     lat, key = si.append_rows(B, seed=20 + cfg)
     rows = B * S
@@ -178,3 +193,24 @@ def test_appended_fp8_rows_decode_close_to_inputs():
     q = np.abs(x) / s
     half = 0.5 * np.maximum(q * 2.0 ** -3, 2.0 ** -9) * s
     assert np.all(np.abs(got - x) <= half * (1 + 1e-5))
+
+
+def test_mx_edge_blocks():
+    # blocks whose maximum sits just below, at and above 448 * 2^k, blocks of
+    # bf16 subnormals, a block with one huge value, alternating signs, -0
+    rng = np.random.default_rng(15)
+    x = rng.normal(size=(6, 576)).astype(np.float32)
+    x[0, :32] = 0.0
+    x[0, 0] = 448.0 * 2.0 ** -5                      # scale 2^-5 exactly, payload 448
+    x[0, 32:64] = 15.5                               # saturates: 496 * 2^-5 clamps to 448
+    x[0, 64:96] = -0.0
+    x[1, :32] = 1.0e-39                              # bf16 subnormals: exponent clamps at 0
+    x[1, 32:64] = 3.0e38                             # near the top of bf16
+    x[1, 64] = -3.0e38
+    x[2, ::2] *= -1.0
+    x[3, 100] = 1e20                                 # one block dominated by one value
+    lat = torch.from_numpy(x).to(torch.bfloat16)
+    key = lat[:, :128].contiguous()
+    T = lat.shape[0]
+    meta = _meta([T], [(0, p) for p in range(T)])
+    _run_and_check(meta, T, lat, key, "mx", "mx", what="mx edge blocks")

@@ -11,7 +11,7 @@ from gpu_helpers import Dev, assert_lse_close, assert_out_close, run_oracle, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4])
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
 def test_decode_workload_full(cfg):
     wl = si.config(cfg)
     say(f"[full] {wl.name}: T={wl.num_tokens} B={wl.num_seqs} max_len={wl.max_len} fp8={wl.fp8}")
@@ -22,7 +22,7 @@ def test_decode_workload_full(cfg):
     got_idx = idx.cpu().numpy()
     bad = [t for t in range(wl.num_tokens) if not np.array_equal(got_idx[t], ref["indices"][t])]
     assert not bad, f"indices differ for tokens {bad}"
-    assert_out_close(out.cpu().numpy(), ref["out"], wl.fp8, wl.name)
+    assert_out_close(out.cpu().numpy(), ref["out"], wl.fp8 and not wl.mx, wl.name)
     assert_lse_close(lse.cpu().numpy(), ref["lse"], wl.name)
 
 

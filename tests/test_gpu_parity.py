@@ -17,7 +17,8 @@ def _check_forward(wl, gate=True, what=""):
     idx, out, lse = dev.forward(gate=gate)
     ref = run_oracle(wl, gate=gate)
     assert np.array_equal(idx.cpu().numpy(), ref["indices"]), "indices differ"
-    assert_out_close(out.cpu().numpy(), ref["out"], wl.fp8, what)
+    # MX rows decode exactly to bf16 values: they are held to the bf16 bar
+    assert_out_close(out.cpu().numpy(), ref["out"], wl.fp8 and not wl.mx, what)
     assert_lse_close(lse.cpu().numpy(), ref["lse"], what)
     return dev, (idx, out, lse), ref
 
@@ -243,3 +244,37 @@ def test_prefill_index_scores_exact():
         n = r.shape[0]
         assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
         assert np.all(np.isnan(s[i, n:])), "wrote beyond the visible rows"
+
+
+def test_mx_caches_small():
+    wl = si.build("mx_small", [3000, 2100], [(0, 2999), (1, 2099), (0, 1000)], seed=21, mx=True)
+    _check_forward(wl)
+
+
+def test_mx_index_scores_exact():
+    # integer keys times power-of-two block scales: every score is exact
+    wl = si.build("mx_scores", [2500, 700], [(0, 2499), (1, 699), (0, 31)], seed=22, mx=True)
+    say("[index_scores] MX keys")
+    dev = Dev(wl)
+    s = dev.scores().cpu().numpy()
+    ref = run_oracle(wl, keep_scores=True)
+    for i, r in enumerate(ref["scores"]):
+        n = r.shape[0]
+        assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
+
+
+def test_mx_attention_given_indices():
+    wl = si.build("mx_attn", [3000], [(0, 2999), (0, 2047)], seed=23, mx=True)
+    say("[attention] MX rows, oracle indices")
+    dev = Dev(wl)
+    ref = run_oracle(wl)
+    out, lse = dev.attention(torch.from_numpy(ref["indices"]).cuda())
+    assert_out_close(out.cpu().numpy(), ref["out"], False, "mx attention")
+    assert_lse_close(lse.cpu().numpy(), ref["lse"], "mx attention")
+
+
+def test_prefill_mx():
+    rng = np.random.default_rng(24)
+    pos = sorted(rng.choice(4200, size=70, replace=False).tolist())
+    wl = si.build("prefill_mx", [4200], [(0, p) for p in pos], seed=24, mx=True)
+    _check_forward(wl)
