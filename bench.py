@@ -161,7 +161,7 @@ def time_cache_append(wl, s, ev, reps: int) -> dict:
     # so each event pair brackets one kernel and not the host's call overhead
     s0, s1 = ev.create(), ev.create()
     ev.record(s0, stream)
-    torch.cuda._sleep(50_000_000)
+    torch.cuda._sleep(5_000_000)
     ev.record(s1, stream)
     t0 = time.perf_counter()
     for a, b in pairs:
