@@ -25,8 +25,12 @@
 // the tiles after those are loaded ahead of the rows that need them. Every
 // load is an unconditional buffer load (a skipped row's offset lies past the
 // end of the buffer and reads zeros), so the compiler's wait for one tile
-// never covers the loads of a later one. Two LDS regions alternate: one is
-// attended while the other is filled.
+// never covers the loads of a later one. Three LDS regions rotate, so one
+// workgroup barrier per tile suffices: before it, each wave stores its part
+// of tile i+1 and computes and posts its partial logits of tile i; after it,
+// it reads its partner's partial logits and finishes tile i (softmax and
+// value product). The region a wave stores into was last read two tiles
+// earlier, before the previous barrier.
 // fp8 rows are widened to bf16 exactly on their way into LDS; the row scale
 // multiplies the row's logit and probability. MX block-32 rows (fact sheet,
 // Training: MXFP8, one scale per 32 consecutive elements) have each 32-column
@@ -157,16 +161,13 @@ struct HalfState {
   f32x4 o[16];
 };
 
-// Attends the wave's 16 heads over one staged tile. flags[r] is the row's
-// scale (fp8), 1 (bf16), or negative for a skipped row.
-template <bool kFp8>
-__device__ __forceinline__ void attend_tile_half(const uint16_t* __restrict__ tile,
-                                                 const float* __restrict__ flags,
-                                                 float* __restrict__ xbuf, HalfState& st,
-                                                 const u32x4 (&qb)[9], float zscale, int lane,
-                                                 int wave, int half) {
+// First half of a tile for the wave's 16 heads: its partial logits^T over
+// this half's 9 k-steps (two chains per row block), posted to its slot of
+// xbuf for the partner wave and returned.
+__device__ __forceinline__ void tile_partial_logits(const uint16_t* __restrict__ tile,
+                                                    float* __restrict__ xbuf, const u32x4 (&qb)[9],
+                                                    int lane, int wave, int half, f32x4 (&part)[2]) {
   const int n16 = lane & 15, g = lane >> 4;
-  // partial logits^T over this half's 9 k-steps; two chains per row block
   f32x4 acc[2][2] = {};
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
@@ -177,14 +178,25 @@ __device__ __forceinline__ void attend_tile_half(const uint16_t* __restrict__ ti
       acc[b][s & 1] = mfma16x16x32(av, qb[s], acc[b][s & 1]);
     }
   }
-  f32x4 part0 = acc[0][0] + acc[0][1], part1 = acc[1][0] + acc[1][1];
+  part[0] = acc[0][0] + acc[0][1];
+  part[1] = acc[1][0] + acc[1][1];
   f32x4* mine = reinterpret_cast<f32x4*>(xbuf + (wave * 64 + lane) * 8);
-  mine[0] = part0;
-  mine[1] = part1;
-  __syncthreads();
-  const f32x4* other = reinterpret_cast<const f32x4*>(xbuf + ((wave ^ 4) * 64 + lane) * 8);
-  const f32x4 full[2] = {part0 + other[0], part1 + other[1]};
+  mine[0] = part[0];
+  mine[1] = part[1];
+}
 
+// Second half of a tile, after the barrier: the full logits (own partial plus
+// the partner's), the online softmax and the value product. flags[r] is the
+// row's scale (fp8), 1 (bf16, MX), or negative for a skipped row.
+template <bool kFp8>
+__device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
+                                            const float* __restrict__ flags,
+                                            const float* __restrict__ xbuf, HalfState& st,
+                                            const f32x4 (&part)[2], float zscale, int lane,
+                                            int wave, int half) {
+  const int g = lane >> 4;
+  const f32x4* other = reinterpret_cast<const f32x4*>(xbuf + ((wave ^ 4) * 64 + lane) * 8);
+  const f32x4 full[2] = {part[0] + other[0], part[1] + other[1]};
   float z[2][4], rsc[2][4];
   float tmax = -INFINITY;
 #pragma unroll
@@ -308,9 +320,9 @@ __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, in
 template <int kFmt>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   constexpr bool kRowScale = kFmt == kFmtFp8;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[2][kRegionBytes];
-  __shared__ float lds_flags[2][kAttnTileRows];
-  __shared__ __attribute__((aligned(16))) float xbuf[kAttnWaves * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[3][kRegionBytes];
+  __shared__ float lds_flags[3][kAttnTileRows];
+  __shared__ __attribute__((aligned(16))) float xbuf[2][kAttnWaves * 64 * 8];
   using Stage = RowStage<kFmt>;
   const int t = blockIdx.y, split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -354,20 +366,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   for (int db = 0; db < 16; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float zscale = a.sm_scale * kLog2e;
 
-  // tile i: store it from its stage, refill the stage with tile i+2 (indices
-  // loaded two tiles earlier) and the indices of tile i+4, then attend it
-  auto step = [&](Stage& sg, int slot, int i) {
-    sg.store(lds_tile[slot], lds_flags[slot]);
-    sg.load_rows(rows, scales, i + 2, nrows, n);
-    sg.load_idx(idx_rs, i + 4);
+  // tile 0 into region 0; its stage is refilled with tile 2
+  s0.store(lds_tile[0], lds_flags[0]);
+  s0.load_rows(rows, scales, 2, nrows, n);
+  s0.load_idx(idx_rs, 4);
+  __syncthreads();
+
+  // step i: store tile i+1 from its stage into region (i+1) % 3, refill the
+  // stage with tile i+3 (indices loaded two tiles earlier) and the indices of
+  // tile i+5, post the partial logits of tile i; barrier; finish tile i
+  int cur = 0;   // region of tile i
+  auto step = [&](Stage& sg, int i) {
+    const int nxt = cur == 2 ? 0 : cur + 1;
+    sg.store(lds_tile[nxt], lds_flags[nxt]);
+    sg.load_rows(rows, scales, i + 3, nrows, n);
+    sg.load_idx(idx_rs, i + 5);
+    const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds_tile[cur]);
+    f32x4 part[2];
+    if (i < ntiles) tile_partial_logits(tile, xbuf[i & 1], qb, lane, wave, half, part);
     __syncthreads();
     if (i < ntiles)
-      attend_tile_half<kRowScale>(reinterpret_cast<const uint16_t*>(lds_tile[slot]), lds_flags[slot],
-                             xbuf, st, qb, zscale, lane, wave, half);
+      tile_finish<kRowScale>(tile, lds_flags[cur], xbuf[i & 1], st, part, zscale, lane, wave, half);
+    cur = nxt;
   };
   for (int i = 0; i < ntiles; i += 2) {
-    step(s0, 0, i);
-    step(s1, 1, i + 1);
+    step(s1, i);
+    step(s0, i + 1);
   }
   finish_half(a, st, t, split, head, lane, half);
 }
