@@ -63,6 +63,16 @@ e = 0. Each element is x / 2^(e - 127) rounded to the nearest E4M3FN value,
 ties to the even code, saturating at 448 (a block whose maximum lies in
 (448, 512) * 2^(e - 127) has its largest elements clamped). The value of a
 stored element is its payload times its block's scale.
+
+Output epilogue (fact sheet facts: value dimension per head 128; hidden state
+7,168; the gate sits on the attention output before o_proj). In the absorbed
+form the attention output of head h stays in the 512-wide latent space; the
+value up-projection of head h (128 x 512) takes it to the head's 128 value
+columns, and the output projection (d_model x (64 * 128)) maps the 64 heads'
+values, concatenated head-major, to the hidden state:
+    u[t, h, :] = W_UV[h] @ o[t, h, :]     y[t, :] = W_O @ u[t].reshape(64 * 128)
+Weights are given as bf16 in the row-major (output x input) layout of a
+linear layer. o is the gated output, so the gate acts before o_proj.
 """
 from __future__ import annotations
 
@@ -74,9 +84,10 @@ import numpy as np
 __all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_scores",
            "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT",
            "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append", "e8m0_table", "MX_BLOCK",
-           "quantize_blocks_mxfp8", "decode_mxfp8"]
+           "quantize_blocks_mxfp8", "decode_mxfp8", "D_V", "output_projection"]
 
 D_LATENT = 512
+D_V = 128        # value dimension per head (fact sheet)
 
 
 def decode_bf16(bits: np.ndarray) -> np.ndarray:
@@ -308,3 +319,15 @@ def forward(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store: Store,
         if keep_scores:
             res["scores"].append(scores)
     return res
+
+
+def output_projection(o: np.ndarray, w_uv: np.ndarray, w_o: np.ndarray) -> np.ndarray:
+    """Gated latent outputs o [T, H, 512], value up-projections w_uv [H, 128, 512]
+    and output projection w_o [d_model, H * 128] (float64 values of the bf16
+    weights) -> hidden-state outputs [T, d_model]."""
+    o = np.asarray(o, dtype=np.float64)
+    T, H, _ = o.shape
+    u = np.empty((T, H, D_V), dtype=np.float64)
+    for h in range(H):
+        u[:, h, :] = o[:, h, :] @ np.asarray(w_uv[h], dtype=np.float64).T
+    return u.reshape(T, H * D_V) @ np.asarray(w_o, dtype=np.float64).T

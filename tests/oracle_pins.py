@@ -469,6 +469,50 @@ def check_forward_mxfp8_store(orc):
     assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
 
 
+def check_output_projection_unabsorbed(orc):
+    """The absorbed path followed by the output epilogue equals MLA computed
+    without absorbing W_UV: each head's values are the selected latent rows
+    times its up-projection, attended with the same probabilities, then the
+    heads are concatenated and projected. Also: gating before o_proj equals
+    scaling each head's values before the projection."""
+    rng = np.random.default_rng(12)
+    H, n, dm = 64, 40, 96
+    rows = rng.standard_normal((n, 576))
+    q = rng.standard_normal((H, 576))
+    g = rng.standard_normal(H) * 2
+    tau = 1 / math.sqrt(192)
+    w_uv = rng.standard_normal((H, 128, 512)) / 24
+    w_o = rng.standard_normal((dm, H * 128)) / 90
+    o, _ = orc.sparse_mla(q, rows, tau)
+    y = orc.output_projection(orc.sigmoid_gate(o, g)[None], w_uv, w_o)[0]
+    # unabsorbed: values per head, softmax written out, gate on the value vectors
+    z = tau * (q @ rows.T)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    vals = np.stack([p[h] @ (rows[:, :512] @ w_uv[h].T) for h in range(H)])     # [H, 128]
+    vals *= (1 / (1 + np.exp(-g)))[:, None]
+    ref = w_o @ vals.reshape(-1)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def check_output_projection_selection(orc):
+    """Selection weights: W_UV[h] picks latent columns 128h' .. of head h, W_O
+    picks one value column per output: the projection returns those entries."""
+    rng = np.random.default_rng(13)
+    T, H = 3, 64
+    o = rng.standard_normal((T, H, 512))
+    w_uv = np.zeros((H, 128, 512))
+    for h in range(H):
+        w_uv[h, np.arange(128), (np.arange(128) + 3 * h) % 512] = 1.0
+    pick = rng.integers(0, H * 128, size=50)
+    w_o = np.zeros((50, H * 128))
+    w_o[np.arange(50), pick] = 2.0
+    y = orc.output_projection(o, w_uv, w_o)
+    hh, vv = pick // 128, pick % 128
+    ref = 2.0 * o[:, hh, (vv + 3 * hh) % 512]
+    assert np.array_equal(y, ref)
+
+
 ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_example,
               check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
               check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
@@ -476,4 +520,5 @@ ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_exampl
               check_forward_dense_limit, check_forward_selects_by_indexer, check_forward_fp8_store,
               check_e4m3fn_encode, check_quantize_rows, check_cache_append, check_e8m0_table,
               check_mxfp8_worked_example, check_mxfp8_brute_force, check_mxfp8_scale_invariance,
-              check_forward_mxfp8_store]
+              check_forward_mxfp8_store, check_output_projection_unabsorbed,
+              check_output_projection_selection]

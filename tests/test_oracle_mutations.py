@@ -132,6 +132,22 @@ def _mx_decode_bias_128(payload, exps):
     return (vals * np.ldexp(1.0, np.asarray(exps, int) - 128)[:, :, None]).reshape(n, d)
 
 
+def _proj_transposed_uv(o, w_uv, w_o):
+    # the up-projection taken as (input x output): columns instead of rows
+    o = np.asarray(o, dtype=np.float64)
+    T, H, _ = o.shape
+    u = np.stack([o[:, h, :128] @ np.asarray(w_uv[h])[:, :128] for h in range(H)], axis=1)
+    return u.reshape(T, -1) @ np.asarray(w_o).T
+
+
+def _proj_value_major(o, w_uv, w_o):
+    # heads concatenated value-major (v * 64 + h) instead of head-major
+    o = np.asarray(o, dtype=np.float64)
+    T, H, _ = o.shape
+    u = np.stack([o[:, h, :] @ np.asarray(w_uv[h]).T for h in range(H)], axis=2)   # [T, 128, H]
+    return u.reshape(T, -1) @ np.asarray(w_o).T
+
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -149,6 +165,8 @@ MUTANTS = {
     "mx_exponent_from_ceil": dict(quantize_blocks_mxfp8=lambda x: _mx_quantize(x, ceil=True)),
     "mx_blocks_of_16": dict(quantize_blocks_mxfp8=lambda x: _mx_quantize(x, block=16)),
     "mx_decode_bias_128": dict(decode_mxfp8=_mx_decode_bias_128),
+    "proj_uv_transposed": dict(output_projection=_proj_transposed_uv),
+    "proj_heads_value_major": dict(output_projection=_proj_value_major),
 }
 
 
