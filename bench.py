@@ -177,6 +177,36 @@ def time_cache_append(wl, s, ev, reps: int) -> dict:
             "host_enqueue_ms": round(host_ms, 3)}
 
 
+def time_output_proj(wl, out, ev, reps: int) -> dict:
+    """Times sga_output_proj of the step's gated output (the output epilogue
+    after the gate), with synthetic bf16 weights for a 7,168-wide hidden state,
+    the same way as the cache append."""
+    dev = out.device
+    w_uv, w_o = si.proj_weights(seed=98)
+    w_uv, w_o = w_uv.to(dev), w_o.to(dev)
+    T, d_model = wl.num_tokens, w_o.shape[0]
+    y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
+    ws = sga.workspace(sga.sga_output_proj_workspace_size(T, d_model), dev)
+    run = lambda: sga.sga_output_proj(out, w_uv, w_o, y, ws=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    torch.cuda._sleep(5_000_000)
+    for a, b in pairs:
+        ev.record(a, stream)
+        run()
+        ev.record(b, stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    nbytes = (w_uv.numel() + w_o.numel()) * 2 + out.numel() * 4 + y.numel() * 4
+    flops = 2 * T * (64 * 128 * 512 + d_model * 64 * 128)
+    return {"us": round(us, 2), "d_model": int(d_model), "algorithmic_bytes": int(nbytes),
+            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
+
+
 # ---------------------------------------------------------------- traffic
 def src_digest() -> str:
     h = hashlib.sha256()
@@ -352,6 +382,7 @@ def main():
     wall = time.perf_counter() - t0
 
     append = time_cache_append(wl, sets[0], ev, reps=20)
+    proj = time_output_proj(wl, out, ev, reps=10)
     idx_ms = [ev.elapsed_ms(tr[i].indexer_begin, tr[i].indexer_end) for i in range(K)]
     topk_ms = [ev.elapsed_ms(tr[i].indexer_end, tr[i].topk_end) for i in range(K)]
     attn_ms = [ev.elapsed_ms(tr[i].topk_end, tr[i].attn_end) for i in range(K)]
@@ -390,7 +421,8 @@ def main():
                   "topk_us": round(float(np.mean(topk_ms)) * 1e3, 2),
                   "attention_us": round(float(np.mean(attn_ms)) * 1e3, 2),
                   "input_copies": len(sets),
-                  "cache_append": append},
+                  "cache_append": append,
+                  "output_proj": proj},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

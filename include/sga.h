@@ -64,6 +64,8 @@ extern "C" {
 #define SGA_MAX_LEN (1 << 19) /* longest visible context a query may have (512K) */
 #define SGA_MAX_K 65536     /* largest top-k */
 #define SGA_MAX_TOKENS 65535 /* most query tokens in one call */
+#define SGA_D_V 128         /* value dimension per head (output epilogue) */
+#define SGA_MAX_D_MODEL 65536 /* widest hidden state sga_output_proj takes */
 
 typedef enum sga_status {
   SGA_OK = 0,
@@ -243,6 +245,31 @@ SGA_API sga_status sga_forward(const sga_batch* batch,
 SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,
                                     void* kv, void* kv_scale, sga_dtype kv_dtype, void* k_idx,
                                     void* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream);
+
+/*
+ * sga_output_proj: the output epilogue after the gate, for T tokens.
+ * Source: the fact sheet's attention facts (value dimension per head 128;
+ * hidden state 7,168; the head-specific gate acts on the attention output
+ * before o_proj).
+ *
+ *   u[t, h, v] = sum_c w_uv[h, v, c] * o_latent[t, h, c]      (c < 512, v < 128)
+ *   y[t, n]    = sum_j w_o[n, j] * u[t, j],  j = h * 128 + v  (n < d_model)
+ *   o_latent [T,64,512] fp32: the gated output of sga_forward / sga_sparse_mla_attn.
+ *   w_uv     [64,128,512] bf16: head h's value up-projection, row-major
+ *            (output x input, the layout of a linear layer's weight).
+ *   w_o      [d_model, 8192] bf16: the output projection, row-major (output x input).
+ *   y        [T, d_model] fp32.
+ *   ws       >= sga_output_proj_workspace_size(T, d_model) bytes.
+ * d_model must be a positive multiple of 64, at most SGA_MAX_D_MODEL
+ * (SGA_ERR_UNSUPPORTED otherwise). All four arrays are 16-byte aligned.
+ * Activations enter the bf16 products as a hi/lo pair (about 16 bits) and
+ * accumulation is fp32; the sum over K is split in a fixed way and added in a
+ * fixed order, so results are deterministic.
+ */
+SGA_API size_t sga_output_proj_workspace_size(int32_t num_tokens, int32_t d_model);
+SGA_API sga_status sga_output_proj(int32_t num_tokens, const float* o_latent, const void* w_uv,
+                                   const void* w_o, int32_t d_model, float* y, void* ws,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 SGA_API const char* sga_status_string(sga_status status);

@@ -224,6 +224,20 @@ def append_rows(num_tokens: int, seed: int, *, kv_sigma: float = 1.0 / 24.0, key
     return _bf16(lat), _bf16(key)
 
 
+D_V = 128             # value dimension per head (fact sheet)
+D_MODEL = 7168        # hidden state (fact sheet)
+
+
+def proj_weights(seed: int, d_model: int = D_MODEL):
+    """Synthetic output-epilogue weights in bf16: the value up-projections
+    w_uv [64, 128, 512] ~ N(0, 1/512) and the output projection
+    w_o [d_model, 64 * 128] ~ N(0, 1/8192), in that draw order."""
+    rng = np.random.default_rng(seed)
+    w_uv = rng.standard_normal((N_HEADS, D_V, D_LATENT), dtype=np.float32) / np.float32(math.sqrt(D_LATENT))
+    w_o = rng.standard_normal((d_model, N_HEADS * D_V), dtype=np.float32) / np.float32(math.sqrt(N_HEADS * D_V))
+    return _bf16(w_uv), _bf16(w_o)
+
+
 def config(i: int, seed: Optional[int] = None) -> Workload:
     """The five workloads, and a sixth: the 256K decode with MX block-32 caches.
     The seed defaults to the workload's number."""

@@ -20,11 +20,12 @@ LIB_PATH = os.path.join(_PKG, "libsga.so")
 SGA_OK, SGA_ERR_INVALID_ARG, SGA_ERR_UNSUPPORTED, SGA_ERR_WORKSPACE, SGA_ERR_HIP = range(5)
 SGA_BF16, SGA_FP8_E4M3, SGA_MXFP8_E4M3 = 0, 1, 2
 MX_BLOCK = 32
-HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK = 64, 64, 128, 512, 576
+HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK, D_V = 64, 64, 128, 512, 576, 128
 
 EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_workspace_size",
            "sga_sparse_mla_attn", "sga_forward_workspace_size", "sga_forward",
-           "sga_cache_append", "sga_status_string", "sga_version")
+           "sga_cache_append", "sga_output_proj_workspace_size", "sga_output_proj",
+           "sga_status_string", "sga_version")
 
 
 class SgaBatch(ctypes.Structure):
@@ -73,6 +74,8 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "sga_forward": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, f32, vp, vp,
                          vp, vp, vp, sz, tp, vp], ctypes.c_int),
         "sga_cache_append": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp], ctypes.c_int),
+        "sga_output_proj_workspace_size": ([i32, i32], sz),
+        "sga_output_proj": ([i32, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int),
         "sga_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sga_version": ([], ctypes.c_int),
     }
@@ -277,3 +280,24 @@ def sga_cache_append(batch: Batch, latent=None, idx_key=None, kv=None, kv_scale=
     _raise("sga_cache_append", load().sga_cache_append(
         ctypes.byref(b), _ptr(latent), _ptr(idx_key), _ptr(kv), _ptr(kv_scale), vdt, _ptr(k_idx),
         _ptr(k_idx_scale), kdt, _stream(ref)))
+
+
+def sga_output_proj_workspace_size(num_tokens: int, d_model: int) -> int:
+    return int(load().sga_output_proj_workspace_size(num_tokens, d_model))
+
+
+def sga_output_proj(o_latent, w_uv, w_o, y, ws: Optional[torch.Tensor] = None) -> None:
+    """y[t] = w_o @ concat_h(w_uv[h] @ o_latent[t, h]): the value up-projection of
+    each head and the output projection, after the gate."""
+    _check(o_latent, "o_latent", (torch.float32,))
+    T = int(o_latent.shape[0])
+    _check(o_latent, "o_latent", (torch.float32,), (T, HEADS, D_LATENT))
+    _check(w_uv, "w_uv", (torch.bfloat16,), (HEADS, D_V, D_LATENT))
+    _check(w_o, "w_o", (torch.bfloat16,), (None, HEADS * D_V))
+    d_model = int(w_o.shape[0])
+    _check(y, "y", (torch.float32,), (T, d_model))
+    if ws is None:
+        ws = workspace(sga_output_proj_workspace_size(T, d_model), o_latent.device)
+    _raise("sga_output_proj", load().sga_output_proj(
+        T, _ptr(o_latent), _ptr(w_uv), _ptr(w_o), d_model, _ptr(y), _ptr(ws), ws.numel(),
+        _stream(o_latent)))

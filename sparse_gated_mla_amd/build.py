@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsga.so")
-SOURCES = ["sga_api.hip", "indexer.hip", "topk.hip", "attention.hip", "cache.hip"]
+SOURCES = ["sga_api.hip", "indexer.hip", "topk.hip", "attention.hip", "cache.hip", "proj.hip"]
 ARCH = "gfx950"
 
 

@@ -12,6 +12,7 @@ namespace {
 using sga::AttnArgs;
 using sga::BatchView;
 using sga::CacheArgs;
+using sga::ProjArgs;
 using sga::IndexerArgs;
 using sga::TopkArgs;
 using sga::TopkCtrl;
@@ -220,6 +221,41 @@ sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* 
   return SGA_OK;
 }
 
+// ---------------------------------------------------------------- output epilogue
+// Splits of K: the largest divisor of the chunk count that keeps the grid
+// within about four workgroups per CU.
+int proj_splits(int64_t tiles, int chunks) {
+  int best = 1;
+  for (int s = 1; s <= chunks; ++s)
+    if (chunks % s == 0 && tiles * s <= 1024) best = s;
+  return best;
+}
+
+struct ProjPlan {
+  int uv_splits, o_splits;
+  size_t u_floats, part_floats;
+};
+
+ProjPlan plan_proj(int32_t T, int32_t d_model) {
+  const int64_t mt = (T + sga::kProjRows - 1) / sga::kProjRows;
+  ProjPlan p;
+  p.uv_splits = proj_splits(mt * (sga::kDV / sga::kProjCols) * sga::kHeads, sga::kDLatent / sga::kProjChunk);
+  p.o_splits = proj_splits(mt * (d_model / sga::kProjCols), sga::kHeads * sga::kDV / sga::kProjChunk);
+  p.u_floats = (size_t)T * sga::kHeads * sga::kDV;
+  const size_t uv_part = p.uv_splits > 1 ? (size_t)p.uv_splits * T * sga::kHeads * sga::kDV : 0;
+  const size_t o_part = p.o_splits > 1 ? (size_t)p.o_splits * T * d_model : 0;
+  p.part_floats = uv_part > o_part ? uv_part : o_part;
+  return p;
+}
+
+size_t proj_ws(int32_t T, int32_t d_model) {
+  const ProjPlan p = plan_proj(T, d_model);
+  Carver c(nullptr);
+  c.take<float>(p.u_floats);
+  if (p.part_floats) c.take<float>(p.part_floats);
+  return c.used;
+}
+
 size_t topk_ws(int32_t T, int32_t max_len) {
   Carver c(nullptr);
   carve_topk(c, T, max_len);
@@ -415,6 +451,67 @@ SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, 
   a.k_idx_scale = do_key ? k_idx_scale : nullptr;
   a.k_idx_fmt = do_key ? (int)k_idx_dtype : sga::kFmtBf16;
   return hip_status(sga::launch_cache_append(a, stream));
+}
+
+SGA_API size_t sga_output_proj_workspace_size(int32_t num_tokens, int32_t d_model) {
+  if (num_tokens <= 0 || d_model <= 0 || d_model % sga::kProjCols != 0 || d_model > SGA_MAX_D_MODEL) return 0;
+  return proj_ws(num_tokens, d_model);
+}
+
+SGA_API sga_status sga_output_proj(int32_t num_tokens, const float* o_latent, const void* w_uv,
+                                   const void* w_o, int32_t d_model, float* y, void* ws,
+                                   size_t ws_bytes, hipStream_t stream) {
+  if (num_tokens < 0 || d_model <= 0) return SGA_ERR_INVALID_ARG;
+  if (num_tokens > SGA_MAX_TOKENS || d_model % sga::kProjCols != 0 || d_model > SGA_MAX_D_MODEL)
+    return SGA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return SGA_OK;
+  if (!o_latent || !w_uv || !w_o || !y) return SGA_ERR_INVALID_ARG;
+  if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(w_o) || !aligned16(y))
+    return SGA_ERR_INVALID_ARG;
+  const size_t need = proj_ws(num_tokens, d_model);
+  if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
+  const ProjPlan plan = plan_proj(num_tokens, d_model);
+  Carver c(ws);
+  float* u = c.take<float>(plan.u_floats);
+  float* part = plan.part_floats ? c.take<float>(plan.part_floats) : nullptr;
+  const int T = num_tokens, HV = sga::kHeads * sga::kDV;
+  // u[t, h, v] = sum_k o[t, h, k] * w_uv[h, v, k]: one product per head
+  ProjArgs uv;
+  uv.a = o_latent;
+  uv.lda = (int64_t)sga::kHeads * sga::kDLatent;
+  uv.a_batch = sga::kDLatent;
+  uv.b = static_cast<const uint16_t*>(w_uv);
+  uv.ldb = sga::kDLatent;
+  uv.b_batch = (int64_t)sga::kDV * sga::kDLatent;
+  uv.c = u;
+  uv.ldc = HV;
+  uv.c_batch = sga::kDV;
+  uv.part = part;
+  uv.M = T;
+  uv.N = sga::kDV;
+  uv.K = sga::kDLatent;
+  uv.batch = sga::kHeads;
+  uv.splits = plan.uv_splits;
+  SGA_HIP(sga::launch_proj(uv, stream));
+  // y[t, n] = sum_j u[t, j] * w_o[n, j]
+  ProjArgs op;
+  op.a = u;
+  op.lda = HV;
+  op.a_batch = 0;
+  op.b = static_cast<const uint16_t*>(w_o);
+  op.ldb = HV;
+  op.b_batch = 0;
+  op.c = y;
+  op.ldc = d_model;
+  op.c_batch = 0;
+  op.part = part;
+  op.M = T;
+  op.N = d_model;
+  op.K = HV;
+  op.batch = 1;
+  op.splits = plan.o_splits;
+  SGA_HIP(sga::launch_proj(op, stream));
+  return SGA_OK;
 }
 
 }  // extern "C"

@@ -98,7 +98,26 @@ struct CacheArgs {
   int k_idx_fmt;
 };
 
+// Output epilogue: C = A . B^T per batch entry, A fp32 [M x K] (row stride
+// lda, batch stride a_batch), B bf16 [N x K] (ldb, b_batch), C fp32 [M x N]
+// (ldc, c_batch). K a multiple of kProjChunk * splits, N of kProjCols.
+constexpr int kDV = 128;              // value dimension per head
+constexpr int kProjRows = 16;         // rows of A per workgroup
+constexpr int kProjCols = 64;         // columns of C per workgroup
+constexpr int kProjChunk = 256;       // K per staged chunk
+struct ProjArgs {
+  const float* a;
+  int64_t lda, a_batch;
+  const uint16_t* b;
+  int64_t ldb, b_batch;
+  float* c;
+  int64_t ldc, c_batch;
+  float* part;             // [splits][batch][M][N] partial sums when splits > 1
+  int M, N, K, batch, splits;
+};
+
 hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
+hipError_t launch_proj(const ProjArgs& a, hipStream_t s);
 hipError_t launch_cache_append(const CacheArgs& a, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s);
 // Eight tokens per workgroup sharing each key tile: for batches with many

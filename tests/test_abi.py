@@ -27,7 +27,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("sga_index_scores", "sga_topk", "sga_sparse_mla_attn", "sga_forward", "sga_cache_append"):
+    for n in ("sga_index_scores", "sga_topk", "sga_sparse_mla_attn", "sga_forward", "sga_cache_append",
+              "sga_output_proj"):
         assert n in names
 
 
@@ -155,6 +156,30 @@ def test_cache_append_rejects_bad_arguments(lib):
     assert call(_batch(T=0, ptr=0), lat=None, kv=None, key=None, kidx=None) == 0
     assert call(_batch(T=0, ptr=0)) == 0       # empty batch: nothing launched
     assert call(lat=None, kv=None, key=None, kidx=None) == 0   # nothing to write
+
+
+def test_output_proj_rejects_bad_arguments(lib):
+    need = lib.sga_output_proj_workspace_size(2, 256)
+    assert need > 0
+
+    def call(T=2, o=FAKE, uv=FAKE, wo=FAKE, dm=256, y=FAKE, ws=FAKE, nb=need):
+        return lib.sga_output_proj(T, o, uv, wo, dm, y, ws, nb, None)
+    assert call(T=-1) == 1
+    assert call(dm=0) == 1
+    assert call(dm=100) == 2                   # not a multiple of 64
+    assert call(dm=(1 << 16) + 64) == 2
+    assert call(T=65536) == 2
+    assert call(o=None) == 1
+    assert call(uv=None) == 1
+    assert call(wo=None) == 1
+    assert call(y=None) == 1
+    assert call(o=FAKE_ODD) == 1
+    assert call(wo=FAKE_ODD) == 1
+    assert call(ws=None) == 3
+    assert call(nb=need - 1) == 3
+    assert call(T=0, o=None, uv=None, wo=None, y=None, ws=None, nb=0) == 0
+    assert lib.sga_output_proj_workspace_size(16, 7168) >= 16 * 8192 * 4
+    assert lib.sga_output_proj_workspace_size(0, 7168) == 0
 
 
 def test_workspace_sizes_grow_with_the_problem(lib):
