@@ -7,15 +7,17 @@
 // Both steps are C = A . B^T with A fp32 activations [M x K] and B bf16
 // weights [N x K] (the row-major weight of a linear layer): the up-projection
 // is 64 such products, one per head, through strides; the output projection is
-// one. Mapping onto gfx950: a workgroup of 4 waves takes 16 rows of A and 64
-// columns of C, 16 per wave, over one split of K. For each 256-wide chunk of K
-// the workgroup stages A's 16 x 256 block in LDS as a bf16 hi/lo pair
-// (a = hi + lo to about 16 bits), and each wave streams its 16 weight rows
-// from memory straight into v_mfma_f32_16x16x32_bf16 B operands, two MFMAs per
-// k-step (hi and lo). The k order inside a chunk is permuted the same way on
-// both sides so that two consecutive k-steps of a lane read 32 contiguous
-// bytes of its weight row: each pair of load instructions covers whole 128-byte
-// lines. With several splits of K the partial sums go to a workspace and
+// one. Mapping onto gfx950: a workgroup of 4 waves takes 16 * MB rows of A
+// (MB = 1 for a few tokens, 4 from 32 tokens on) and 64 * NB columns of C
+// (NB = 2 from 32 tokens on), 16 * NB per wave, over one split of K. For each chunk of K (256 wide, 128 when MB = 4)
+// the workgroup stages A's block in LDS as a bf16 hi/lo pair (a = hi + lo to
+// about 16 bits), and each wave streams its 16 weight rows from memory
+// straight into v_mfma_f32_16x16x32_bf16 B operands; each B operand serves
+// MB row blocks, two MFMAs each (hi and lo), so the weights are read once per
+// 16 * MB rows. The k order inside a chunk is permuted the same way on both
+// sides so that two consecutive k-steps of a lane read 32 contiguous bytes of
+// its weight row: each pair of load instructions covers whole 128-byte lines.
+// With several splits of K the partial sums go to a workspace and
 // proj_reduce_kernel adds them in split order, so results do not depend on
 // scheduling.
 #include "sga_kernels.h"
@@ -24,69 +26,90 @@ namespace sga {
 namespace {
 
 constexpr int kProjThreads = 256;
-constexpr int kProjStride = kProjChunk + 8;   // bf16 per LDS row (16-byte pad)
 
 // k offset, inside a chunk, of the 8 elements lane group g holds at k-step s
 __device__ __forceinline__ int proj_k(int s, int g) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); }
 
+template <int MB, int NB>
 __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kProjRows][kProjStride];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kProjRows][kProjStride];
+  constexpr int kChunk = proj_chunk(MB);
+  constexpr int kSteps = kChunk / 32;
+  constexpr int kRows = kProjRows * MB;
+  constexpr int kStride = kChunk + 8;                  // bf16 per LDS row (16-byte pad)
+  constexpr int kPerThread = kRows * kChunk / kProjThreads;   // A floats each thread stages: 16 or 32
+  constexpr int kThreadsPerRow = kChunk / kPerThread;
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[2][kRows][kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[2][kRows][kStride];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n16 = lane & 15, g = lane >> 4;
   const int bz = blockIdx.z;
   const int batch = bz / a.splits, split = bz % a.splits;
-  const int m0 = blockIdx.y * kProjRows;
-  const int n = blockIdx.x * kProjCols + 16 * wave + n16;   // this lane's weight row
-  const int chunks = a.K / kProjChunk / a.splits;
-  const int k_begin = split * chunks * kProjChunk;
+  const int m0 = blockIdx.y * kRows;
+  // this lane's weight row in column block 0; block j adds 64 * j
+  const int n = blockIdx.x * (kProjCols * NB) + 16 * wave + n16;
+  const int chunks = a.K / kChunk / a.splits;
+  const int k_begin = split * chunks * kChunk;
   const float* A = a.a + (int64_t)batch * a.a_batch;
   const uint16_t* B = a.b + (int64_t)batch * a.b_batch + (int64_t)n * a.ldb + k_begin;
+  const int64_t b_next = (int64_t)kProjCols * a.ldb;         // to column block j + 1
 
-  // A staging: thread x loads row x/16 of the block, k = 16*(x%16) .. +15
-  const int am = threadIdx.x >> 4, ak = 16 * (threadIdx.x & 15);
+  // A staging: thread x loads row x / kThreadsPerRow of the block and
+  // kPerThread consecutive k from kPerThread * (x % kThreadsPerRow)
+  const int am = threadIdx.x / kThreadsPerRow, ak = kPerThread * (threadIdx.x % kThreadsPerRow);
   const bool arow = m0 + am < a.M;
   const float* Ap = A + (int64_t)(arow ? m0 + am : 0) * a.lda + k_begin + ak;
-  f32x4 av[4];
+  f32x4 av[kPerThread / 4];
   auto load_a = [&](int c) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      av[j] = arow ? *reinterpret_cast<const f32x4*>(Ap + c * kProjChunk + 4 * j) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kPerThread / 4; ++j)
+      av[j] = arow ? *reinterpret_cast<const f32x4*>(Ap + c * kChunk + 4 * j) : f32x4{0.f, 0.f, 0.f, 0.f};
   };
   auto store_a = [&](int buf) {
-    uint32_t hi[8], lo[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float x0 = av[j >> 1][2 * (j & 1)], x1 = av[j >> 1][2 * (j & 1) + 1];
-      const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-      hi[j] = h0 | (h1 << 16);
-      lo[j] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
-              (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+    for (int q = 0; q < kPerThread / 8; ++q) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x0 = av[2 * q + (j >> 1)][2 * (j & 1)], x1 = av[2 * q + (j >> 1)][2 * (j & 1) + 1];
+        const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+        hi[j] = h0 | (h1 << 16);
+        lo[j] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
+                (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+      }
+      *reinterpret_cast<u32x4*>(&lds_hi[buf][am][ak + 8 * q]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(&lds_lo[buf][am][ak + 8 * q]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }
-    u32x4* ph = reinterpret_cast<u32x4*>(&lds_hi[buf][am][ak]);
-    u32x4* pl = reinterpret_cast<u32x4*>(&lds_lo[buf][am][ak]);
-    ph[0] = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    ph[1] = u32x4{hi[4], hi[5], hi[6], hi[7]};
-    pl[0] = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    pl[1] = u32x4{lo[4], lo[5], lo[6], lo[7]};
   };
-  // this lane's B operands of one chunk (8 k-steps)
-  u32x4 bq[2][8];
-  auto load_b = [&](u32x4 (&dst)[8], int c) {
-    const uint16_t* p = B + c * kProjChunk;
+  // this lane's B operands of one chunk, per column block
+  u32x4 bq[2][NB][kSteps];
+  auto load_b = [&](u32x4 (&dst)[NB][kSteps], int c) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = *reinterpret_cast<const u32x4*>(p + proj_k(s, g));
+    for (int j = 0; j < NB; ++j) {
+      const uint16_t* p = B + j * b_next + c * kChunk;
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) dst[j][s] = *reinterpret_cast<const u32x4*>(p + proj_k(s, g));
+    }
   };
 
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const u32x4 (&bs)[8], int buf) {
+  f32x4 acc[MB][NB];
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) acc[mb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const u32x4 (&bs)[NB][kSteps], int buf) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
       const int k = proj_k(s, g);
-      const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds_hi[buf][n16][k]);
-      const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds_lo[buf][n16][k]);
-      acc = mfma16x16x32(ahi, bs[s], acc);
-      acc = mfma16x16x32(alo, bs[s], acc);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds_hi[buf][16 * mb + n16][k]);
+        const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds_lo[buf][16 * mb + n16][k]);
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          acc[mb][j] = mfma16x16x32(ahi, bs[j][s], acc[mb][j]);
+          acc[mb][j] = mfma16x16x32(alo, bs[j][s], acc[mb][j]);
+        }
+      }
     }
   };
 
@@ -114,18 +137,22 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs a) {
     }
   }
 
-  // acc[r] = C[m0 + 4g + r][column n of this lane's 16]
-  const int col = blockIdx.x * kProjCols + 16 * wave + n16;
+  // acc[mb][j][r] = C[m0 + 16 mb + 4g + r][n + 64 j]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int m = m0 + 4 * g + r;
-    if (m < a.M) {
-      if (a.splits == 1)
-        a.c[(int64_t)batch * a.c_batch + (int64_t)m * a.ldc + col] = acc[r];
-      else
-        a.part[(((int64_t)split * a.batch + batch) * a.M + m) * a.N + col] = acc[r];
-    }
-  }
+  for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * mb + 4 * g + r;
+        const int col = n + kProjCols * j;
+        if (m < a.M) {
+          if (a.splits == 1)
+            a.c[(int64_t)batch * a.c_batch + (int64_t)m * a.ldc + col] = acc[mb][j][r];
+          else
+            a.part[(((int64_t)split * a.batch + batch) * a.M + m) * a.N + col] = acc[mb][j][r];
+        }
+      }
 }
 
 // C[b][m][n] = sum over splits s, in order, of part[s][b][m][n].
@@ -146,8 +173,15 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
 
 hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  const dim3 grid(a.N / kProjCols, (a.M + kProjRows - 1) / kProjRows, a.batch * a.splits);
-  proj_kernel<<<grid, kProjThreads, 0, s>>>(a);
+  const int mb = proj_row_blocks(a.M), nb = proj_col_blocks(a.M, a.N);
+  const dim3 grid(a.N / (kProjCols * nb), (a.M + kProjRows * mb - 1) / (kProjRows * mb), a.batch * a.splits);
+  if (mb == 4) {
+    if (nb == 2) proj_kernel<4, 2><<<grid, kProjThreads, 0, s>>>(a);
+    else proj_kernel<4, 1><<<grid, kProjThreads, 0, s>>>(a);
+  } else {
+    if (nb == 2) proj_kernel<1, 2><<<grid, kProjThreads, 0, s>>>(a);
+    else proj_kernel<1, 1><<<grid, kProjThreads, 0, s>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
   const int64_t per = (int64_t)a.batch * a.M * a.N;

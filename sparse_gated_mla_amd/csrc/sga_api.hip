@@ -237,10 +237,14 @@ struct ProjPlan {
 };
 
 ProjPlan plan_proj(int32_t T, int32_t d_model) {
-  const int64_t mt = (T + sga::kProjRows - 1) / sga::kProjRows;
+  const int mb = sga::proj_row_blocks(T);
+  const int64_t mt = (T + sga::kProjRows * mb - 1) / (sga::kProjRows * mb);
+  const int chunk = sga::proj_chunk(mb);
   ProjPlan p;
-  p.uv_splits = proj_splits(mt * (sga::kDV / sga::kProjCols) * sga::kHeads, sga::kDLatent / sga::kProjChunk);
-  p.o_splits = proj_splits(mt * (d_model / sga::kProjCols), sga::kHeads * sga::kDV / sga::kProjChunk);
+  // the up-projection is 64 products with K = 512: never split (no second pass)
+  p.uv_splits = 1;
+  const int nb = sga::proj_col_blocks(T, d_model);
+  p.o_splits = proj_splits(mt * (d_model / (sga::kProjCols * nb)), sga::kHeads * sga::kDV / chunk);
   p.u_floats = (size_t)T * sga::kHeads * sga::kDV;
   const size_t uv_part = p.uv_splits > 1 ? (size_t)p.uv_splits * T * sga::kHeads * sga::kDV : 0;
   const size_t o_part = p.o_splits > 1 ? (size_t)p.o_splits * T * d_model : 0;

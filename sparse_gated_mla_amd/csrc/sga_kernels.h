@@ -100,11 +100,19 @@ struct CacheArgs {
 
 // Output epilogue: C = A . B^T per batch entry, A fp32 [M x K] (row stride
 // lda, batch stride a_batch), B bf16 [N x K] (ldb, b_batch), C fp32 [M x N]
-// (ldc, c_batch). K a multiple of kProjChunk * splits, N of kProjCols.
+// (ldc, c_batch). K a multiple of proj_chunk() * splits, N of kProjCols.
 constexpr int kDV = 128;              // value dimension per head
-constexpr int kProjRows = 16;         // rows of A per workgroup
+constexpr int kProjRows = 16;         // rows of A per MFMA row block
 constexpr int kProjCols = 64;         // columns of C per workgroup
-constexpr int kProjChunk = 256;       // K per staged chunk
+// row blocks per workgroup: 4 (64 rows, weights read once per 64 rows) from
+// 32 rows on, else 1; K per staged chunk: 256 with one row block, 128 with four
+__host__ __device__ constexpr int proj_row_blocks(int M) { return M >= 32 ? 4 : 1; }
+__host__ __device__ constexpr int proj_chunk(int mb) { return mb == 4 ? 128 : 256; }
+// column blocks of 64 per workgroup: 2 from 32 rows on, when N allows it (each
+// A element read from LDS then serves two weight rows; measured slower below)
+__host__ __device__ constexpr int proj_col_blocks(int M, int N) {
+  return (M >= 32 && N % (2 * kProjCols) == 0) ? 2 : 1;
+}
 struct ProjArgs {
   const float* a;
   int64_t lda, a_batch;
