@@ -64,6 +64,14 @@ ties to the even code, saturating at 448 (a block whose maximum lies in
 (448, 512) * 2^(e - 127) has its largest elements clamped). The value of a
 stored element is its payload times its block's scale.
 
+MX block-32 with 4-bit elements (the FP4 member of the same family; the pages
+cite 4-bit serving): OCP E2M1 elements (1 sign bit, 2 exponent bits with bias
+1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with the
+lower-indexed element in the low nibble, and one E8M0 exponent per 32
+elements with e - 127 = floor(log2(max|x|)) - 2 (2 = exponent of E2M1's
+largest value, 6 = 1.5 * 2^2), clamped and zero-block handled as above;
+elements nearest-even, saturating at 6.
+
 Output epilogue (fact sheet facts: value dimension per head 128; hidden state
 7,168; the gate sits on the attention output before o_proj). In the absorbed
 form the attention output of head h stays in the 512-wide latent space; the
@@ -84,7 +92,8 @@ import numpy as np
 __all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_scores",
            "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT",
            "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append", "e8m0_table", "MX_BLOCK",
-           "quantize_blocks_mxfp8", "decode_mxfp8", "D_V", "output_projection"]
+           "quantize_blocks_mxfp8", "decode_mxfp8", "D_V", "output_projection",
+           "e2m1_table", "encode_e2m1", "quantize_blocks_mxfp4", "decode_mxfp4"]
 
 D_LATENT = 512
 D_V = 128        # value dimension per head (fact sheet)
@@ -176,6 +185,60 @@ def quantize_blocks_mxfp8(x: np.ndarray):
     return payload, exps
 
 
+def e2m1_table() -> np.ndarray:
+    """The 16 values of OCP E2M1, built from the format's field definition."""
+    t = np.empty(16, dtype=np.float64)
+    for c in range(16):
+        e, m = (c >> 1) & 3, c & 1
+        v = m * 0.5 if e == 0 else (1.0 + m / 2.0) * 2.0 ** (e - 1)
+        t[c] = -v if c & 8 else v
+    return t
+
+
+_E2M1 = e2m1_table()
+
+
+def encode_e2m1(x: np.ndarray) -> np.ndarray:
+    """Each value to the nearest E2M1 code (uint8 0..15), ties to the even code,
+    |x| > 6 saturating to 6; the sign bit follows the sign of x."""
+    x = np.asarray(x, dtype=np.float64)
+    mags = _E2M1[:8]
+    a = np.minimum(np.abs(x), mags[-1])
+    d = np.abs(a[..., None] - mags)                    # distance to each magnitude code
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    # ties: the even code (of two equidistant codes exactly one is even)
+    even = cand & (np.arange(8) % 2 == 0)
+    code = np.where(cand.sum(axis=-1) > 1, np.argmax(even, axis=-1), np.argmax(cand, axis=-1))
+    return (code | np.where(np.signbit(x), 8, 0)).astype(np.uint8)
+
+
+def quantize_blocks_mxfp4(x: np.ndarray):
+    """Rows [n, D] (D a multiple of 32) -> (uint8 packed E2M1 payloads [n, D/2],
+    element 2i in the low nibble of byte i; uint8 E8M0 exponents [n, D/32])."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    blocks = x.reshape(n, d // MX_BLOCK, MX_BLOCK)
+    amax = np.max(np.abs(blocks), axis=2)
+    exps = np.zeros(amax.shape, dtype=np.uint8)
+    nz = amax > 0
+    _, e2 = np.frexp(amax[nz])
+    exps[nz] = np.clip(e2 - 1 - 2, -127, 127) + 127   # floor(log2 amax) - 2, biased
+    codes = encode_e2m1(blocks / _E8M0[exps][:, :, None]).reshape(n, d)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), exps
+
+
+def decode_mxfp4(payload: np.ndarray, exps: np.ndarray) -> np.ndarray:
+    """uint8 packed payload rows [n, D/2] and E8M0 exponents [n, D/32] -> float64 [n, D]."""
+    p = np.asarray(payload, dtype=np.uint8)
+    n, half = p.shape
+    codes = np.empty((n, 2 * half), dtype=np.uint8)
+    codes[:, 0::2] = p & 0xF
+    codes[:, 1::2] = p >> 4
+    vals = _E2M1[codes].reshape(n, 2 * half // MX_BLOCK, MX_BLOCK)
+    return (vals * _E8M0[np.asarray(exps, dtype=np.uint8)][:, :, None]).reshape(n, 2 * half)
+
+
 def decode_mxfp8(payload: np.ndarray, exps: np.ndarray) -> np.ndarray:
     """uint8 payload rows [n, D] and E8M0 block exponents [n, D/32] -> float64 [n, D]."""
     p = np.asarray(payload, dtype=np.uint8)
@@ -188,8 +251,9 @@ def cache_append(token_seq, token_pos, seq_start, seq_len, cache_rows: int, rows
                  fmt: str):
     """The rows the append writes: {cache row: (payload row, scale or None)}.
     rows: [T, D] bf16 bit patterns (uint16). fmt: "bf16" (copied bits),
-    "e4m3fn" (quantised per row; the scale is a float32) or "mxfp8" (quantised
-    per 32-element block; the scale is the row's uint8 E8M0 exponents). A token
+    "e4m3fn" (quantised per row; the scale is a float32), "mxfp8" or "mxfp4"
+    (quantised per 32-element block; the scale is the row's uint8 E8M0
+    exponents, the mxfp4 payload two elements per byte). A token
     whose position lies outside its sequence's rows, or whose row lies outside
     the cache, writes nothing."""
     out = {}
@@ -206,6 +270,9 @@ def cache_append(token_seq, token_pos, seq_start, seq_len, cache_rows: int, rows
         elif fmt == "mxfp8":
             pay, ex = quantize_blocks_mxfp8(vals[t:t + 1])
             out[r] = (pay[0], ex[0])
+        elif fmt == "mxfp4":
+            pay, ex = quantize_blocks_mxfp4(vals[t:t + 1])
+            out[r] = (pay[0], ex[0])
         else:
             pay, sc = quantize_rows_e4m3fn(vals[t:t + 1])
             out[r] = (pay[0], np.float32(sc[0]))
@@ -220,10 +287,11 @@ def decode_e4m3fn(payload: np.ndarray, scale: np.ndarray) -> np.ndarray:
 
 @dataclass
 class Store:
-    """A flat cache: raw bits per row plus the format ('bf16', 'e4m3fn' or 'mxfp8')."""
-    bits: np.ndarray                  # uint16 [rows, D] (bf16) or uint8 [rows, D] (e4m3fn, mxfp8)
+    """A flat cache: raw bits per row plus the format ('bf16', 'e4m3fn', 'mxfp8' or 'mxfp4')."""
+    bits: np.ndarray                  # uint16 [rows, D] (bf16), uint8 [rows, D] (e4m3fn, mxfp8)
+                                      # or uint8 [rows, D/2] (mxfp4, two elements per byte)
     fmt: str
-    scale: Optional[np.ndarray] = None  # float32 [rows] (e4m3fn) or uint8 [rows, D/32] (mxfp8)
+    scale: Optional[np.ndarray] = None  # float32 [rows] (e4m3fn) or uint8 [rows, D/32] (mx)
 
     def rows(self, idx) -> np.ndarray:
         if self.fmt == "bf16":
@@ -232,6 +300,8 @@ class Store:
             return decode_e4m3fn(self.bits[idx], self.scale[idx])
         if self.fmt == "mxfp8":
             return decode_mxfp8(self.bits[idx], self.scale[idx])
+        if self.fmt == "mxfp4":
+            return decode_mxfp4(self.bits[idx], self.scale[idx])
         raise ValueError(self.fmt)
 
 

@@ -103,6 +103,9 @@ def check_cache_append(orc):
     assert sorted(q) == [4, 12]
     assert np.allclose(orc.decode_e4m3fn(q[4][0][None], np.array([q[4][1]]))[0],
                        orc.decode_bf16(rows[0]), rtol=1 / 16, atol=0)
+    f4 = orc.cache_append(token_seq, token_pos, seq_start, seq_len, 13,
+                          np.tile(rows, (1, 4)), "mxfp4")
+    assert sorted(f4) == [4, 12] and f4[4][0].shape == (16,) and f4[4][1].shape == (1,)
     m = orc.cache_append(token_seq, token_pos, seq_start, seq_len, 13,
                          np.tile(rows, (1, 4)), "mxfp8")
     assert sorted(m) == [4, 12] and m[4][1].shape == (1,)
@@ -179,6 +182,103 @@ def check_mxfp8_scale_invariance(orc):
         assert np.array_equal(p0, p1) and np.array_equal(e1.astype(int), e0.astype(int) + k)
     dec = orc.decode_mxfp8(p0, e0)
     assert np.allclose(dec, x, rtol=1 / 16, atol=0)
+
+
+def check_e2m1_table(orc):
+    # the format's value list (OCP E2M1): 0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    t = orc.e2m1_table()
+    assert t[:8].tolist() == mags and t[8:].tolist() == [-m for m in mags]
+    assert np.signbit(t[8])
+
+
+def check_mxfp4_worked_example(orc):
+    g = _golden("mxfp4_worked_example.json")
+    x = np.zeros((1, 32))
+    for i, v in g["values"].items():
+        x[0, int(i)] = v
+    pay, ex = orc.quantize_blocks_mxfp4(x)
+    assert ex.tolist() == [[g["exp"]]], ex
+    for i, b in g["bytes"].items():
+        assert int(pay[0, int(i)]) == b, (i, int(pay[0, int(i)]), b)
+    assert not pay[0, 4:].any()
+
+
+def check_mxfp4_brute_force(orc):
+    # every element is the nearest of the 16 E2M1 values times its block's scale
+    # (ties to the even code, beyond 6 the largest); exponent found by search
+    rng = np.random.default_rng(5)
+    x = rng.normal(size=(5, 96)) * np.ldexp(1.0, rng.integers(-15, 15, size=(5, 1)))
+    x[1, 32:64] = 0.0
+    x[2, :32] = 0.0
+    x[2, 0] = 4.0                                     # scale 1: ties among the codes
+    x[2, 1:9] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.75]
+    pay, ex = orc.quantize_blocks_mxfp4(x)
+    codes = np.empty(x.shape, dtype=np.uint8)
+    codes[:, 0::2], codes[:, 1::2] = pay & 0xF, pay >> 4
+    table = orc.e2m1_table()
+    for r in range(x.shape[0]):
+        for b in range(3):
+            blk = x[r, 32 * b:32 * b + 32]
+            amax = np.abs(blk).max()
+            if amax == 0:
+                assert ex[r, b] == 0 and not codes[r, 32 * b:32 * b + 32].any()
+                continue
+            e = 0
+            while 2.0 ** (e + 1) <= amax:
+                e += 1
+            while 2.0 ** e > amax:
+                e -= 1
+            assert int(ex[r, b]) == e - 2 + 127, (r, b)
+            sc = 2.0 ** (e - 2)
+            for j, v in enumerate(blk):
+                a = min(abs(v) / sc, 6.0)
+                d = np.abs(table[:8] - a)
+                best = np.flatnonzero(d == d.min())
+                want = best[best % 2 == 0][0] if len(best) > 1 else best[0]
+                if v < 0 or (v == 0 and np.signbit(v)):
+                    want |= 8
+                assert int(codes[r, 32 * b + j]) == int(want), (r, b, j, v)
+
+
+def check_mxfp4_scale_invariance(orc):
+    rng = np.random.default_rng(6)
+    x = rng.normal(size=(3, 64))
+    p0, e0 = orc.quantize_blocks_mxfp4(x)
+    for k in (-11, 2, 30):
+        p1, e1 = orc.quantize_blocks_mxfp4(np.ldexp(x, k))
+        assert np.array_equal(p0, p1) and np.array_equal(e1.astype(int), e0.astype(int) + k)
+    dec = orc.decode_mxfp4(p0, e0)
+    amax = np.abs(x).reshape(3, 2, 32).max(axis=2).repeat(32, axis=1)
+    assert np.all(np.abs(dec - x) <= amax / 4 + 1e-12)   # half of E2M1's widest step, scaled
+
+
+def check_forward_mxfp4_store(orc):
+    """The path over MX block-32 stores with E2M1 elements equals the path over
+    the same values stored exactly in bf16."""
+    rng = np.random.default_rng(14)
+    n = 24
+    codes = rng.integers(0, 16, (n, 576)).astype(np.uint8)
+    exps = rng.integers(118, 126, (n, 18)).astype(np.uint8)
+    vals = orc.e2m1_table()[codes] * np.ldexp(1.0, exps.astype(int) - 127).repeat(32, axis=1)
+    vals_bits = torch.from_numpy(vals.astype(np.float32)).to(torch.bfloat16)
+    assert np.array_equal(vals_bits.double().numpy(), vals)
+    kint = rng.integers(-3, 4, (n, 128))
+    kcodes = orc.encode_e2m1(kint.astype(float))
+    kexps = rng.integers(125, 130, (n, 4)).astype(np.uint8)
+    kvals = torch.from_numpy((kint * np.ldexp(1.0, kexps.astype(int) - 127).repeat(32, axis=1)).astype(np.float32))
+    pack = lambda c: (c[:, 0::2] | (c[:, 1::2] << 4)).astype(np.uint8)
+    q_idx = rng.integers(-3, 4, (1, 64, 128)).astype(float)
+    w = rng.integers(0, 5, (1, 64)).astype(float)
+    q_abs = rng.standard_normal((1, 64, 576))
+    tau = 1 / math.sqrt(192)
+    args = (np.zeros(1, np.int32), np.array([n - 1], np.int32), np.zeros(1, np.int64), np.array([n], np.int32))
+    a = orc.forward(*args, q_idx, w, orc.Store(pack(kcodes), "mxfp4", kexps), q_abs,
+                    orc.Store(pack(codes), "mxfp4", exps), None, 5, tau)
+    b = orc.forward(*args, q_idx, w, orc.Store(kvals.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), "bf16"),
+                    q_abs, orc.Store(vals_bits.view(torch.int16).numpy().view(np.uint16), "bf16"), None, 5, tau)
+    assert np.array_equal(a["indices"], b["indices"])
+    assert np.allclose(a["out"], b["out"], rtol=1e-13, atol=1e-15)
 
 
 # ---------------------------------------------------------------- indexer
@@ -521,4 +621,5 @@ ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_exampl
               check_e4m3fn_encode, check_quantize_rows, check_cache_append, check_e8m0_table,
               check_mxfp8_worked_example, check_mxfp8_brute_force, check_mxfp8_scale_invariance,
               check_forward_mxfp8_store, check_output_projection_unabsorbed,
-              check_output_projection_selection]
+              check_output_projection_selection, check_e2m1_table, check_mxfp4_worked_example,
+              check_mxfp4_brute_force, check_mxfp4_scale_invariance, check_forward_mxfp4_store]

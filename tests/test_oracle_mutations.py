@@ -148,6 +148,25 @@ def _proj_value_major(o, w_uv, w_o):
     return u.reshape(T, -1) @ np.asarray(w_o).T
 
 
+def _mx4_nibbles_swapped(x):
+    pay, ex = _ORIG_MX4(x)
+    return ((pay >> 4) | ((pay & 0xF) << 4)).astype(np.uint8), ex
+
+
+def _mx4_exponent_like_fp8(x):
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    blocks = x.reshape(n, d // 32, 32)
+    amax = np.max(np.abs(blocks), axis=2)
+    exps = np.zeros(amax.shape, dtype=np.uint8)
+    nz = amax > 0
+    exps[nz] = np.clip(np.floor(np.log2(amax[nz])) - 8, -127, 127) + 127
+    codes = base.encode_e2m1(blocks / np.ldexp(1.0, exps.astype(int) - 127)[:, :, None]).reshape(n, d)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), exps
+
+
+_ORIG_MX4 = base.quantize_blocks_mxfp4
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -167,6 +186,8 @@ MUTANTS = {
     "mx_decode_bias_128": dict(decode_mxfp8=_mx_decode_bias_128),
     "proj_uv_transposed": dict(output_projection=_proj_transposed_uv),
     "proj_heads_value_major": dict(output_projection=_proj_value_major),
+    "mx4_nibbles_swapped": dict(quantize_blocks_mxfp4=_mx4_nibbles_swapped),
+    "mx4_exponent_offset_8": dict(quantize_blocks_mxfp4=_mx4_exponent_like_fp8),
 }
 
 
