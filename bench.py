@@ -44,7 +44,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
 COPY_BYTES = 1 << 30                # calibration copy size
 WORKLOADS = {"tiny_decode_4k": 0, "batched_decode_ragged_16k_32k": 1, "long_decode_128k": 2,
              "chunked_prefill_128k": 3,
-             "extended_decode_256k_fp8": 4, "extended_decode_256k_mxfp8": 5}
+             "extended_decode_256k_fp8": 4, "extended_decode_256k_mxfp8": 5,
+             "extended_decode_256k_mxfp4": 6}
 PMC_WORKLOAD = "long_decode_128k"
 PMC_FILE = os.path.join(ROOT, "profiles", "indexer_long_decode_128k_pmc.json")
 # the sources the indexer kernel is built from
@@ -102,12 +103,19 @@ def visible(wl) -> np.ndarray:
     return wl.token_pos.astype(np.int64) + 1
 
 
+# bytes per cached row, scales included: the indexer key (128 elements) and the
+# latent row (576): bf16; E4M3FN + an fp32 row scale; MX E4M3FN or E2M1 + one
+# E8M0 byte per 32 elements
+KEY_ROW_BYTES = {"bf16": 256, "e4m3fn": 128 + 4, "mxfp8": 128 + 4, "mxfp4": 64 + 4}
+KV_ROW_BYTES = {"bf16": 1152, "e4m3fn": 576 + 4, "mxfp8": 576 + 18, "mxfp4": 288 + 18}
+
+
 def indexer_bytes(wl) -> int:
     """Algorithmic bytes of one indexer launch: every visible indexer key once
-    (128 elements, plus a 4-byte scale for fp8) and each token's 64x128 bf16
+    (KEY_ROW_BYTES for the cache format) and each token's 64x128 bf16
     query and 64 fp32 head weights. Keys shared by several tokens of one
     sequence count once."""
-    per_row = 128 * (1 if wl.fp8 else 2) + (4 if wl.fp8 else 0)   # MX: 4 one-byte exponents
+    per_row = KEY_ROW_BYTES[wl.cache_fmt]
     rows = 0
     for b in range(wl.num_seqs):
         sel = wl.token_seq == b
@@ -125,10 +133,10 @@ def indexer_flops(wl) -> int:
 
 def step_bytes(wl) -> int:
     """Algorithmic bytes of one whole step: the indexer's bytes plus, per token,
-    its min(k, visible) selected latent rows (576 elements, plus a scale for fp8),
+    its min(k, visible) selected latent rows (KV_ROW_BYTES for the format),
     its 64x576 bf16 absorbed query, 64 gate logits, and its fp32 output
     (64x512) and lse (64)."""
-    per_row = 576 * (1 if wl.fp8 else 2) + ((18 if wl.mx else 4) if wl.fp8 else 0)
+    per_row = KV_ROW_BYTES[wl.cache_fmt]
     sel_rows = int(np.minimum(visible(wl), wl.k).sum())
     per_tok = 64 * 576 * 2 + 64 * 4 + 64 * 512 * 4 + 64 * 4
     return indexer_bytes(wl) + sel_rows * per_row + wl.num_tokens * per_tok
@@ -138,9 +146,8 @@ def append_bytes(wl) -> int:
     """Algorithmic bytes of one cache append of every token's new rows: the
     bf16 latent (576) and indexer key (128) read, the token's metadata
     (sequence, position, start, length: 20 bytes) read, and the rows written
-    in the cache format (plus one fp32 scale per row for fp8, one byte per
-    32 elements for MX)."""
-    out = ((576 + 128 + (22 if wl.mx else 8)) if wl.fp8 else (576 + 128) * 2)
+    in the cache format, scales included (KV_ROW_BYTES + KEY_ROW_BYTES)."""
+    out = KV_ROW_BYTES[wl.cache_fmt] + KEY_ROW_BYTES[wl.cache_fmt]
     return wl.num_tokens * ((576 + 128) * 2 + 20 + out)
 
 

@@ -41,6 +41,11 @@
  *   to bf16, which is exact while the products are bf16 normals or zero, so
  *   every exponent of a nonzero block must be at least 10 (scale >= 2^-117);
  *   below that the smallest values lose bits.
+ * - SGA_MXFP4_E2M1 is the same block-32 form with OCP E2M1 elements (values
+ *   0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte, element
+ *   2i in the low nibble of byte i: 64 payload bytes per indexer key row and
+ *   288 per latent row, with the same exponent arrays. Exponents of nonzero
+ *   blocks must be at least 2 (scale >= 2^-125).
  */
 #ifndef SGA_H
 #define SGA_H
@@ -78,7 +83,8 @@ typedef enum sga_status {
 typedef enum sga_dtype {
   SGA_BF16 = 0,
   SGA_FP8_E4M3 = 1,         /* OCP E4M3FN payload + fp32 scale per row */
-  SGA_MXFP8_E4M3 = 2        /* OCP E4M3FN payload + E8M0 exponent per 32 elements */
+  SGA_MXFP8_E4M3 = 2,       /* OCP E4M3FN payload + E8M0 exponent per 32 elements */
+  SGA_MXFP4_E2M1 = 3        /* OCP E2M1 payload, two per byte + E8M0 exponent per 32 elements */
 } sga_dtype;
 
 /*
@@ -131,9 +137,10 @@ typedef struct sga_trace {
  * times its 32-element block's E8M0 scale (MX).
  *   q_idx       [T,64,128] bf16, row-major.
  *   w           [T,64] fp32 head weights.
- *   k_idx       [cache_rows,128] bf16 or E4M3FN payload, row-major (256 or 128 B per row).
- *   k_idx_scale [cache_rows] fp32 (fp8), [cache_rows,4] uint8 E8M0 (MX, 4-byte
- *               aligned); must be NULL for bf16.
+ *   k_idx       [cache_rows,128] bf16, E4M3FN or packed E2M1 payload, row-major
+ *               (256, 128 or 64 B per row).
+ *   k_idx_scale [cache_rows] fp32 (fp8), [cache_rows,4] uint8 E8M0 (MX, both
+ *               element types, 4-byte aligned); must be NULL for bf16.
  *   scores      [T, ld] fp32, ld >= max_len. Only entries s < n_t are written.
  * Accumulation is fp32 (bf16 products are exact in fp32). With integer-valued
  * inputs every partial sum is an integer, so the scores are exact whenever
@@ -180,7 +187,8 @@ SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t
  *   lse[t*64+h] = log(sum_j exp(z_j))                (natural log)
  * An fp8 row is payload * kv_scale[row]; an MX row is each payload times its
  * 32-column block's scale. With J empty, out = 0 and lse = -inf.
- *   q_abs [T,64,576] bf16. kv [cache_rows,576] bf16 or E4M3FN payload.
+ *   q_abs [T,64,576] bf16. kv [cache_rows,576] bf16, E4M3FN or packed E2M1
+ *   payload (1152, 576 or 288 B per row).
  *   kv_scale [cache_rows] fp32 (fp8), [cache_rows,18] uint8 E8M0 (MX), NULL
  *   for bf16. indices [T,k] int32.
  *   out [T,64,512] fp32. lse [T,64] fp32 or NULL.
@@ -236,6 +244,10 @@ SGA_API sga_status sga_forward(const sga_batch* batch,
  *   e = clamp(floor(log2 max|x|) - 8, -127, 127) + 127 (e = 0 for a block of
  *   zeros; 8 is the exponent of 448), stored in byte r*D/32 + block of the
  *   scale array, and payload = x * 2^(127 - e) encoded as above.
+ * An SGA_MXFP4_E2M1 cache gets e = clamp(floor(log2 max|x|) - 2, -127, 127)
+ *   + 127 (2 is the exponent of 6) and payload = x * 2^(127 - e) rounded to
+ *   the nearest E2M1 value, ties to the even code, saturating at 6, packed two
+ *   per byte, low nibble first.
  * The scale arrays must be NULL for a bf16 cache and non-NULL otherwise.
  * A token with b outside [0, num_seqs), p outside [0, seq_len[b]) or r outside
  * [0, cache_rows) writes nothing. Tokens writing the same row race; the

@@ -36,6 +36,11 @@ drawn in their stored form:
   2^(e - 127), cast to E4M3FN (nearest even, clamped to 448);
 - indexer keys: payload = the integer itself, each block's exponent 127 + u
   with u drawn uniformly from [-2, 2].
+The same with four-bit E2M1 elements (two per byte, low nibble first):
+- latent rows: every element's code drawn uniformly from the 16 E2M1 codes,
+  each block's exponent uniform in [119, 120];
+- indexer keys: the E2M1 code of the integer (0, 1, 2, 3 are codes 0, 2, 4,
+  5, negatives add the sign bit 8), exponents as above.
 """
 from __future__ import annotations
 
@@ -58,7 +63,7 @@ E4M3_MAX = 448.0
 
 CONFIG_NAMES = ("tiny_decode_4k", "batched_decode_ragged_16k_32k",
                 "long_decode_128k", "chunked_prefill_128k", "extended_decode_256k_fp8",
-                "extended_decode_256k_mxfp8")
+                "extended_decode_256k_mxfp8", "extended_decode_256k_mxfp4")
 
 
 @dataclass
@@ -70,9 +75,9 @@ class Workload:
     token_pos: np.ndarray    # int32 [T]
     q_idx: torch.Tensor      # bf16 [T, 64, 128]
     w: torch.Tensor          # fp32 [T, 64]
-    k_idx: torch.Tensor      # bf16 or float8_e4m3fn [rows, 128]
+    k_idx: torch.Tensor      # bf16 or float8_e4m3fn [rows, 128], or uint8 [rows, 64] (E2M1 pairs)
     k_idx_scale: Optional[torch.Tensor]  # fp32 [rows] (fp8), uint8 [rows, 4] (MX), else None
-    kv: torch.Tensor         # bf16 or float8_e4m3fn [rows, 576]
+    kv: torch.Tensor         # bf16 or float8_e4m3fn [rows, 576], or uint8 [rows, 288] (E2M1 pairs)
     kv_scale: Optional[torch.Tensor]     # fp32 [rows] (fp8), uint8 [rows, 18] (MX), else None
     q_abs: torch.Tensor      # bf16 [T, 64, 576]
     gate: torch.Tensor       # fp32 [T, 64]
@@ -99,18 +104,18 @@ class Workload:
         return int(self.token_pos.max()) + 1
 
     @property
+    def cache_fmt(self) -> str:
+        """The format name the oracle's Store uses: bf16, e4m3fn, mxfp8 or mxfp4."""
+        return self.meta.get("fmt", "bf16")
+
+    @property
     def fp8(self) -> bool:
-        """One-byte E4M3FN payloads (per-row or MX block scales)."""
-        return self.kv.dtype == torch.float8_e4m3fn
+        """Narrow payloads with scales (E4M3FN per row, or an MX format)."""
+        return self.cache_fmt != "bf16"
 
     @property
     def mx(self) -> bool:
-        return self.kv_scale is not None and self.kv_scale.dim() == 2
-
-    @property
-    def cache_fmt(self) -> str:
-        """The format name the oracle's Store uses."""
-        return "mxfp8" if self.mx else ("e4m3fn" if self.fp8 else "bf16")
+        return self.cache_fmt in ("mxfp8", "mxfp4")
 
 
 def _bf16(x: np.ndarray) -> torch.Tensor:
@@ -133,16 +138,18 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
           fp8: bool = False, kv_sigma: float = 1.0 / 24.0, q_abs_mult: float = 1.0,
           idx_range: int = 3, w_range: tuple = (0, 4), gate_sigma: float = 2.0,
           k: int = TOP_K, sm_scale: float = SM_SCALE, chunk_rows: int = 1 << 16,
-          mx: bool = False) -> Workload:
+          mx: bool = False, mx4: bool = False) -> Workload:
     """Draw one workload.
 
     lengths: cached rows per sequence. tokens: (sequence, position) per query token.
     Draw order: lengths are given; then indexer keys, indexer queries, head
     weights, latent cache (with each chunk's block exponents for MX), absorbed
     queries, gate logits, fp8 key-scale exponents. mx: MX block-32 caches
-    (implies fp8 payloads).
+    with E4M3FN elements; mx4: with four-bit E2M1 elements.
     """
-    fp8 = fp8 or mx
+    fmt = "mxfp4" if mx4 else ("mxfp8" if mx else ("e4m3fn" if fp8 else "bf16"))
+    fp8 = fmt != "bf16"
+    mx = fmt in ("mxfp8", "mxfp4")
     rng = np.random.default_rng(seed)
     lengths = np.asarray(lengths, dtype=np.int64)
     B = int(lengths.shape[0])
@@ -168,7 +175,12 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
         r1 = min(rows, r0 + chunk_rows)
         x = rng.standard_normal(size=(r1 - r0, D_QK), dtype=np.float32)
         x *= np.float32(kv_sigma)
-        if mx:
+        if mx4:
+            codes = rng.integers(0, 16, size=(r1 - r0, D_QK), dtype=np.uint8)
+            e = rng.integers(119, 121, size=(r1 - r0, D_QK // 32))
+            kv_parts.append(torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)))
+            kv_scale_parts.append(torch.from_numpy(e.astype(np.uint8)))
+        elif mx:
             e = rng.integers(118, 122, size=(r1 - r0, D_QK // 32))
             inv = np.ldexp(np.float32(1.0), 127 - e).astype(np.float32)
             kv_parts.append(_to_e4m3(x * np.repeat(inv, 32, axis=1)))
@@ -181,6 +193,8 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
             kv_parts.append(_bf16(x))
     if kv_parts:
         kv = torch.cat(kv_parts)
+    elif mx4:
+        kv = torch.zeros((0, D_QK // 2), dtype=torch.uint8)
     else:
         kv = torch.zeros((0, D_QK), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16)
     if mx:
@@ -191,7 +205,13 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
     q_abs = rng.standard_normal(size=(T, N_HEADS, D_QK), dtype=np.float32) * np.float32(q_abs_mult)
     gate = (rng.standard_normal(size=(T, N_HEADS)) * gate_sigma).astype(np.float32)
 
-    if mx:
+    if mx4:
+        u = rng.integers(-2, 3, size=(rows, IDX_DIM // 32))
+        mag = np.array([0, 2, 4, 5], dtype=np.uint8)[np.abs(k_int)]     # E2M1 codes of 0..3
+        codes = mag | np.where(k_int < 0, np.uint8(8), np.uint8(0)).astype(np.uint8)
+        k_idx = torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+        k_idx_scale = torch.from_numpy((127 + u).astype(np.uint8))
+    elif mx:
         u = rng.integers(-2, 3, size=(rows, IDX_DIM // 32))
         k_idx = _to_e4m3(k_int.astype(np.float32))
         k_idx_scale = torch.from_numpy((127 + u).astype(np.uint8))
@@ -207,7 +227,7 @@ def build(name: str, lengths: Sequence[int], tokens: Sequence[tuple], seed: int,
                     token_seq=token_seq, token_pos=token_pos, q_idx=_bf16(q_idx),
                     w=torch.from_numpy(w), k_idx=k_idx, k_idx_scale=k_idx_scale, kv=kv,
                     kv_scale=kv_scale, q_abs=_bf16(q_abs), gate=torch.from_numpy(gate),
-                    k=k, sm_scale=sm_scale, meta={"seed": seed, "fp8": fp8, "mx": mx})
+                    k=k, sm_scale=sm_scale, meta={"seed": seed, "fmt": fmt})
 
 
 def append_rows(num_tokens: int, seed: int, *, kv_sigma: float = 1.0 / 24.0, key_sigma: float = 1.0,
@@ -239,7 +259,8 @@ def proj_weights(seed: int, d_model: int = D_MODEL):
 
 
 def config(i: int, seed: Optional[int] = None) -> Workload:
-    """The five workloads, and a sixth: the 256K decode with MX block-32 caches.
+    """The five workloads, then the 256K decode with MX block-32 caches of E4M3FN
+    (6th) and of four-bit E2M1 elements (7th).
     The seed defaults to the workload's number."""
     s = i if seed is None else seed
     if i == 0:   # tiny decode: 1 sequence of 4096, tokens at 4092..4095
@@ -256,10 +277,13 @@ def config(i: int, seed: Optional[int] = None) -> Workload:
         return build(CONFIG_NAMES[4], [262144] * 8, [(b, 262143) for b in range(8)], s, fp8=True)
     if i == 5:   # the same shape with MX block-32 caches (the training recipe's format)
         return build(CONFIG_NAMES[5], [262144] * 8, [(b, 262143) for b in range(8)], s, mx=True)
+    if i == 6:   # and with four-bit MX block-32 caches
+        return build(CONFIG_NAMES[6], [262144] * 8, [(b, 262143) for b in range(8)], s, mx4=True)
     raise ValueError(f"no workload {i}")
 
 
 def describe(wl: Workload) -> dict:
     return {"workload": wl.name, "batch": wl.num_seqs, "query_tokens": wl.num_tokens,
             "max_context": wl.max_len, "top_k": wl.k,
-            "cache": "mxfp8_e4m3" if wl.mx else ("fp8_e4m3" if wl.fp8 else "bf16")}
+            "cache": {"bf16": "bf16", "e4m3fn": "fp8_e4m3", "mxfp8": "mxfp8_e4m3",
+                      "mxfp4": "mxfp4_e2m1"}[wl.cache_fmt]}

@@ -18,7 +18,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsga.so")
 
 SGA_OK, SGA_ERR_INVALID_ARG, SGA_ERR_UNSUPPORTED, SGA_ERR_WORKSPACE, SGA_ERR_HIP = range(5)
-SGA_BF16, SGA_FP8_E4M3, SGA_MXFP8_E4M3 = 0, 1, 2
+SGA_BF16, SGA_FP8_E4M3, SGA_MXFP8_E4M3, SGA_MXFP4_E2M1 = 0, 1, 2, 3
 MX_BLOCK = 32
 HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK, D_V = 64, 64, 128, 512, 576, 128
 
@@ -118,24 +118,38 @@ def _check(t: torch.Tensor, name: str, dtypes, shape=None):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {shape}")
 
 
-def _store_dtype(t: torch.Tensor, scale: Optional[torch.Tensor], name: str) -> int:
-    """The cache format from the tensors: bf16 rows; float8_e4m3fn rows with one
-    fp32 scale per row; or float8_e4m3fn rows with one E8M0 exponent (uint8 or
-    float8_e8m0fnu) per 32 elements, [rows, width/32] (MX block-32)."""
+_E8M0 = tuple(d for d in (torch.uint8, getattr(torch, "float8_e8m0fnu", None)) if d is not None)
+_FP4X2 = tuple(d for d in (torch.uint8, getattr(torch, "float4_e2m1fn_x2", None)) if d is not None)
+
+
+def _cache_dtype(t: torch.Tensor, scale: Optional[torch.Tensor], name: str, rows: int, width: int) -> int:
+    """Checks a cache of `rows` rows of `width` elements and its scales, and
+    returns its sga_dtype from the tensors:
+    - bfloat16 [rows, width], no scale;
+    - float8_e4m3fn [rows, width] with fp32 scales [rows] (one per row);
+    - float8_e4m3fn [rows, width] with E8M0 exponents [rows, width/32] (uint8 or
+      float8_e8m0fnu): MX block-32;
+    - uint8 or float4_e2m1fn_x2 [rows, width/2] (two E2M1 elements per byte,
+      low nibble first) with E8M0 exponents [rows, width/32]: MX block-32, four-bit."""
     if t.dtype == torch.bfloat16:
+        _check(t, name, (torch.bfloat16,), (rows, width))
         if scale is not None:
             raise ValueError(f"{name}: bf16 storage takes no scale")
         return SGA_BF16
+    if scale is None:
+        raise ValueError(f"{name}: {t.dtype} storage needs scales")
     if t.dtype == torch.float8_e4m3fn:
-        if scale is None:
-            raise ValueError(f"{name}: fp8 storage needs scales")
+        _check(t, name, (torch.float8_e4m3fn,), (rows, width))
         if scale.dtype == torch.float32:
-            _check(scale, name + "_scale", (torch.float32,), (t.shape[0],))
+            _check(scale, name + "_scale", (torch.float32,), (rows,))
             return SGA_FP8_E4M3
-        _check(scale, name + "_scale", (torch.uint8, torch.float8_e8m0fnu),
-               (t.shape[0], t.shape[1] // MX_BLOCK))
+        _check(scale, name + "_scale", _E8M0, (rows, width // MX_BLOCK))
         return SGA_MXFP8_E4M3
-    raise TypeError(f"{name} must be bfloat16 or float8_e4m3fn, got {t.dtype}")
+    if t.dtype in _FP4X2:
+        _check(t, name, _FP4X2, (rows, width // 2))
+        _check(scale, name + "_scale", _E8M0, (rows, width // MX_BLOCK))
+        return SGA_MXFP4_E2M1
+    raise TypeError(f"{name} must be bfloat16, float8_e4m3fn or packed four-bit (uint8), got {t.dtype}")
 
 
 def _stream(t: torch.Tensor):
@@ -179,8 +193,7 @@ def sga_index_scores(batch: Batch, q_idx, w, k_idx, k_idx_scale, scores) -> None
     T = batch.num_tokens
     _check(q_idx, "q_idx", (torch.bfloat16,), (T, IDX_HEADS, IDX_DIM))
     _check(w, "w", (torch.float32,), (T, IDX_HEADS))
-    _check(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, IDX_DIM))
-    dt = _store_dtype(k_idx, k_idx_scale, "k_idx")
+    dt = _cache_dtype(k_idx, k_idx_scale, "k_idx", batch.cache_rows, IDX_DIM)
     _check(scores, "scores", (torch.float32,), (T, None))
     b = batch.c()
     _raise("sga_index_scores", load().sga_index_scores(
@@ -211,8 +224,7 @@ def sga_sparse_mla_attn(batch: Batch, q_abs, kv, kv_scale, indices, k: int, sm_s
                         gate, out, lse=None, ws: Optional[torch.Tensor] = None) -> None:
     T = batch.num_tokens
     _check(q_abs, "q_abs", (torch.bfloat16,), (T, HEADS, D_QK))
-    _check(kv, "kv", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, D_QK))
-    dt = _store_dtype(kv, kv_scale, "kv")
+    dt = _cache_dtype(kv, kv_scale, "kv", batch.cache_rows, D_QK)
     _check(indices, "indices", (torch.int32,), (T, k))
     if gate is not None:
         _check(gate, "gate", (torch.float32,), (T, HEADS))
@@ -237,11 +249,9 @@ def sga_forward(batch: Batch, q_idx, w, k_idx, k_idx_scale, q_abs, kv, kv_scale,
     T = batch.num_tokens
     _check(q_idx, "q_idx", (torch.bfloat16,), (T, IDX_HEADS, IDX_DIM))
     _check(w, "w", (torch.float32,), (T, IDX_HEADS))
-    _check(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, IDX_DIM))
-    kdt = _store_dtype(k_idx, k_idx_scale, "k_idx")
+    kdt = _cache_dtype(k_idx, k_idx_scale, "k_idx", batch.cache_rows, IDX_DIM)
     _check(q_abs, "q_abs", (torch.bfloat16,), (T, HEADS, D_QK))
-    _check(kv, "kv", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, D_QK))
-    vdt = _store_dtype(kv, kv_scale, "kv")
+    vdt = _cache_dtype(kv, kv_scale, "kv", batch.cache_rows, D_QK)
     if gate is not None:
         _check(gate, "gate", (torch.float32,), (T, HEADS))
     _check(out, "out", (torch.float32,), (T, HEADS, D_LATENT))
@@ -270,11 +280,9 @@ def sga_cache_append(batch: Batch, latent=None, idx_key=None, kv=None, kv_scale=
     if idx_key is not None:
         _check(idx_key, "idx_key", (torch.bfloat16,), (T, IDX_DIM))
     if kv is not None:
-        _check(kv, "kv", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, D_QK))
-        vdt = _store_dtype(kv, kv_scale, "kv")
+        vdt = _cache_dtype(kv, kv_scale, "kv", batch.cache_rows, D_QK)
     if k_idx is not None:
-        _check(k_idx, "k_idx", (torch.bfloat16, torch.float8_e4m3fn), (batch.cache_rows, IDX_DIM))
-        kdt = _store_dtype(k_idx, k_idx_scale, "k_idx")
+        kdt = _cache_dtype(k_idx, k_idx_scale, "k_idx", batch.cache_rows, IDX_DIM)
     ref = next((t for t in (latent, idx_key, kv, k_idx) if t is not None), batch.token_seq)
     b = batch.c()
     _raise("sga_cache_append", load().sga_cache_append(

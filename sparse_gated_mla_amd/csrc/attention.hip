@@ -35,7 +35,8 @@
 // multiplies the row's logit and probability. MX block-32 rows (fact sheet,
 // Training: MXFP8, one scale per 32 consecutive elements) have each 32-column
 // block multiplied by its power-of-two scale as it is widened, which is exact
-// in bf16, and are then attended like bf16 rows.
+// in bf16, and are then attended like bf16 rows. The same holds for MX rows of
+// four-bit E2M1 elements (two per byte).
 //
 // With several splits per token, each split writes its output normalised by
 // its own exp-sum, in fp16 with a per-half scale, plus (max, exp-sum);
@@ -70,11 +71,12 @@ __device__ __forceinline__ float gate_factor(const float* gate, int64_t idx) {
 // of the tile (row u / kUnitsPerRow, unit u % kUnitsPerRow of that row).
 template <int kFmt>
 struct RowStage {
-  static constexpr bool kFp8 = kFmt != kFmtBf16;                  // one-byte payloads
-  static constexpr int kRowBytes = kFp8 ? kDQK : 2 * kDQK;       // cached bytes per row
-  static constexpr int kUnitsPerRow = kRowBytes / 16;             // 36 or 72
-  static constexpr int kUnits = kAttnTileRows * kUnitsPerRow;     // 1152 or 2304
-  static constexpr int kPer = (kUnits + kAttnThreads - 1) / kAttnThreads;  // 3 or 5
+  static constexpr bool kFp8 = kFmt != kFmtBf16;                  // narrow payloads, widened in LDS
+  static constexpr bool kMx = kFmt == kFmtMx || kFmt == kFmtMx4;  // E8M0 block exponents
+  static constexpr int kRowBytes = row_bytes(kFmt, kDQK);         // cached bytes per row
+  static constexpr int kUnitsPerRow = kRowBytes / 16;             // 72, 36 or 18
+  static constexpr int kUnits = kAttnTileRows * kUnitsPerRow;     // 2304, 1152 or 576
+  static constexpr int kPer = (kUnits + kAttnThreads - 1) / kAttnThreads;  // 5, 3 or 2
   u32x4 v[kPer];
   uint32_t s[kPer];     // the unit's fp32 row scale (fp8) or its block's E8M0 exponent (MX)
   int32_t idx[kPer];    // row indices for the next load_rows
@@ -110,9 +112,10 @@ struct RowStage {
                                            rows, (int)(((uint32_t)id * kRowBytes + 16u * c) | skip), 0, kNonTemporal));
       if constexpr (kFmt == kFmtFp8)
         s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, (int)(((uint32_t)id * 4u) | skip), 0, 0);
-      if constexpr (kFmt == kFmtMx)   // 16 payload bytes = half of block c/2
+      if constexpr (kMx)   // the unit's block: c/2 (16 E4M3FN bytes) or c (32 E2M1 nibbles)
         s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-            scales, (int)(((uint32_t)id * (kDQK / 32) + (uint32_t)(c >> 1)) | skip), 0, 0);
+            scales, (int)(((uint32_t)id * (kDQK / 32) + (uint32_t)(kFmt == kFmtMx ? c >> 1 : c)) | skip),
+            0, 0);
     }
     ok = m;
     // keep each tile's loads together, in program order
@@ -130,6 +133,13 @@ struct RowStage {
         uint8_t* row = region + r * (2 * kRowStride);
         if constexpr (!kFp8) {
           *reinterpret_cast<u32x4*>(row + 16 * c) = v[q];
+        } else if constexpr (kFmt == kFmtMx4) {
+          const float bs = e8m0_to_f32(s[q]);
+          u32x4* dst = reinterpret_cast<u32x4*>(row + 64 * c);
+          dst[0] = e2m1x8_scaled_to_bf16x8(v[q].x, bs);
+          dst[1] = e2m1x8_scaled_to_bf16x8(v[q].y, bs);
+          dst[2] = e2m1x8_scaled_to_bf16x8(v[q].z, bs);
+          dst[3] = e2m1x8_scaled_to_bf16x8(v[q].w, bs);
         } else {
           u32x2 a0, a1, a2, a3;
           if constexpr (kFmt == kFmtMx) {
@@ -340,8 +350,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   const rsrc_t rows = make_rsrc(a.kv + base * Stage::kRowBytes, rows_bytes);
   const rsrc_t scales =
       kFmt == kFmtFp8 ? make_rsrc(static_cast<const float*>(a.kv_scale) + base, (uint32_t)max(n, 0) * 4u)
-      : kFmt == kFmtMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
-                                   (uint32_t)max(n, 0) * (kDQK / 32))
+      : Stage::kMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
+                               (uint32_t)max(n, 0) * (kDQK / 32))
                        : make_rsrc(a.kv, 0u);
   const rsrc_t idx_rs = make_rsrc(a.indices + (int64_t)t * a.k + j_begin, (uint32_t)nrows * 4u);
 
@@ -453,6 +463,7 @@ hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s) {
   dim3 grid(a.splits, a.num_tokens);
   if (fmt == kFmtFp8) attn_kernel<kFmtFp8><<<grid, kAttnThreads, 0, s>>>(a);
   else if (fmt == kFmtMx) attn_kernel<kFmtMx><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4><<<grid, kAttnThreads, 0, s>>>(a);
   else attn_kernel<kFmtBf16><<<grid, kAttnThreads, 0, s>>>(a);
   return hipGetLastError();
 }

@@ -17,7 +17,10 @@
 // MX: block exponent e - 127 = floor(log2 max|x|) - 8 (8 = exponent of 448),
 // clamped to [-127, 127], e = 0 for a block of zeros (the Open Compute
 // Project MX format's rule); each element is x * 2^(127 - e) (exact) encoded
-// as above.
+// as above. With four-bit E2M1 elements the exponent is floor(log2 max|x|) - 2
+// (6 = 1.5 * 2^2 is E2M1's largest value), the element spacing is 2^(e-1) in
+// binade [2^e, 2^(e+1)) and 0.5 below 1, rounding is nearest-even, saturating
+// at 6, and two elements share a byte, the lower-indexed one in the low nibble.
 //
 // Mapping: one workgroup of two waves per token; wave 0 writes the latent row
 // (72 16-byte units, one or two per lane), wave 1 the indexer key (16 units).
@@ -40,6 +43,22 @@ __device__ __forceinline__ uint32_t e4m3fn_encode(float x) {
   if (ev < -6) return sign | (uint32_t)ldexpf(v, 9);          // subnormal: v / 2^-9
   const uint32_t m = (uint32_t)ldexpf(v, 3 - ev) - 8u;        // v / 2^(ev-3) in [8, 16)
   return sign | ((uint32_t)(ev + 7) << 3) | m;
+}
+
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 28) & 0x8u;
+  const float a = fminf(fabsf(x), 6.0f);
+  int ea;
+  frexpf(a, &ea);                       // a = f * 2^ea, f in [0.5, 1)
+  const int eb = max(ea - 1, 0);        // binade exponent; below 1 the spacing stays 0.5
+  const float v = ldexpf(rintf(ldexpf(a, 1 - eb)), eb - 1);   // nearest code value
+  if (v == 0.0f) return sign;
+  if (v < 1.0f) return sign | 1u;       // 0.5
+  int ev;
+  frexpf(v, &ev);
+  ev -= 1;                              // floor(log2 v): 0, 1 or 2
+  const uint32_t m = ldexpf(v, -ev) > 1.0f ? 1u : 0u;        // 1.5 * 2^ev
+  return sign | ((uint32_t)(ev + 1) << 1) | m;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -69,7 +88,8 @@ __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uin
     }
     return;
   }
-  if (fmt == kFmtMx) {
+  if (fmt == kFmtMx || fmt == kFmtMx4) {
+    const bool four = fmt == kFmtMx4;
     // a block of 32 elements is units 4b .. 4b+3: four neighbouring lanes
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
@@ -83,19 +103,29 @@ __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uin
       if (bmax > 0.0f) {
         int ea;
         frexpf(bmax, &ea);                       // floor(log2 bmax) = ea - 1
-        e = min(max(ea - 1 - 8, -127), 127) + 127;
+        e = min(max(ea - 1 - (four ? 2 : 8), -127), 127) + 127;
       }
       if (u < kUnits) {
-        uint32_t b[8];
+        if (four) {
+          uint32_t out = 0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          b[2 * c] = e4m3fn_encode(ldexpf(bf16_lo(v[j][c]), 127 - e));
-          b[2 * c + 1] = e4m3fn_encode(ldexpf(bf16_hi(v[j][c]), 127 - e));
+          for (int c = 0; c < 4; ++c) {
+            out |= e2m1_encode(ldexpf(bf16_lo(v[j][c]), 127 - e)) << (8 * c);
+            out |= e2m1_encode(ldexpf(bf16_hi(v[j][c]), 127 - e)) << (8 * c + 4);
+          }
+          *reinterpret_cast<uint32_t*>(dst + 4 * u) = out;
+        } else {
+          uint32_t b[8];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            b[2 * c] = e4m3fn_encode(ldexpf(bf16_lo(v[j][c]), 127 - e));
+            b[2 * c + 1] = e4m3fn_encode(ldexpf(bf16_hi(v[j][c]), 127 - e));
+          }
+          u32x2 out;
+          out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+          out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+          *reinterpret_cast<u32x2*>(dst + 8 * u) = out;
         }
-        u32x2 out;
-        out.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
-        out.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
-        *reinterpret_cast<u32x2*>(dst + 8 * u) = out;
         if ((u & 3) == 0) static_cast<uint8_t*>(scale_out)[u >> 2] = (uint8_t)e;
       }
     }
@@ -125,7 +155,7 @@ __device__ __forceinline__ void append_row(const uint16_t* __restrict__ src, uin
 // Where row `row`'s scale goes: an fp32 per row, or width/32 E8M0 bytes per row.
 __device__ __forceinline__ void* scale_row(void* base, int fmt, int64_t row, int width) {
   if (fmt == kFmtFp8) return static_cast<float*>(base) + row;
-  if (fmt == kFmtMx) return static_cast<uint8_t*>(base) + row * (width / 32);
+  if (fmt == kFmtMx || fmt == kFmtMx4) return static_cast<uint8_t*>(base) + row * (width / 32);
   return nullptr;
 }
 
@@ -140,12 +170,12 @@ __global__ __launch_bounds__(128) void cache_append_kernel(CacheArgs a) {
   if (row < 0 || row >= a.batch.cache_rows) return;
   if (wave == 0) {
     if (!a.latent || !a.kv) return;
-    append_row<kDQK / 8>(a.latent + (int64_t)t * kDQK, a.kv + row * (a.kv_fmt != kFmtBf16 ? kDQK : 2 * kDQK),
+    append_row<kDQK / 8>(a.latent + (int64_t)t * kDQK, a.kv + row * row_bytes(a.kv_fmt, kDQK),
                          scale_row(a.kv_scale, a.kv_fmt, row, kDQK), a.kv_fmt, lane);
   } else {
     if (!a.key || !a.k_idx) return;
     append_row<kIdxDim / 8>(a.key + (int64_t)t * kIdxDim,
-                            a.k_idx + row * (a.k_idx_fmt != kFmtBf16 ? kIdxDim : 2 * kIdxDim),
+                            a.k_idx + row * row_bytes(a.k_idx_fmt, kIdxDim),
                             scale_row(a.k_idx_scale, a.k_idx_fmt, row, kIdxDim), a.k_idx_fmt, lane);
   }
 }

@@ -22,11 +22,12 @@
 // - Epilogue, per lane: ReLU, times w, summed over the lane's 32 heads. One
 //   cross-half shuffle then gives each position's score, which is stored at
 //   once (and counted, see below) while the wave's next tiles are in flight.
-// - fp8. Keys are widened to bf16 exactly on the LDS read. A per-row fp32
+// - fp8 and MX. Keys are widened to bf16 exactly on the LDS read. A per-row fp32
 //   scale multiplies each head's dot product before the ReLU. An MX block-32
 //   key (fact sheet, Training: MXFP8 with one scale per 32 consecutive
 //   elements) has four E8M0 exponents per row; each is applied to its 32 dims
-//   as they are widened (payload times a power of two is exact in bf16).
+//   as they are widened by gfx950's scaled conversions (payload times a power
+//   of two is exact in bf16), for E4M3FN or E2M1 (four-bit) payloads.
 // - Fused top-k. The variant used by the whole forward pass also counts the
 //   top 12 key bits of every score into a per-token histogram (the first radix
 //   level of the top-k).
@@ -59,14 +60,16 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
 // + r % kRowsPerLoad.
 template <int kFmt>
 struct KeyTile {
-  static constexpr bool kFp8 = kFmt != kFmtBf16;   // one-byte payloads
-  // bf16 tile: 8 loads of 1 KiB (4 rows of 256 B each); load s, lane l -> tile
-  //   row 4s + l/16, 16-byte chunk l%16.
-  // fp8 tile:  4 loads of 1 KiB (8 rows of 128 B each); load s, lane l -> tile
-  //   row 8s + l/8, chunk l%8; plus the 32-bit scale word of tile row l%32
-  //   (the fp32 row scale, or the four E8M0 block exponents).
-  static constexpr int kLoads = kFp8 ? 4 : 8;
-  static constexpr int kRowBytes = kFp8 ? 128 : 256;
+  static constexpr bool kFp8 = kFmt != kFmtBf16;   // a 32-bit scale word per row
+  // A tile is kLoads loads of 1 KiB, kRowsPerLoad rows of kRowBytes each:
+  //   bf16 (256 B rows): 8 loads of 4 rows; fp8 and MX8 (128 B): 4 loads of 8
+  //   rows; MX4 (64 B): 2 loads of 16 rows. Load s, lane l -> tile row
+  //   kRowsPerLoad*s + l/kChunksPerRow, 16-byte chunk l%kChunksPerRow. One-byte
+  //   and four-bit tiles add the 32-bit scale word of tile row l%32 (the fp32
+  //   row scale, or the four E8M0 block exponents).
+  static constexpr int kRowBytes = row_bytes(kFmt, kIdxDim);
+  static constexpr int kChunksPerRow = kRowBytes / 16;
+  static constexpr int kLoads = kTile * kRowBytes / 1024;
   static constexpr int kRowsPerLoad = 1024 / kRowBytes;
   static constexpr int kGroupRows = kWaves * kTile;
   u32x4 v[kLoads];
@@ -91,16 +94,17 @@ struct KeyTile {
     __builtin_amdgcn_sched_barrier(0);
   }
 
-  // swizzled 16-byte slot of chunk c in row r
+  // swizzled 16-byte slot of chunk c in row r: the 16 rows that a b128 read
+  // of one chunk meets in one pass land on 16 distinct 16-byte bank groups
   static __device__ __forceinline__ int slot(int r, int c) {
-    return kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+    return c ^ ((r / (16 / kChunksPerRow)) & (kChunksPerRow - 1));
   }
 
   __device__ __forceinline__ void store(uint8_t* lds, int lane) const {
 #pragma unroll
     for (int s = 0; s < kLoads; ++s) {
-      const int r = kFp8 ? (8 * s + (lane >> 3)) : (4 * s + (lane >> 4));
-      const int c = kFp8 ? (lane & 7) : (lane & 15);
+      const int r = kRowsPerLoad * s + lane / kChunksPerRow;
+      const int c = lane % kChunksPerRow;
       *reinterpret_cast<u32x4*>(lds + r * kRowBytes + 16 * slot(r, c)) = v[s];
     }
   }
@@ -114,6 +118,17 @@ struct KeyTile {
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         b[s] = *reinterpret_cast<const u32x4*>(lds + n * 256 + 16 * slot(n, 8 * g + s));
+    } else if constexpr (kFmt == kFmtMx4) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // chunk 2g + h holds dims 64g + 32h .. +31 (block 2g + h) = steps 4h .. 4h+3
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(lds + n * 64 + 16 * slot(n, 2 * g + h));
+        const float bs = e8m0_to_f32((sw >> (8 * (2 * g + h))) & 0xFFu);
+        b[4 * h] = e2m1x8_scaled_to_bf16x8(raw.x, bs);
+        b[4 * h + 1] = e2m1x8_scaled_to_bf16x8(raw.y, bs);
+        b[4 * h + 2] = e2m1x8_scaled_to_bf16x8(raw.z, bs);
+        b[4 * h + 3] = e2m1x8_scaled_to_bf16x8(raw.w, bs);
+      }
     } else {
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -398,6 +413,7 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int fmt, bool fused_hist
   if (a.num_tokens == 0) return hipSuccess;
   if (fmt == kFmtFp8) return launch_prefill_fmt<kFmtFp8>(a, fused_hist, s);
   if (fmt == kFmtMx) return launch_prefill_fmt<kFmtMx>(a, fused_hist, s);
+  if (fmt == kFmtMx4) return launch_prefill_fmt<kFmtMx4>(a, fused_hist, s);
   return launch_prefill_fmt<kFmtBf16>(a, fused_hist, s);
 }
 
@@ -405,6 +421,7 @@ hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStr
   if (a.num_tokens == 0) return hipSuccess;
   if (fmt == kFmtFp8) return launch_indexer_fmt<kFmtFp8>(a, fused_hist, s);
   if (fmt == kFmtMx) return launch_indexer_fmt<kFmtMx>(a, fused_hist, s);
+  if (fmt == kFmtMx4) return launch_indexer_fmt<kFmtMx4>(a, fused_hist, s);
   return launch_indexer_fmt<kFmtBf16>(a, fused_hist, s);
 }
 

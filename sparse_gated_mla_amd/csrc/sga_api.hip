@@ -127,7 +127,8 @@ sga_status check_store(const void* data, const void* scale, sga_dtype dt, uintpt
   const uintptr_t sa = reinterpret_cast<uintptr_t>(scale);
   if (dt == SGA_BF16) return scale ? SGA_ERR_INVALID_ARG : SGA_OK;
   if (dt == SGA_FP8_E4M3) return scale && sa % alignof(float) == 0 ? SGA_OK : SGA_ERR_INVALID_ARG;
-  if (dt == SGA_MXFP8_E4M3) return scale && sa % mx_align == 0 ? SGA_OK : SGA_ERR_INVALID_ARG;
+  if (dt == SGA_MXFP8_E4M3 || dt == SGA_MXFP4_E2M1)
+    return scale && sa % mx_align == 0 ? SGA_OK : SGA_ERR_INVALID_ARG;
   return SGA_ERR_UNSUPPORTED;
 }
 
@@ -275,7 +276,7 @@ size_t attn_ws(int32_t T, int32_t k) {
 }  // namespace
 
 static_assert(SGA_BF16 == sga::kFmtBf16 && SGA_FP8_E4M3 == sga::kFmtFp8 &&
-                  SGA_MXFP8_E4M3 == sga::kFmtMx,
+                  SGA_MXFP8_E4M3 == sga::kFmtMx && SGA_MXFP4_E2M1 == sga::kFmtMx4,
               "cache formats are passed to the kernels as their sga_dtype values");
 
 extern "C" {

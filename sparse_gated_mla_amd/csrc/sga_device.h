@@ -58,19 +58,23 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
 }
 
 // Four OCP E4M3FN bytes times a power-of-two block scale -> four bf16, packed
-// two per dword. The products are exact in fp32; keeping the upper 16 bits is
-// exact whenever they are bf16 normals or zero (block scale >= 2^-117).
+// two per dword (v_cvt_scalef32_pk_bf16_fp8; exact whenever the products are
+// bf16 normals or zero, i.e. for block scales >= 2^-117).
 __device__ __forceinline__ u32x2 e4m3x4_scaled_to_bf16x4(uint32_t packed, float scale) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, true);
-  lo.x *= scale;
-  lo.y *= scale;
-  hi.x *= scale;
-  hi.y *= scale;
   u32x2 r;
-  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, scale, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, scale, true));
   return r;
+}
+
+// Eight OCP E2M1 nibbles (element 2i in the low nibble of byte i) times a
+// power-of-two block scale -> eight bf16 (v_cvt_scalef32_pk_bf16_fp4; exact
+// for block scales >= 2^-125).
+__device__ __forceinline__ u32x4 e2m1x8_scaled_to_bf16x8(uint32_t packed, float scale) {
+  return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 0)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 1)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 2)),
+               __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 3))};
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).

@@ -19,9 +19,15 @@ struct TopkCtrl {
 constexpr int kFmtBf16 = 0;    // bf16 rows
 constexpr int kFmtFp8 = 1;     // E4M3FN rows, one fp32 scale per row
 constexpr int kFmtMx = 2;      // E4M3FN rows, one E8M0 exponent per 32 elements
+constexpr int kFmtMx4 = 3;     // E2M1 rows (two per byte), one E8M0 exponent per 32 elements
+
+// Cached bytes of a `width`-element row in format fmt (scales apart).
+__host__ __device__ constexpr int row_bytes(int fmt, int width) {
+  return fmt == kFmtBf16 ? 2 * width : fmt == kFmtMx4 ? width / 2 : width;
+}
 
 constexpr int kIndexerChunk = 2048;   // positions per indexer workgroup (bf16 keys)
-// fp8 keys are half the bytes: a workgroup takes twice the positions
+// one-byte and four-bit keys: a workgroup takes twice the positions
 // (measured: one round of workgroups streams fp8 keys best)
 __host__ __device__ constexpr int indexer_chunk(bool fp8) { return fp8 ? 2 * kIndexerChunk : kIndexerChunk; }
 constexpr int kSelectChunk = 4096;    // positions per select workgroup

@@ -112,7 +112,8 @@ def test_attention_rejects_bad_arguments(lib):
     assert call(b, kv=FAKE_ODD) == 1
     assert call(b, dt=1) == 1                  # fp8 without scales
     assert call(b, dt=2) == 1                  # MX without exponents
-    assert call(b, dt=3) == 2
+    assert call(b, dt=3) == 1
+    assert call(b, dt=4) == 2
 
 
 def test_forward_rejects_bad_arguments(lib):

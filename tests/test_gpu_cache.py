@@ -31,6 +31,9 @@ def _meta(lengths, tokens, starts=None):
 def _cache(rows, width, fmt):
     if fmt == "bf16":
         return torch.full((rows, width), SENT_BF16, dtype=torch.int16, device="cuda").view(torch.bfloat16), None
+    if fmt == "mx4":
+        return (torch.full((rows, width // 2), SENT_FP8, dtype=torch.uint8, device="cuda"),
+                torch.full((rows, width // 32), SENT_MX, dtype=torch.uint8, device="cuda"))
     data = torch.full((rows, width), SENT_FP8, dtype=torch.uint8, device="cuda").view(torch.float8_e4m3fn)
     if fmt == "mx":
         return data, torch.full((rows, width // 32), SENT_MX, dtype=torch.uint8, device="cuda")
@@ -51,7 +54,7 @@ def _check_cache(data, scale, fmt, expect, rows_to_check=None):
     rows = list(range(data.shape[0])) if rows_to_check is None else list(rows_to_check)
     bits = _bits(data, None if rows_to_check is None else rows)
     sc = None if scale is None else scale.cpu().numpy()
-    if fmt == "mx":
+    if fmt in ("mx", "mx4"):
         for i, r in enumerate(rows):
             if r in expect:
                 pay, ex = expect[r]
@@ -89,7 +92,7 @@ def _append(meta, cache_rows, latent, key, kv_fmt, key_fmt, max_len=None):
 def _oracle(meta, cache_rows, rows, fmt):
     seq, pos, starts, lens = meta
     bits = rows.view(torch.int16).numpy().view(np.uint16)
-    name = {"bf16": "bf16", "fp8": "e4m3fn", "mx": "mxfp8"}[fmt]
+    name = {"bf16": "bf16", "fp8": "e4m3fn", "mx": "mxfp8", "mx4": "mxfp4"}[fmt]
     return oracle.cache_append(seq, pos, starts, lens, cache_rows, bits, name)
 
 
@@ -104,7 +107,8 @@ def _run_and_check(meta, cache_rows, latent, key, kv_fmt, key_fmt, rows_to_check
 
 @pytest.mark.parametrize("kv_fmt,key_fmt", [("bf16", "bf16"), ("fp8", "fp8"), ("bf16", "fp8"),
                                             ("fp8", "bf16"), ("fp8", None), (None, "fp8"),
-                                            ("mx", "mx"), ("mx", "fp8"), ("bf16", "mx")])
+                                            ("mx", "mx"), ("mx", "fp8"), ("bf16", "mx"),
+                                            ("mx4", "mx4"), ("mx4", "bf16"), ("fp8", "mx4")])
 def test_ragged_batch(kv_fmt, key_fmt):
     lens = [37, 300, 5, 1000]
     toks = [(0, 0), (0, 36), (1, 299), (1, 150), (1, 0), (2, 4), (3, 999), (3, 998), (3, 500), (0, 17)]
@@ -119,7 +123,7 @@ def test_out_of_range_tokens_write_nothing():
     toks = [(0, 9), (-1, 3), (3, 0), (1, -1), (1, 20), (1, 19), (2, 14), (2, 15), (2, 29), (0, 0)]
     meta = _meta(lens, toks, starts)
     lat, key = si.append_rows(len(toks), seed=12)
-    for fmt in ("bf16", "fp8", "mx"):
+    for fmt in ("bf16", "fp8", "mx", "mx4"):
         expect = _oracle(meta, 60, lat, fmt)
         assert sorted(expect) == [0, 9, 29, 59], sorted(expect)      # the oracle's skip rules
         _run_and_check(meta, 60, lat, key, fmt, fmt, what=f"skips {fmt}")
@@ -157,7 +161,7 @@ def test_edge_values():
     key = lat[:, :128].contiguous()
     T = lat.shape[0]
     meta = _meta([T], [(0, p) for p in range(T)])
-    for fmt in ("bf16", "fp8", "mx"):
+    for fmt in ("bf16", "fp8", "mx", "mx4"):
         _run_and_check(meta, T, lat, key, fmt, fmt, what=f"edge {fmt}")
 
 
@@ -168,12 +172,13 @@ def test_prefill_chunk():
     _run_and_check(meta, 8192, lat, key, "fp8", "fp8", what="prefill fp8")
     _run_and_check(meta, 8192, lat, key, "bf16", "bf16", what="prefill bf16")
     _run_and_check(meta, 8192, lat, key, "mx", "mx", what="prefill mx")
+    _run_and_check(meta, 8192, lat, key, "mx4", "mx4", what="prefill mx4")
 
 
-@pytest.mark.parametrize("cfg", [2, 4, 5])
+@pytest.mark.parametrize("cfg", [2, 4, 5, 6])
 def test_full_size_decode(cfg):
     # the long-context decode shapes: 16 x 131072 bf16, 8 x 262144 fp8 or MX; one new row per sequence
-    B, S, fmt = {2: (16, 131072, "bf16"), 4: (8, 262144, "fp8"), 5: (8, 262144, "mx")}[cfg]
+    B, S, fmt = {2: (16, 131072, "bf16"), 4: (8, 262144, "fp8"), 5: (8, 262144, "mx"), 6: (8, 262144, "mx4")}[cfg]
     meta = _meta([S] * B, [(b, S - 1) for b in range(B)])
     lat, key = si.append_rows(B, seed=20 + cfg)
     rows = B * S
@@ -214,3 +219,4 @@ def test_mx_edge_blocks():
     T = lat.shape[0]
     meta = _meta([T], [(0, p) for p in range(T)])
     _run_and_check(meta, T, lat, key, "mx", "mx", what="mx edge blocks")
+    _run_and_check(meta, T, lat, key, "mx4", "mx4", what="mx4 edge blocks")

@@ -11,7 +11,7 @@ from gpu_helpers import Dev, assert_lse_close, assert_out_close, run_oracle, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 4, 5, 6])
 def test_decode_workload_full(cfg):
     wl = si.config(cfg)
     say(f"[full] {wl.name}: T={wl.num_tokens} B={wl.num_seqs} max_len={wl.max_len} fp8={wl.fp8}")

@@ -278,3 +278,36 @@ def test_prefill_mx():
     pos = sorted(rng.choice(4200, size=70, replace=False).tolist())
     wl = si.build("prefill_mx", [4200], [(0, p) for p in pos], seed=24, mx=True)
     _check_forward(wl)
+
+
+def test_mx4_caches_small():
+    wl = si.build("mx4_small", [3000, 2100], [(0, 2999), (1, 2099), (0, 1000)], seed=25, mx4=True)
+    _check_forward(wl)
+
+
+def test_mx4_index_scores_exact():
+    wl = si.build("mx4_scores", [2500, 700], [(0, 2499), (1, 699), (0, 31)], seed=26, mx4=True)
+    say("[index_scores] four-bit MX keys")
+    dev = Dev(wl)
+    s = dev.scores().cpu().numpy()
+    ref = run_oracle(wl, keep_scores=True)
+    for i, r in enumerate(ref["scores"]):
+        n = r.shape[0]
+        assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
+
+
+def test_mx4_attention_given_indices():
+    wl = si.build("mx4_attn", [3000], [(0, 2999), (0, 2047)], seed=27, mx4=True)
+    say("[attention] four-bit MX rows, oracle indices")
+    dev = Dev(wl)
+    ref = run_oracle(wl)
+    out, lse = dev.attention(torch.from_numpy(ref["indices"]).cuda())
+    assert_out_close(out.cpu().numpy(), ref["out"], False, "mx4 attention")
+    assert_lse_close(lse.cpu().numpy(), ref["lse"], "mx4 attention")
+
+
+def test_prefill_mx4():
+    rng = np.random.default_rng(28)
+    pos = sorted(rng.choice(4200, size=70, replace=False).tolist())
+    wl = si.build("prefill_mx4", [4200], [(0, p) for p in pos], seed=28, mx4=True)
+    _check_forward(wl)
