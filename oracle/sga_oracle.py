@@ -72,6 +72,16 @@ elements with e - 127 = floor(log2(max|x|)) - 2 (2 = exponent of E2M1's
 largest value, 6 = 1.5 * 2^2), clamped and zero-block handled as above;
 elements nearest-even, saturating at 6.
 
+Sparse indexer loss (technical report abstract: the indexer is warmed up
+against its own sparse top-k selection rather than the dense attention
+distribution; fact sheet, Training: an indexer-only sparse warmup, then joint
+training with the indexer loss down-weighted). The loss form is not printed;
+the reading taken is the DSA-style one restricted to the selected set S_t of
+query t: the target p_t is the main attention's distribution over S_t,
+averaged over the heads (each head's softmax of its logits over S_t), the
+indexer's distribution q_t is the softmax of its scores over S_t, and the loss
+is KL(p_t || q_t) = sum_s p_t[s] (log p_t[s] - log q_t[s]), one value per query.
+
 Output epilogue (fact sheet facts: value dimension per head 128; hidden state
 7,168; the gate sits on the attention output before o_proj). In the absorbed
 form the attention output of head h stays in the 512-wide latent space; the
@@ -93,7 +103,8 @@ __all__ = ["decode_bf16", "e4m3fn_table", "decode_e4m3fn", "Store", "index_score
            "select_topk", "sparse_mla", "sigmoid_gate", "forward", "D_LATENT",
            "encode_e4m3fn", "quantize_rows_e4m3fn", "cache_append", "e8m0_table", "MX_BLOCK",
            "quantize_blocks_mxfp8", "decode_mxfp8", "D_V", "output_projection",
-           "e2m1_table", "encode_e2m1", "quantize_blocks_mxfp4", "decode_mxfp4"]
+           "e2m1_table", "encode_e2m1", "quantize_blocks_mxfp4", "decode_mxfp4",
+           "sparse_indexer_loss", "indexer_loss"]
 
 D_LATENT = 512
 D_V = 128        # value dimension per head (fact sheet)
@@ -401,3 +412,38 @@ def output_projection(o: np.ndarray, w_uv: np.ndarray, w_o: np.ndarray) -> np.nd
     for h in range(H):
         u[:, h, :] = o[:, h, :] @ np.asarray(w_uv[h], dtype=np.float64).T
     return u.reshape(T, H * D_V) @ np.asarray(w_o, dtype=np.float64).T
+
+
+def sparse_indexer_loss(q_abs: np.ndarray, rows: np.ndarray, sm_scale: float,
+                        scores_sel: np.ndarray) -> float:
+    """KL(p || q) over one query's selected rows: p is the head-mean of each
+    head's attention softmax over the rows (logits sm_scale * q_abs[h] . row),
+    q the softmax of the indexer scores of the same rows. q_abs [H, 576],
+    rows [m, 576], scores_sel [m]. An empty selection gives 0."""
+    if rows.shape[0] == 0:
+        return 0.0
+    z = sm_scale * (np.asarray(q_abs, dtype=np.float64) @ np.asarray(rows, dtype=np.float64).T)   # [H, m]
+    ph = np.exp(z - z.max(axis=1, keepdims=True))
+    ph /= ph.sum(axis=1, keepdims=True)
+    p = ph.mean(axis=0)
+    i = np.asarray(scores_sel, dtype=np.float64)
+    log_q = i - (i.max() + np.log(np.exp(i - i.max()).sum()))
+    pos = p > 0
+    return float(np.sum(p[pos] * (np.log(p[pos]) - log_q[pos])))
+
+
+def indexer_loss(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store: "Store", q_abs,
+                 kv_store: "Store", k: int, sm_scale: float, tokens: Optional[Sequence[int]] = None):
+    """The sparse indexer loss of each token: its scores, its top-k set, then
+    sparse_indexer_loss over that set. Returns float64 [T] (or [len(tokens)])."""
+    sel = range(len(token_seq)) if tokens is None else tokens
+    out = []
+    for t in sel:
+        b, p = int(token_seq[t]), int(token_pos[t])
+        n = min(p + 1, int(seq_len[b]))
+        base = int(seq_start[b])
+        scores = index_scores(q_idx[t], w[t], k_store.rows(np.arange(base, base + n)))
+        idx = select_topk(scores, k)
+        idx = idx[idx >= 0]
+        out.append(sparse_indexer_loss(q_abs[t], kv_store.rows(base + idx), sm_scale, scores[idx]))
+    return np.asarray(out, dtype=np.float64)

@@ -613,6 +613,37 @@ def check_output_projection_selection(orc):
     assert np.array_equal(y, ref)
 
 
+def check_indexer_loss_worked_example(orc):
+    g = _golden("indexer_loss_worked_example.json")
+    rows = np.zeros((2, 576))
+    rows[:, 0] = g["rows_col0"]
+    q = np.zeros((2, 576))
+    q[:, 0] = g["q_col0"]
+    got = orc.sparse_indexer_loss(q, rows, 1.0, np.array(g["scores"]))
+    assert abs(got - g["loss"]) < 1e-14, got
+
+
+def check_indexer_loss_properties(orc):
+    """KL against torch's kl_div on the same distributions; zero when the
+    indexer's softmax equals the target; invariant to a shift of the scores and
+    to the order of the selected rows; non-negative."""
+    rng = np.random.default_rng(15)
+    H, m = 64, 300
+    q = rng.standard_normal((H, 576))
+    rows = rng.standard_normal((m, 576)) / 24
+    sc = rng.standard_normal(m) * 3
+    tau = 1 / math.sqrt(192)
+    got = orc.sparse_indexer_loss(q, rows, tau, sc)
+    zt = torch.from_numpy(tau * q @ rows.T)
+    p = torch.softmax(zt, dim=1).mean(dim=0)
+    ref = torch.nn.functional.kl_div(torch.log_softmax(torch.from_numpy(sc), 0), p, reduction="sum").item()
+    assert abs(got - ref) < 1e-12 * max(1.0, abs(ref)) and got >= 0
+    assert abs(orc.sparse_indexer_loss(q, rows, tau, np.log(p.numpy()) + 7.0)) < 1e-12
+    assert abs(orc.sparse_indexer_loss(q, rows, tau, sc + 100.0) - got) < 1e-12
+    perm = rng.permutation(m)
+    assert abs(orc.sparse_indexer_loss(q, rows[perm], tau, sc[perm]) - got) < 1e-12
+
+
 ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_example,
               check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
               check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
@@ -622,4 +653,5 @@ ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_exampl
               check_mxfp8_worked_example, check_mxfp8_brute_force, check_mxfp8_scale_invariance,
               check_forward_mxfp8_store, check_output_projection_unabsorbed,
               check_output_projection_selection, check_e2m1_table, check_mxfp4_worked_example,
-              check_mxfp4_brute_force, check_mxfp4_scale_invariance, check_forward_mxfp4_store]
+              check_mxfp4_brute_force, check_mxfp4_scale_invariance, check_forward_mxfp4_store,
+              check_indexer_loss_worked_example, check_indexer_loss_properties]

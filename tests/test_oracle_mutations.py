@@ -167,6 +167,27 @@ def _mx4_exponent_like_fp8(x):
 
 _ORIG_MX4 = base.quantize_blocks_mxfp4
 
+
+def _loss_reversed_kl(q_abs, rows, sm_scale, scores_sel):
+    # KL(q || p) instead of KL(p || q)
+    z = sm_scale * (np.asarray(q_abs, float) @ np.asarray(rows, float).T)
+    ph = np.exp(z - z.max(axis=1, keepdims=True))
+    p = (ph / ph.sum(axis=1, keepdims=True)).mean(axis=0)
+    i = np.asarray(scores_sel, float)
+    qd = np.exp(i - i.max())
+    qd /= qd.sum()
+    return float(np.sum(qd * (np.log(qd) - np.log(p))))
+
+
+def _loss_pooled_logits(q_abs, rows, sm_scale, scores_sel):
+    # one softmax of the head-mean logits instead of the mean of per-head softmaxes
+    z = (sm_scale * (np.asarray(q_abs, float) @ np.asarray(rows, float).T)).mean(axis=0)
+    p = np.exp(z - z.max())
+    p /= p.sum()
+    i = np.asarray(scores_sel, float)
+    log_q = i - (i.max() + np.log(np.exp(i - i.max()).sum()))
+    return float(np.sum(p * (np.log(p) - log_q)))
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -188,6 +209,8 @@ MUTANTS = {
     "proj_heads_value_major": dict(output_projection=_proj_value_major),
     "mx4_nibbles_swapped": dict(quantize_blocks_mxfp4=_mx4_nibbles_swapped),
     "mx4_exponent_offset_8": dict(quantize_blocks_mxfp4=_mx4_exponent_like_fp8),
+    "loss_reversed_kl": dict(sparse_indexer_loss=_loss_reversed_kl),
+    "loss_pooled_logits": dict(sparse_indexer_loss=_loss_pooled_logits),
 }
 
 
