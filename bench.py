@@ -214,6 +214,32 @@ def time_output_proj(wl, out, ev, reps: int) -> dict:
             "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
 
 
+def time_indexer_loss(wl, s, idx, lse, ev, reps: int) -> dict:
+    """Times sga_indexer_loss over the step's selection (indices and lse of the
+    last step, the scores from sga_index_scores), the same way as the cache append."""
+    dev = idx.device
+    T = wl.num_tokens
+    scores = torch.empty((T, wl.max_len), dtype=torch.float32, device=dev)
+    sga.sga_index_scores(s["batch"], s["q_idx"], s["w"], s["k_idx"], s["k_idx_scale"], scores)
+    loss = torch.empty((T,), dtype=torch.float32, device=dev)
+    ws = sga.workspace(sga.sga_indexer_loss_workspace_size(T, wl.k), dev)
+    run = lambda: sga.sga_indexer_loss(s["batch"], s["q_abs"], s["kv"], s["kv_scale"], idx, wl.k,
+                                       wl.sm_scale, lse, scores, loss, ws=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+    torch.cuda._sleep(5_000_000)
+    for a, b in pairs:
+        ev.record(a, stream)
+        run()
+        ev.record(b, stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    return {"us": round(us, 2), "mean_loss": round(float(loss.mean().item()), 6)}
+
+
 # ---------------------------------------------------------------- traffic
 def src_digest() -> str:
     h = hashlib.sha256()
@@ -388,8 +414,12 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    append = time_cache_append(wl, sets[0], ev, reps=20)
+    # around the step, after it: the indexer loss over the last step's selection
+    # (input set (K - 1) % copies), the output epilogue of its output, then the
+    # cache append (which writes into the caches, so it comes last)
+    loss = time_indexer_loss(wl, sets[(K - 1) % len(sets)], idx, lse, ev, reps=10)
     proj = time_output_proj(wl, out, ev, reps=10)
+    append = time_cache_append(wl, sets[0], ev, reps=20)
     idx_ms = [ev.elapsed_ms(tr[i].indexer_begin, tr[i].indexer_end) for i in range(K)]
     topk_ms = [ev.elapsed_ms(tr[i].indexer_end, tr[i].topk_end) for i in range(K)]
     attn_ms = [ev.elapsed_ms(tr[i].topk_end, tr[i].attn_end) for i in range(K)]
@@ -429,7 +459,8 @@ def main():
                   "attention_us": round(float(np.mean(attn_ms)) * 1e3, 2),
                   "input_copies": len(sets),
                   "cache_append": append,
-                  "output_proj": proj},
+                  "output_proj": proj,
+                  "indexer_loss": loss},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -259,6 +259,31 @@ SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, 
                                     void* k_idx_scale, sga_dtype k_idx_dtype, hipStream_t stream);
 
 /*
+ * sga_indexer_loss: the sparse indexer loss of each token.
+ * Source: the technical report abstract (the indexer is warmed up against its
+ * own sparse top-k selection rather than the dense attention distribution)
+ * and the fact sheet's Training section (an indexer-only sparse warmup, then
+ * joint training with the indexer loss down-weighted). The loss form is not
+ * printed; this is the DSA-style reading restricted to the selected set.
+ *
+ * For token t let S = the entries j of indices[t*k ..] with 0 <= j < n_t.
+ *   p[j] = (1/64) sum_h exp(z_h,j - lse[t*64+h]),  z_h,j = sm_scale * q_abs[t,h,:] . row_j
+ *   q[j] = exp(scores[t*ld + j]) / sum_{i in S} exp(scores[t*ld + i])
+ *   loss[t] = sum_{j in S, p[j] > 0} p[j] * (log p[j] - log q[j])     (KL(p || q))
+ * lse must be the attention's own output for the same indices (then p sums to
+ * one over S); scores are sga_index_scores' output ([T, ld], ld >= max_len).
+ * A token with S empty gets loss 0. q_abs, kv, kv_scale, kv_dtype, indices,
+ * k and sm_scale are as for sga_sparse_mla_attn. fp32 throughout.
+ *   ws >= sga_indexer_loss_workspace_size(T, k) bytes.
+ */
+SGA_API size_t sga_indexer_loss_workspace_size(int32_t num_tokens, int32_t k);
+SGA_API sga_status sga_indexer_loss(const sga_batch* batch, const void* q_abs, const void* kv,
+                                    const void* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
+                                    int32_t k, float sm_scale, const float* lse, const float* scores,
+                                    int64_t ld, float* loss, void* ws, size_t ws_bytes,
+                                    hipStream_t stream);
+
+/*
  * sga_output_proj: the output epilogue after the gate, for T tokens.
  * Source: the fact sheet's attention facts (value dimension per head 128;
  * hidden state 7,168; the head-specific gate acts on the attention output

@@ -25,6 +25,7 @@ HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK, D_V = 64, 64, 128, 512, 576, 128
 EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_workspace_size",
            "sga_sparse_mla_attn", "sga_forward_workspace_size", "sga_forward",
            "sga_cache_append", "sga_output_proj_workspace_size", "sga_output_proj",
+           "sga_indexer_loss_workspace_size", "sga_indexer_loss",
            "sga_status_string", "sga_version")
 
 
@@ -75,6 +76,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
                          vp, vp, vp, sz, tp, vp], ctypes.c_int),
         "sga_cache_append": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp], ctypes.c_int),
         "sga_output_proj_workspace_size": ([i32, i32], sz),
+        "sga_indexer_loss_workspace_size": ([i32, i32], sz),
+        "sga_indexer_loss": ([bp, vp, vp, vp, ctypes.c_int, vp, i32, f32, vp, vp, i64, vp, vp, sz, vp],
+                             ctypes.c_int),
         "sga_output_proj": ([i32, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int),
         "sga_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sga_version": ([], ctypes.c_int),
@@ -309,3 +313,26 @@ def sga_output_proj(o_latent, w_uv, w_o, y, ws: Optional[torch.Tensor] = None) -
     _raise("sga_output_proj", load().sga_output_proj(
         T, _ptr(o_latent), _ptr(w_uv), _ptr(w_o), d_model, _ptr(y), _ptr(ws), ws.numel(),
         _stream(o_latent)))
+
+
+def sga_indexer_loss_workspace_size(num_tokens: int, k: int) -> int:
+    return int(load().sga_indexer_loss_workspace_size(num_tokens, k))
+
+
+def sga_indexer_loss(batch: Batch, q_abs, kv, kv_scale, indices, k: int, sm_scale: float, lse,
+                     scores, loss, ws: Optional[torch.Tensor] = None) -> None:
+    """loss[t] = KL(p || q) over token t's selected rows: p the head-mean attention
+    probabilities (with the attention's lse), q the softmax of the indexer scores."""
+    T = batch.num_tokens
+    _check(q_abs, "q_abs", (torch.bfloat16,), (T, HEADS, D_QK))
+    dt = _cache_dtype(kv, kv_scale, "kv", batch.cache_rows, D_QK)
+    _check(indices, "indices", (torch.int32,), (T, k))
+    _check(lse, "lse", (torch.float32,), (T, HEADS))
+    _check(scores, "scores", (torch.float32,), (T, None))
+    _check(loss, "loss", (torch.float32,), (T,))
+    if ws is None:
+        ws = workspace(sga_indexer_loss_workspace_size(T, k), q_abs.device)
+    b = batch.c()
+    _raise("sga_indexer_loss", load().sga_indexer_loss(
+        ctypes.byref(b), _ptr(q_abs), _ptr(kv), _ptr(kv_scale), dt, _ptr(indices), k, float(sm_scale),
+        _ptr(lse), _ptr(scores), scores.shape[1], _ptr(loss), _ptr(ws), ws.numel(), _stream(q_abs)))

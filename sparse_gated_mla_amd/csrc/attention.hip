@@ -327,12 +327,53 @@ __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, in
   }
 }
 
-template <int kFmt>
+// The probabilities variant, after the barrier: each selected row's head-mean
+// attention probability (1/64) sum_h exp(z_h - lse_h), with lse the
+// attention's own log-sum-exp over all selected rows (an input). The waves of
+// half 0 sum their 16 heads per row and post them; after a second barrier
+// the first 32 threads add the four head groups and write the tile's rows.
+template <bool kFp8>
+__device__ __forceinline__ void tile_probs(const float* __restrict__ flags,
+                                           const float* __restrict__ xbuf, float* __restrict__ psum,
+                                           const f32x4 (&part)[2], float zscale, float lse2,
+                                           float* __restrict__ prob_out, int nrows_left, int lane,
+                                           int wave) {
+  const int g = lane >> 4;
+  if (wave < 4) {
+    const f32x4* other = reinterpret_cast<const f32x4*>(xbuf + ((wave ^ 4) * 64 + lane) * 8);
+    const f32x4 full[2] = {part[0] + other[0], part[1] + other[1]};
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float rs = flags[16 * b + 4 * g + r];
+        float v = full[b][r] * zscale;
+        if constexpr (kFp8) v *= rs;
+        float e = rs < 0.0f ? 0.0f : __builtin_amdgcn_exp2f(v - lse2);
+        // sum over the 16 heads of this lane group
+        e += __shfl_xor(e, 1);
+        e += __shfl_xor(e, 2);
+        e += __shfl_xor(e, 4);
+        e += __shfl_xor(e, 8);
+        if ((lane & 15) == 0) psum[wave * kAttnTileRows + 16 * b + 4 * g + r] = e;
+      }
+  }
+  __syncthreads();
+  if (threadIdx.x < kAttnTileRows && (int)threadIdx.x < nrows_left) {
+    const int r = threadIdx.x;
+    const float sum = psum[r] + psum[kAttnTileRows + r] + psum[2 * kAttnTileRows + r] +
+                      psum[3 * kAttnTileRows + r];
+    prob_out[r] = sum * (1.0f / kHeads);
+  }
+}
+
+template <int kFmt, bool kProbs>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   constexpr bool kRowScale = kFmt == kFmtFp8;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tile[3][kRegionBytes];
   __shared__ float lds_flags[3][kAttnTileRows];
   __shared__ __attribute__((aligned(16))) float xbuf[2][kAttnWaves * 64 * 8];
+  __shared__ float psum[kProbs ? 2 : 1][kProbs ? 4 * kAttnTileRows : 1];
   using Stage = RowStage<kFmt>;
   const int t = blockIdx.y, split = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -375,6 +416,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < 16; ++db) st.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
   const float zscale = a.sm_scale * kLog2e;
+  float lse2 = 0.0f;   // the head's log-sum-exp in base 2 (probabilities variant)
+  if constexpr (kProbs) lse2 = a.lse_in[(int64_t)t * kHeads + head] * kLog2e;
 
   // tile 0 into region 0; its stage is refilled with tile 2
   s0.store(lds_tile[0], lds_flags[0]);
@@ -395,15 +438,22 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     f32x4 part[2];
     if (i < ntiles) tile_partial_logits(tile, xbuf[i & 1], qb, lane, wave, half, part);
     __syncthreads();
-    if (i < ntiles)
-      tile_finish<kRowScale>(tile, lds_flags[cur], xbuf[i & 1], st, part, zscale, lane, wave, half);
+    if constexpr (kProbs) {
+      if (i < ntiles)
+        tile_probs<kRowScale>(lds_flags[cur], xbuf[i & 1], psum[i & 1], part, zscale, lse2,
+                              a.probs + (int64_t)t * a.k + j_begin + i * kAttnTileRows,
+                              nrows - i * kAttnTileRows, lane, wave);
+    } else {
+      if (i < ntiles)
+        tile_finish<kRowScale>(tile, lds_flags[cur], xbuf[i & 1], st, part, zscale, lane, wave, half);
+    }
     cur = nxt;
   };
   for (int i = 0; i < ntiles; i += 2) {
     step(s1, i);
     step(s0, i + 1);
   }
-  finish_half(a, st, t, split, head, lane, half);
+  if constexpr (!kProbs) finish_half(a, st, t, split, head, lane, half);
 }
 
 // Merges the split partials by log-sum-exp, then gates. One workgroup per
@@ -456,15 +506,84 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
   if (a.lse && db == 0 && q == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
+// The sparse indexer loss of one token: KL(p || q) over its selected rows,
+// p the head-mean attention probabilities (from the probabilities variant),
+// q the softmax of the indexer scores over the same rows. One workgroup per
+// token: the scores' maximum, their log-sum-exp, then the KL sum.
+__device__ __forceinline__ float block_reduce(float v, float* red, bool take_max) {
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float w = __shfl_xor(v, o);
+    v = take_max ? fmaxf(v, w) : v + w;
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float r = red[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = take_max ? fmaxf(r, red[w]) : r + red[w];
+  return r;
+}
+
+__global__ __launch_bounds__(256) void indexer_loss_kernel(LossArgs a) {
+  __shared__ float red[4];
+  const int t = blockIdx.x;
+  int64_t base;
+  int n;
+  a.batch.token(t, base, n);
+  const int32_t* idx = a.indices + (int64_t)t * a.k;
+  const float* sc = a.scores + (int64_t)t * a.ld;
+  const float* pr = a.probs + (int64_t)t * a.k;
+  float m = -INFINITY;
+  for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
+    const int s = idx[j];
+    if (s >= 0 && s < n) m = fmaxf(m, sc[s]);
+  }
+  m = block_reduce(m, red, true);
+  if (m == -INFINITY) {   // nothing selected
+    if (threadIdx.x == 0) a.loss[t] = 0.0f;
+    return;
+  }
+  float z = 0.0f;
+  for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
+    const int s = idx[j];
+    if (s >= 0 && s < n) z += expf(sc[s] - m);
+  }
+  const float lse = m + logf(block_reduce(z, red, false));
+  float kl = 0.0f;
+  for (int j = threadIdx.x; j < a.k; j += blockDim.x) {
+    const int s = idx[j];
+    const float p = pr[j];
+    if (s >= 0 && s < n && p > 0.0f) kl += p * (logf(p) - (sc[s] - lse));
+  }
+  kl = block_reduce(kl, red, false);
+  if (threadIdx.x == 0) a.loss[t] = kl;
+}
+
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid(a.splits, a.num_tokens);
-  if (fmt == kFmtFp8) attn_kernel<kFmtFp8><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx) attn_kernel<kFmtMx><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4><<<grid, kAttnThreads, 0, s>>>(a);
-  else attn_kernel<kFmtBf16><<<grid, kAttnThreads, 0, s>>>(a);
+  if (fmt == kFmtFp8) attn_kernel<kFmtFp8, false><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx) attn_kernel<kFmtMx, false><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4, false><<<grid, kAttnThreads, 0, s>>>(a);
+  else attn_kernel<kFmtBf16, false><<<grid, kAttnThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_probs(const AttnArgs& a, int fmt, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  dim3 grid(a.splits, a.num_tokens);
+  if (fmt == kFmtFp8) attn_kernel<kFmtFp8, true><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx) attn_kernel<kFmtMx, true><<<grid, kAttnThreads, 0, s>>>(a);
+  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4, true><<<grid, kAttnThreads, 0, s>>>(a);
+  else attn_kernel<kFmtBf16, true><<<grid, kAttnThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_indexer_loss(const LossArgs& a, hipStream_t s) {
+  if (a.num_tokens == 0) return hipSuccess;
+  indexer_loss_kernel<<<a.num_tokens, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

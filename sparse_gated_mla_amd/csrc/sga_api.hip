@@ -13,6 +13,7 @@ using sga::AttnArgs;
 using sga::BatchView;
 using sga::CacheArgs;
 using sga::ProjArgs;
+using sga::LossArgs;
 using sga::IndexerArgs;
 using sga::TopkArgs;
 using sga::TopkCtrl;
@@ -456,6 +457,59 @@ SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, 
   a.k_idx_scale = do_key ? k_idx_scale : nullptr;
   a.k_idx_fmt = do_key ? (int)k_idx_dtype : sga::kFmtBf16;
   return hip_status(sga::launch_cache_append(a, stream));
+}
+
+SGA_API size_t sga_indexer_loss_workspace_size(int32_t num_tokens, int32_t k) {
+  if (num_tokens <= 0 || k <= 0) return 0;
+  Carver c(nullptr);
+  c.take<float>((size_t)num_tokens * k);
+  return c.used;
+}
+
+SGA_API sga_status sga_indexer_loss(const sga_batch* batch, const void* q_abs, const void* kv,
+                                    const void* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
+                                    int32_t k, float sm_scale, const float* lse, const float* scores,
+                                    int64_t ld, float* loss, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+  SGA_TRY(check_batch(batch));
+  if (k < 1) return SGA_ERR_INVALID_ARG;
+  if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
+  if (!isfinite(sm_scale)) return SGA_ERR_INVALID_ARG;
+  if (batch->num_tokens == 0) return SGA_OK;
+  if (!q_abs || !indices || !lse || !scores || !loss || !aligned16(q_abs)) return SGA_ERR_INVALID_ARG;
+  if (ld < batch->max_len) return SGA_ERR_INVALID_ARG;
+  SGA_TRY(check_store(kv, kv_scale, kv_dtype, 1));
+  const size_t need = sga_indexer_loss_workspace_size(batch->num_tokens, k);
+  if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
+  Carver c(ws);
+  float* probs = c.take<float>((size_t)batch->num_tokens * k);
+  const AttnPlan plan = plan_attention(batch->num_tokens, k);
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.batch = view_of(batch);
+  a.num_tokens = batch->num_tokens;
+  a.q_abs = static_cast<const uint16_t*>(q_abs);
+  a.kv = static_cast<const uint8_t*>(kv);
+  a.kv_scale = kv_scale;
+  a.indices = indices;
+  a.k = k;
+  a.sm_scale = sm_scale;
+  a.splits = plan.splits;
+  a.rows_per_split = plan.rows_per_split;
+  a.lse_in = lse;
+  a.probs = probs;
+  SGA_HIP(sga::launch_attention_probs(a, (int)kv_dtype, stream));
+  LossArgs l;
+  l.batch = a.batch;
+  l.num_tokens = batch->num_tokens;
+  l.indices = indices;
+  l.k = k;
+  l.scores = scores;
+  l.ld = ld;
+  l.probs = probs;
+  l.loss = loss;
+  SGA_HIP(sga::launch_indexer_loss(l, stream));
+  return SGA_OK;
 }
 
 SGA_API size_t sga_output_proj_workspace_size(int32_t num_tokens, int32_t d_model) {

@@ -88,6 +88,21 @@ struct AttnArgs {
   uint16_t* part_o;        // [T,splits,32 column blocks,64 heads,16] fp16, normalised
   float* part_ml;          // [T,splits,64,4]: max logit (base 2), exp-sum, output scale of
                            // columns 0..255 and of columns 256..511
+  // probabilities variant (sparse indexer loss)
+  const float* lse_in;     // [T,64] natural log-sum-exp of each head over the selected rows
+  float* probs;            // [T,k] head-mean probability of each selected row
+};
+
+// Sparse indexer loss per token from the head-mean probabilities.
+struct LossArgs {
+  BatchView batch;
+  int num_tokens;
+  const int32_t* indices;  // [T,k]
+  int k;
+  const float* scores;     // [T,ld] indexer scores
+  int64_t ld;
+  const float* probs;      // [T,k]
+  float* loss;             // [T]
 };
 
 // Cache append: token t writes row seq_start[b] + p of each given cache.
@@ -149,5 +164,7 @@ int topk_token_lds_cap(int64_t words);       // 0: use the multi-kernel top-k
 hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_probs(const AttnArgs& a, int fmt, hipStream_t s);
+hipError_t launch_indexer_loss(const LossArgs& a, hipStream_t s);
 
 }  // namespace sga

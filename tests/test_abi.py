@@ -28,7 +28,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("sga_index_scores", "sga_topk", "sga_sparse_mla_attn", "sga_forward", "sga_cache_append",
-              "sga_output_proj"):
+              "sga_output_proj", "sga_indexer_loss"):
         assert n in names
 
 
@@ -181,6 +181,32 @@ def test_output_proj_rejects_bad_arguments(lib):
     assert call(T=0, o=None, uv=None, wo=None, y=None, ws=None, nb=0) == 0
     assert lib.sga_output_proj_workspace_size(16, 7168) >= 16 * 8192 * 4
     assert lib.sga_output_proj_workspace_size(0, 7168) == 0
+
+
+def test_indexer_loss_rejects_bad_arguments(lib):
+    b = _batch()
+    need = lib.sga_indexer_loss_workspace_size(2, 8)
+    assert need >= 2 * 8 * 4
+
+    def call(bb=b, q=FAKE, kv=FAKE, sc=None, dt=0, idx=FAKE, k=8, tau=0.07, lse=FAKE, s=FAKE,
+             ld=100, loss=FAKE, ws=FAKE, nb=need):
+        return lib.sga_indexer_loss(ctypes.byref(bb), q, kv, sc, dt, idx, k, tau, lse, s, ld, loss,
+                                    ws, nb, None)
+    assert call(k=0) == 1
+    assert call(k=(1 << 16) + 1) == 2
+    assert call(tau=math.nan) == 1
+    assert call(q=None) == 1
+    assert call(q=FAKE_ODD) == 1
+    assert call(idx=None) == 1
+    assert call(lse=None) == 1
+    assert call(s=None) == 1
+    assert call(loss=None) == 1
+    assert call(ld=50) == 1
+    assert call(dt=1) == 1                     # fp8 without scales
+    assert call(dt=9) == 2
+    assert call(ws=None) == 3
+    assert call(nb=need - 1) == 3
+    assert call(bb=_batch(T=0, ptr=0), q=None, idx=None, lse=None, s=None, loss=None) == 0
 
 
 def test_workspace_sizes_grow_with_the_problem(lib):
