@@ -225,11 +225,11 @@ sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* 
 
 // ---------------------------------------------------------------- output epilogue
 // Splits of K: the largest divisor of the chunk count that keeps the grid
-// within about four workgroups per CU.
+// within about two workgroups per CU (measured best from 16 to 256 rows).
 int proj_splits(int64_t tiles, int chunks) {
   int best = 1;
   for (int s = 1; s <= chunks; ++s)
-    if (chunks % s == 0 && tiles * s <= 1024) best = s;
+    if (chunks % s == 0 && tiles * s <= 512) best = s;
   return best;
 }
 
