@@ -375,7 +375,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float xbuf[2][kAttnWaves * 64 * 8];
   __shared__ float psum[kProbs ? 2 : 1][kProbs ? 4 * kAttnTileRows : 1];
   using Stage = RowStage<kFmt>;
-  const int t = blockIdx.y, split = blockIdx.x;
+  const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int t = wg / a.splits, split = wg % a.splits;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = wave >> 2;
   const int head = 16 * (wave & 3) + (lane & 15);
@@ -464,7 +465,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 constexpr int kCombineRound = 16;
 
 __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a) {
-  const int db = blockIdx.x, t = blockIdx.y;
+  const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
+  const int db = wg % (kDLatent / 16), t = wg / (kDLatent / 16);
   const int h = threadIdx.x >> 2, q = threadIdx.x & 3;
   const int S = a.splits;
   const int64_t th = (int64_t)t * kHeads + h;

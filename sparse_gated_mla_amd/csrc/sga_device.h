@@ -158,4 +158,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// The dispatcher deals workgroups to the chip's 8 XCDs round-robin by linear
+// id, and each XCD has its own L2. This maps linear id b (of `total`) to an
+// index whose consecutive values run on one XCD: XCD x gets indices
+// x*per + min(x, rem) + 0, 1, ..., so workgroups that share input (the splits
+// of one token share its query) read it through one L2.
+__device__ __forceinline__ int xcd_grouped(int b, int total) {
+  constexpr int kXcds = 8;
+  const int per = total / kXcds, rem = total % kXcds;
+  const int x = b % kXcds, j = b / kXcds;
+  return x * per + min(x, rem) + j;
+}
+
 }  // namespace sga
