@@ -39,15 +39,13 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 // ---------------------------------------------------------------- conversions
-// Four OCP E4M3FN bytes -> four bf16 (exact: every E4M3 value is a bf16 value),
-// packed two per dword.
+// Four OCP E4M3FN bytes -> four bf16, packed two per dword: the scaled
+// conversion (v_cvt_scalef32_pk_bf16_fp8) with scale 1, two instructions for
+// four values. Exact: every E4M3FN value, subnormals included, is a bf16 normal.
 __device__ __forceinline__ u32x2 e4m3x4_to_bf16x4(uint32_t packed) {
-  f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, false);
-  f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)packed, true);
   u32x2 r;
-  // keep the upper 16 bits of each fp32 (exact for E4M3 values)
-  r.x = __builtin_amdgcn_perm(__float_as_uint(lo.y), __float_as_uint(lo.x), 0x07060302u);
-  r.y = __builtin_amdgcn_perm(__float_as_uint(hi.y), __float_as_uint(hi.x), 0x07060302u);
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, true));
   return r;
 }
 
