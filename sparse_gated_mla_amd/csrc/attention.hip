@@ -52,6 +52,7 @@ constexpr int kRowStride = kDQK + 8;  // bf16 elements per LDS row (1168 B)
 constexpr int kRegionBytes = kAttnTileRows * kRowStride * 2;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyMax = 8.0f;  // base-2 headroom of the running max (probabilities <= 256)
 constexpr int kNonTemporal = 2;   // cache-policy bit: rows are read once per token
 constexpr int kRsrcWord3 = 0x00020000;
 
@@ -220,11 +221,14 @@ __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
       z[b][r] = rs < 0.0f ? -INFINITY : v;
       tmax = fmaxf(tmax, z[b][r]);
     }
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-  tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-  const float m_new = fmaxf(st.m_run, tmax);
-  const float alpha = (st.m_run == -INFINITY) ? (m_new == -INFINITY ? 1.0f : 0.0f)
-                                              : __builtin_amdgcn_exp2f(st.m_run - m_new);
+  tmax = max_xor32(max_xor16(tmax));
+  // The running max moves only when the tile's max passes it by more than
+  // kLazyMax (base 2): the probabilities then stay below 2^kLazyMax and the
+  // accumulators are rescaled only on such a jump. Any reference point gives
+  // the same softmax, as o and l share it; (m, l) record it for the merge.
+  const float m_new = tmax > st.m_run + kLazyMax ? tmax : st.m_run;
+  const float alpha = (st.m_run == -INFINITY || m_new == st.m_run)
+                          ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
   float p[2][4];
   float psum = 0.0f;
 #pragma unroll
@@ -243,19 +247,10 @@ __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
     for (int db = 0; db < 16; ++db) st.o[db] *= alpha;
   }
   // probabilities as bf16 hi/lo B operands: k-slot 8g+i <-> row 4g+i (i<4), 16+4g+i-4
-  uint32_t hi_b[8], lo_b[8];
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t h = f32_to_bf16_rne(p[b][r]);
-      hi_b[4 * b + r] = h;
-      lo_b[4 * b + r] = f32_to_bf16_rne(p[b][r] - __uint_as_float(h << 16));
-    }
-  const u32x4 phi = {hi_b[0] | (hi_b[1] << 16), hi_b[2] | (hi_b[3] << 16),
-                     hi_b[4] | (hi_b[5] << 16), hi_b[6] | (hi_b[7] << 16)};
-  const u32x4 plo = {lo_b[0] | (lo_b[1] << 16), lo_b[2] | (lo_b[3] << 16),
-                     lo_b[4] | (lo_b[5] << 16), lo_b[6] | (lo_b[7] << 16)};
+  uint32_t lo[4];
+  const u32x4 phi = {split_bf16x2(p[0][0], p[0][1], lo[0]), split_bf16x2(p[0][2], p[0][3], lo[1]),
+                     split_bf16x2(p[1][0], p[1][1], lo[2]), split_bf16x2(p[1][2], p[1][3], lo[3])};
+  const u32x4 plo = {lo[0], lo[1], lo[2], lo[3]};
   // transposed reads: lane s reads row 4(s/16) + (s%16)/4 [+16], columns 4(s%4) .. +3
   // of each 16-column block
   const int tr_row = 4 * (lane >> 4) + ((lane & 15) >> 2);
@@ -278,8 +273,7 @@ __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
 __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, int t, int split,
                                             int head, int lane, int half) {
   const int g = lane >> 4;
-  float l_tot = st.l_run + __shfl_xor(st.l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
+  const float l_tot = sum_xor32(sum_xor16(st.l_run));
   const int64_t th = (int64_t)t * kHeads + head;
   if (a.splits == 1) {
     const float gs = gate_factor(a.gate, th);
@@ -302,8 +296,7 @@ __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, in
   for (int db = 0; db < 16; ++db)
 #pragma unroll
     for (int r = 0; r < 4; ++r) amax = fmaxf(amax, fabsf(st.o[db][r]));
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  amax = max_xor32(max_xor16(amax));
   amax *= inv_l;
   const float scale = amax > 0.0f ? amax : 1.0f;
   const float k = inv_l / scale;

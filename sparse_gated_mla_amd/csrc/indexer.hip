@@ -186,7 +186,7 @@ __device__ __forceinline__ float score_tile(const uint8_t* lds, uint32_t sw, int
       sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
     }
   }
-  return sc + __shfl_xor(sc, 32);
+  return sum_xor32(sc);
 }
 
 // query heads as MFMA A operands: qa[mb][s] = q[32mb + l%32][64g + 8s .. +7]

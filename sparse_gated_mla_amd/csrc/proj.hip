@@ -69,13 +69,8 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs a) {
     for (int q = 0; q < kPerThread / 8; ++q) {
       uint32_t hi[4], lo[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x0 = av[2 * q + (j >> 1)][2 * (j & 1)], x1 = av[2 * q + (j >> 1)][2 * (j & 1) + 1];
-        const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-        hi[j] = h0 | (h1 << 16);
-        lo[j] = f32_to_bf16_rne(x0 - __uint_as_float(h0 << 16)) |
-                (f32_to_bf16_rne(x1 - __uint_as_float(h1 << 16)) << 16);
-      }
+      for (int j = 0; j < 4; ++j)
+        hi[j] = split_bf16x2(av[2 * q + (j >> 1)][2 * (j & 1)], av[2 * q + (j >> 1)][2 * (j & 1) + 1], lo[j]);
       *reinterpret_cast<u32x4*>(&lds_hi[buf][am][ak + 8 * q]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
       *reinterpret_cast<u32x4*>(&lds_lo[buf][am][ak + 8 * q]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
     }

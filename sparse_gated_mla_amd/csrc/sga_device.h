@@ -75,15 +75,35 @@ __device__ __forceinline__ u32x4 e2m1x8_scaled_to_bf16x8(uint32_t packed, float 
                __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, 3))};
 }
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// Two fp32 -> two bf16 packed low then high, round to nearest even
+// (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+// The bf16 hi/lo pair of two fp32 values x0, x1: x = hi + lo to about 16
+// significant bits. Returns the packed hi pair and stores the packed lo pair.
+__device__ __forceinline__ uint32_t split_bf16x2(float x0, float x1, uint32_t& lo) {
+  const uint32_t hi = pack_bf16x2(x0, x1);
+  lo = pack_bf16x2(x0 - __uint_as_float(hi << 16), x1 - __uint_as_float(hi & 0xFFFF0000u));
+  return hi;
+}
+
+// The max and the sum of x over the lane pairs (l, l ^ 16) and (l, l ^ 32):
+// v_permlane16_swap / v_permlane32_swap hand each lane both values of its
+// pair, in either order, without an LDS round trip.
+__device__ __forceinline__ f32x2 pair16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ f32x2 pair32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return f32x2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor16(float x) { const f32x2 p = pair16(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float max_xor32(float x) { const f32x2 p = pair32(x); return fmaxf(p.x, p.y); }
+__device__ __forceinline__ float sum_xor16(float x) { const f32x2 p = pair16(x); return p.x + p.y; }
+__device__ __forceinline__ float sum_xor32(float x) { const f32x2 p = pair32(x); return p.x + p.y; }
 
 // Two fp32 -> two IEEE fp16 (round to nearest even), packed low then high.
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
