@@ -155,23 +155,20 @@ struct KeyTile {
   }
 };
 
-// The head weights of a lane's accumulator rows: wv[2q + mb] = w[32mb + 8q +
-// 4g .. +3] (g = lane/32), read from the token's 64 weights in LDS.
-__device__ __forceinline__ void tile_weights(const float* lds_w, int lane, f32x4 (&wv)[8]) {
-  const int g = lane >> 5;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    wv[2 * q] = *reinterpret_cast<const f32x4*>(lds_w + 8 * q + 4 * g);
-    wv[2 * q + 1] = *reinterpret_cast<const f32x4*>(lds_w + 32 + 8 * q + 4 * g);
-  }
+// The head weights of a lane's accumulator rows: weight vector k = 2q + mb
+// holds w[32mb + 8q + 4g .. +3] (g = lane/32), read from the token's 64
+// weights in LDS.
+__device__ __forceinline__ f32x4 tile_weight(const float* lds_w, int lane, int k) {
+  return *reinterpret_cast<const f32x4*>(lds_w + 32 * (k & 1) + 8 * (k >> 1) + 4 * (lane >> 5));
 }
 
 // Scores one staged tile. Returns, in lanes 0..31, the score of tile row
-// `lane` (lanes 32..63 hold the same values). wv: the lane's head weights
-// (tile_weights). sw: the scale word of row lane % 32.
-template <int kFmt>
+// `lane` (lanes 32..63 hold the same values). wt(k): weight vector k of the
+// lane (tile_weight, or a copy held in registers). sw: the scale word of row
+// lane % 32.
+template <int kFmt, class Weights>
 __device__ __forceinline__ float score_tile(const uint8_t* lds, uint32_t sw, int lane,
-                                            const u32x4 (&qa)[2][8], const f32x4 (&wv)[8]) {
+                                            const u32x4 (&qa)[2][8], Weights wt) {
   u32x4 b[8];
   KeyTile<kFmt>::operands(lds, lane, sw, b);
   const float kscale = __uint_as_float(sw);
@@ -185,12 +182,13 @@ __device__ __forceinline__ float score_tile(const uint8_t* lds, uint32_t sw, int
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     // accumulator rows 4q..4q+3 of block mb are heads 32mb + 8q + 4g + 0..3
+    const f32x4 w0 = wt(2 * q), w1 = wt(2 * q + 1);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float d0 = acc0[4 * q + j], d1 = acc1[4 * q + j];
       if constexpr (kFmt == kFmtFp8) { d0 *= kscale; d1 *= kscale; }
-      sc = fmaf(wv[2 * q][j], fmaxf(d0, 0.0f), sc);
-      sc = fmaf(wv[2 * q + 1][j], fmaxf(d1, 0.0f), sc);
+      sc = fmaf(w0[j], fmaxf(d0, 0.0f), sc);
+      sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
     }
   }
   return sum_xor32(sc);
@@ -256,9 +254,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
         if (i + j < ngroups) {
           // scores go out as they are made: each is stored and counted while
           // the wave's later tiles are still in flight
-          f32x4 wv[8];
-          tile_weights(lds_w, lane, wv);
-          const float sc = score_tile<kFmt>(lds, ks, lane, qa, wv);
+          const float sc = score_tile<kFmt>(lds, ks, lane, qa,
+                                            [&](int k) { return tile_weight(lds_w, lane, k); });
           const int p = Tile::position(i + j, wave, lane);
           if (lane < 32 && p < len) {
             srow[p] = sc;
@@ -352,7 +349,8 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
     f32x4 wv[8];   // the token's head weights, held for the whole pass
     if (mine) {
       load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
-      tile_weights(lds_w[wave], lane, wv);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) wv[k] = tile_weight(lds_w[wave], lane, k);
     }
     float* srow = a.scores + (int64_t)t * a.ld;
     const int ntiles = (N + kTile - 1) / kTile;
@@ -383,7 +381,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
         __syncthreads();
         if (mine && i < ntiles) {
           const uint32_t ks = kFp8 ? lds_scale[i & 1][lane & 31] : 0u;
-          const float sc = score_tile<kFmt>(lds_tiles[i & 1], ks, lane, qa, wv);
+          const float sc = score_tile<kFmt>(lds_tiles[i & 1], ks, lane, qa, [&](int k) { return wv[k]; });
           // tile row r is position 32i + r in this layout
           const int p = i * kTile + lane;
           if (lane < 32 && p < n) {
