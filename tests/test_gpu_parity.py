@@ -142,6 +142,39 @@ def test_attention_skips_invalid_indices():
     assert_out_close(out.cpu().numpy(), np.stack(want), False, "poisoned indices")
 
 
+def test_attention_running_max_jumps():
+    # Rows planted in the later tiles of every split whose logits rise far
+    # above the rest (by about 15, 30 and 45, natural log, plus a per-split
+    # offset): each split's running max jumps after its first tile, so its
+    # accumulators are rescaled mid-split, and the merge of the splits meets
+    # very different maxima. The lift sits in the 64 RoPE columns, which enter
+    # the logits only, so the outputs keep their usual size.
+    n = 6000
+    wl = si.build("maxjump", [n], [(0, n - 1)], seed=42)
+    rng = np.random.default_rng(43)
+    sel = np.sort(rng.choice(n, size=wl.k, replace=False)).astype(np.int32)
+    q = wl.q_abs[0].double().numpy()
+    qsum = q[:, 512:].sum(axis=0)
+    unit = qsum / np.linalg.norm(qsum)                  # a RoPE direction every head's query favours
+    per_head = q[:, 512:] @ unit                        # logit per unit of length, before sm_scale
+    rows_per_split, tile = 128, 32                      # one token: 16 splits of 4 tiles
+    kv = wl.kv.clone()
+    for s in range(wl.k // rows_per_split):
+        for i, lift in ((1, 15.0), (2, 30.0), (3, 45.0)):
+            pos = int(sel[s * rows_per_split + i * tile + 7])
+            length = (lift + 2.0 * s) / (wl.sm_scale * float(per_head.mean()))
+            kv[pos, 512:] = torch.from_numpy(length * unit).to(torch.bfloat16)
+    wl.kv = kv
+    dev = Dev(wl)
+    say("[attention] running max jumps inside splits")
+    out, lse = dev.attention(torch.from_numpy(sel[None, :]).cuda())
+    _, vs = stores(wl)
+    o, l = oracle.sparse_mla(q, vs.rows(sel.astype(np.int64)), wl.sm_scale)
+    want = oracle.sigmoid_gate(o, wl.gate[0].double().numpy())
+    assert_out_close(out.cpu().numpy()[0], want, False, "max jumps")
+    assert_lse_close(lse.cpu().numpy()[0], l, "max jumps")
+
+
 def test_token_without_visible_rows():
     wl = si.build("novis", [50], [(0, 10), (0, 49)], seed=10)
     dev = Dev(wl)
