@@ -371,6 +371,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int t = wg / a.splits, split = wg % a.splits;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the two waves of a pair share a SIMD and leave each barrier together; the
+  // first gets the higher issue priority, so it reaches its value product while
+  // the second one still runs its softmax
+  if (wave < 4) __builtin_amdgcn_s_setprio(2);
   const int half = wave >> 2;
   const int head = 16 * (wave & 3) + (lane & 15);
   const int g = lane >> 4;

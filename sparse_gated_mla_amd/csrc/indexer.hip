@@ -299,6 +299,10 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
   __shared__ int32_t lds_n[kPfTokens];
   __shared__ int64_t lds_base[kPfTokens];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // waves w and w + 4 share a SIMD and leave each barrier together; the first
+  // gets the higher issue priority, so it finishes its MFMAs first and runs its
+  // epilogue while the second one's MFMAs are in the pipe
+  if (wave < 4) __builtin_amdgcn_s_setprio(2);
   const int t = blockIdx.x * kPfTokens + wave;
   const bool live = t < a.num_tokens;
   int64_t base = 0;
