@@ -308,7 +308,9 @@ __device__ __forceinline__ void finish_half(const AttnArgs& a, HalfState& st, in
     u32x2 packed;
     packed.x = pack_f16x2(v[0], v[1]);
     packed.y = pack_f16x2(v[2], v[3]);
-    *reinterpret_cast<u32x2*>(dst + db * (kHeads * 16)) = packed;
+    // streaming store: the partials are read once, by the merge, and little
+    // of them is left dirty in L2 when the kernel ends
+    __builtin_nontemporal_store(packed, reinterpret_cast<u32x2*>(dst + db * (kHeads * 16)));
   }
   if (g == 0) {
     float* ml = a.part_ml + 4 * (ts * kHeads + head);
