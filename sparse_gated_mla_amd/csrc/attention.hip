@@ -380,22 +380,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   const int half = wave >> 2;
   const int head = 16 * (wave & 3) + (lane & 15);
   const int g = lane >> 4;
-  int64_t base;
-  int n;
-  a.batch.token(t, base, n);
   const int j_begin = split * a.rows_per_split;
   const int nrows = max(0, min(a.k, j_begin + a.rows_per_split) - j_begin);
   const int ntiles = (nrows + kAttnTileRows - 1) / kAttnTileRows;
-
-  const uint32_t rows_bytes = (uint32_t)max(n, 0) * Stage::kRowBytes;
-  const rsrc_t rows = make_rsrc(a.kv + base * Stage::kRowBytes, rows_bytes);
-  const rsrc_t scales =
-      kFmt == kFmtFp8 ? make_rsrc(static_cast<const float*>(a.kv_scale) + base, (uint32_t)max(n, 0) * 4u)
-      : Stage::kMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
-                               (uint32_t)max(n, 0) * (kDQK / 32))
-                       : make_rsrc(a.kv, 0u);
   const rsrc_t idx_rs = make_rsrc(a.indices + (int64_t)t * a.k + j_begin, (uint32_t)nrows * 4u);
 
+  // the indices and the query do not depend on the batch metadata: their
+  // loads go out first and travel while the metadata's two scalar rounds run
   Stage s0, s1;
   s0.load_idx(idx_rs, 0);
   s1.load_idx(idx_rs, 1);
@@ -405,6 +396,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 9; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
   }
+  int64_t base;
+  int n;
+  a.batch.token(t, base, n);
+  const uint32_t rows_bytes = (uint32_t)max(n, 0) * Stage::kRowBytes;
+  const rsrc_t rows = make_rsrc(a.kv + base * Stage::kRowBytes, rows_bytes);
+  const rsrc_t scales =
+      kFmt == kFmtFp8 ? make_rsrc(static_cast<const float*>(a.kv_scale) + base, (uint32_t)max(n, 0) * 4u)
+      : Stage::kMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
+                               (uint32_t)max(n, 0) * (kDQK / 32))
+                       : make_rsrc(a.kv, 0u);
   s0.load_rows(rows, scales, 0, nrows, n);
   s0.load_idx(idx_rs, 2);
   s1.load_rows(rows, scales, 1, nrows, n);

@@ -149,6 +149,13 @@ __device__ __forceinline__ int visible_rows(int pos, int seq_len, int max_len,
   return n > 0 ? (int)n : 0;
 }
 
+// A load through the constant address space: data no kernel of the launch
+// writes, such as the batch metadata. Uniform addresses become scalar loads.
+template <class T>
+__device__ __forceinline__ T load_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 struct BatchView {
   const int32_t* token_seq;
   const int32_t* token_pos;
@@ -159,11 +166,21 @@ struct BatchView {
   int64_t cache_rows;
 
   // Resolves token t: first flat row of its sequence and its visible row count.
+  // Two rounds of loads at most, with no branch between them: the token's
+  // sequence and position, then the sequence's start and length (read for
+  // sequence 0 when the token's id is invalid, and then not used). With a
+  // workgroup-uniform t these are scalar loads, which leave the vector memory
+  // counter to loads the caller issued before.
   __device__ __forceinline__ void token(int t, int64_t& base, int& n) const {
-    int b = token_seq[t];
-    if (b < 0 || b >= num_seqs) { base = 0; n = 0; return; }
-    base = seq_start[b];
-    n = visible_rows(token_pos[t], seq_len[b], max_len, base, cache_rows);
+    if (num_seqs <= 0) { base = 0; n = 0; return; }
+    const int b = load_const(token_seq, t);
+    const int pos = load_const(token_pos, t);
+    const bool ok = b >= 0 && b < num_seqs;
+    const int bc = ok ? b : 0;
+    const int64_t start = load_const(seq_start, bc);
+    const int len = load_const(seq_len, bc);
+    base = ok ? start : 0;
+    n = ok ? visible_rows(pos, len, max_len, start, cache_rows) : 0;
   }
 };
 

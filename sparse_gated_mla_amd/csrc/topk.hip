@@ -62,22 +62,25 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t lds_count;
   constexpr int kSteps = kSelectChunk / kSelThreads;   // 64-position steps per wave
   const int t = blockIdx.y;
+  const int c0 = blockIdx.x * kSelectChunk;   // < max_len: the grid covers max_len
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const float* srow = a.scores + (int64_t)t * a.ld;
+  // the histogram first, then every score load of this workgroup, before the
+  // batch metadata (scalar loads): the cut is taken while the scores are still
+  // in flight. Scores past the token's visible rows (below max_len, inside the
+  // row) are read and then masked.
+  HistRun<kSelThreads, kHist1> h1;
+  h1.load(a.hist + (int64_t)t * kHist1);
+  const int c_end = min(a.batch.max_len, c0 + kSelectChunk);
+  float v[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) v[i] = srow[min(c0 + i * kSelThreads + wave * 64 + lane, c_end - 1)];
   int64_t base;
   int n;
   a.batch.token(t, base, n);
   if (n <= a.k) return;  // every visible position is kept; finalize writes them
-  const int c0 = blockIdx.x * kSelectChunk;
   if (c0 >= n) return;
   const int c1 = min(n, c0 + kSelectChunk);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const float* srow = a.scores + (int64_t)t * a.ld;
-  // the histogram first, then every score load of this workgroup: the cut is
-  // taken while the scores are still in flight
-  HistRun<kSelThreads, kHist1> h1;
-  h1.load(a.hist + (int64_t)t * kHist1);
-  float v[kSteps];
-#pragma unroll
-  for (int i = 0; i < kSteps; ++i) v[i] = srow[min(c0 + i * kSelThreads + wave * 64 + lane, c1 - 1)];
   if (threadIdx.x == 0) lds_count = 0;
   // first radix cut, taken redundantly by every workgroup of the token from the
   // histogram the previous kernel completed (no cross-workgroup hand-off)
@@ -146,6 +149,21 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   uint32_t* n_few = scratch + 40;   // short-list length, then the k-th key and ties kept
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // one round of loads, issued before the batch metadata (scalar loads): the
+  // cut, the slice counts, the digit-2 histogram and the first 4 * kFinThreads
+  // words of the selection bitmap, all inside this token's workspace rows
+  // (entries past the token's own are loaded and not used)
+  // (the cut as a per-lane vector load, lanes 0 and 1 reading its two words:
+  // a uniform scalar load would be sunk past the metadata's branch)
+  const uint32_t ctrl_word = (&a.ctrl[t].digit1)[threadIdx.x & 1];
+  uint32_t cnt = 0;
+  if (threadIdx.x < a.max_select_wgs) cnt = a.wg_count[(int64_t)t * a.max_select_wgs + threadIdx.x];
+  HistRun<kFinThreads, kHist2> h2;
+  h2.load(a.hist2 + (int64_t)t * kHist2);
+  const uint32_t* sel = a.sel + (int64_t)t * a.words;
+  uint32_t w[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) w[u] = sel[min(u * kFinThreads + (int)threadIdx.x, (int)a.words - 1)];
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -156,27 +174,20 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   }
   const int nsel = (n + kSelectChunk - 1) / kSelectChunk;
   const int words = (n + 31) >> 5;
-  // one round of loads: the cut, the slice counts, the digit-2 histogram and
-  // the selection bitmap
-  const uint32_t d1 = a.ctrl[t].digit1;
-  const uint32_t r1 = (uint32_t)a.k - a.ctrl[t].above1;  // still needed from the candidates
-  uint32_t cnt = 0;
-  if (threadIdx.x < nsel) cnt = a.wg_count[(int64_t)t * a.max_select_wgs + threadIdx.x];
-  HistRun<kFinThreads, kHist2> h2;
-  h2.load(a.hist2 + (int64_t)t * kHist2);
-  {
-    const uint32_t* sel = a.sel + (int64_t)t * a.words;
-    for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
-      uint32_t w[4];
+  const uint32_t d1 = __builtin_amdgcn_readlane(ctrl_word, 0);
+  const uint32_t r1 = (uint32_t)a.k - __builtin_amdgcn_readlane(ctrl_word, 1);  // still needed from the candidates
+  if ((int)threadIdx.x >= nsel) cnt = 0;
+  for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
+    if (i0 > 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) w[u] = sel[min(i0 + u * kFinThreads + (int)threadIdx.x, words - 1)];
+    }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int i = i0 + u * kFinThreads + threadIdx.x;
-        if (i < words) {
-          selL[i] = w[u];
-          tie[i] = 0;
-        }
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * kFinThreads + threadIdx.x;
+      if (i < words) {
+        selL[i] = w[u];
+        tie[i] = 0;
       }
     }
   }
