@@ -164,7 +164,8 @@ SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, c
  * The result is exact: it depends only on the score values, never on
  * rounding or scheduling. Scores must not be NaN; for NaN inputs the result is
  * unspecified but stays in bounds.
- *   scores  [T, ld] fp32 (only s < n_t read). indices [T, k] int32.
+ *   scores  [T, ld] fp32, ld >= max_len. Entries below max_len may be read;
+ *           only s < n_t affect the result. indices [T, k] int32.
  *   ws      >= sga_topk_workspace_size(T, max_len, k) bytes.
  */
 SGA_API size_t sga_topk_workspace_size(int32_t num_tokens, int32_t max_len, int32_t k);
