@@ -214,6 +214,14 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the head weights and the query need no batch metadata: their loads go
+  // out first (the weights first, so that the wait for them leaves the query
+  // in flight) and travel while the metadata's scalar rounds run
+  // (every thread loads, clamped: a branch here would make t divergent and
+  // turn the metadata's scalar loads into vector ones)
+  const float wt = a.w[(int64_t)t * kIdxHeads + min((int)threadIdx.x, kIdxHeads - 1)];
+  u32x4 qa[2][8];
+  load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -221,15 +229,13 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   if constexpr (kHist) {
     for (int b = threadIdx.x; b < kHist1; b += kThreads) lds_hist[b] = 0;
   }
-  if (threadIdx.x < kIdxHeads) lds_w[threadIdx.x] = a.w[(int64_t)t * kIdxHeads + threadIdx.x];
+  if (threadIdx.x < kIdxHeads) lds_w[threadIdx.x] = wt;
   __syncthreads();
 
   const int chunk0 = blockIdx.x * indexer_chunk(kFp8);
   const int len = min(n - chunk0, indexer_chunk(kFp8));   // positions of this chunk (<= 0: none)
   if (len > 0) {
     uint8_t* lds = lds_tiles + wave * kTileBytes;
-    u32x4 qa[2][8];
-    load_query(a.q_idx + (int64_t)t * kIdxHeads * kIdxDim, lane, qa);
 
     const rsrc_t keys = make_rsrc(a.k_idx + (base + chunk0) * Tile::kRowBytes,
                                   (uint32_t)len * Tile::kRowBytes);
