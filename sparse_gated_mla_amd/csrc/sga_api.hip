@@ -191,7 +191,7 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
     a.lds_cand_cap = token_cap;
     SGA_HIP(sga::launch_topk_token(a, stream));
   } else {
-    a.lds_cand_cap = sga::topk_finalize_lds_cap(L.words);
+    a.lds_cand_cap = 0;
     SGA_HIP(sga::launch_topk_select(a, stream));
     SGA_HIP(sga::launch_topk_finalize(a, stream));
   }

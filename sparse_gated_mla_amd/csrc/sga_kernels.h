@@ -68,7 +68,7 @@ struct TopkArgs {
   int64_t cand_cap;        // a multiple of kSelectChunk covering the longest context
   uint32_t* wg_count;      // [T,max_select_wgs] candidates each select workgroup wrote
   int max_select_wgs;
-  int lds_cand_cap;        // candidates the finalize kernel can stage in LDS
+  int lds_cand_cap;        // candidates the one-kernel top-k can stage in LDS
 };
 
 struct AttnArgs {
@@ -159,7 +159,6 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);
 constexpr size_t kFinalizeLds = 160 * 1024;  // dynamic LDS of the finalize kernels
 constexpr int64_t kMaxTokenWords = 8192;     // bitmap words for the one-kernel top-k (256K)
-int topk_finalize_lds_cap(int64_t words);
 int topk_token_lds_cap(int64_t words);       // 0: use the multi-kernel top-k
 hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s);

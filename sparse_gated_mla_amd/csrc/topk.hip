@@ -131,39 +131,56 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
 }
 
-// Dynamic LDS: staged output (4096 words) | level-3
-// histogram or short key list (256) | scratch (64) | slice offsets
-// (kMaxSelectWgs + 1) | tie bitmap (words) | selection bitmap (words) |
-// staged candidate positions (lds_cand_cap) | their keys (lds_cand_cap).
+// Dynamic LDS: staged output (4096 words) | level-3 histogram or short key
+// list (256) | scratch (64) | tie bitmap (words) | selection bitmap (words).
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
   constexpr int kFinWaves = kFinThreads / 64;
+  constexpr int kPreSlices = 4;   // slices per wave held in registers: 256K positions
   uint32_t* out_stage = lds;
   uint32_t* hist3 = out_stage + kHist2;
   uint32_t* scratch = hist3 + kHist3;
-  uint32_t* offs = scratch + 64;
-  uint32_t* tie = offs + kMaxSelectWgs + 1;
+  uint32_t* tie = scratch + 64;
   uint32_t* selL = tie + a.words;
-  uint32_t* lpos = selL + a.words;
-  uint32_t* lkey = lpos + a.lds_cand_cap;
   uint32_t* n_few = scratch + 40;   // short-list length, then the k-th key and ties kept
   const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // one round of loads, issued before the batch metadata (scalar loads): the
-  // cut, the slice counts, the digit-2 histogram and the first 4 * kFinThreads
-  // words of the selection bitmap, all inside this token's workspace rows
-  // (entries past the token's own are loaded and not used)
-  // (the cut as a per-lane vector load, lanes 0 and 1 reading its two words:
-  // a uniform scalar load would be sunk past the metadata's branch)
+  // One round of loads, issued before the batch metadata (scalar loads): the
+  // cut, the digit-2 histogram, the first 4 * kFinThreads words of the
+  // selection bitmap and, for wave w, the lengths of candidate slices
+  // w + q * kFinWaves (q < kPreSlices) with their first 128 entries. All lie
+  // inside this token's workspace rows; entries past the token's own are
+  // loaded and not used.
+  // (The cut is a per-lane vector load, lanes 0 and 1 reading its two words:
+  // a uniform scalar load would be sunk past the metadata's branch.)
   const uint32_t ctrl_word = (&a.ctrl[t].digit1)[threadIdx.x & 1];
-  uint32_t cnt = 0;
-  if (threadIdx.x < a.max_select_wgs) cnt = a.wg_count[(int64_t)t * a.max_select_wgs + threadIdx.x];
   HistRun<kFinThreads, kHist2> h2;
   h2.load(a.hist2 + (int64_t)t * kHist2);
   const uint32_t* sel = a.sel + (int64_t)t * a.words;
   uint32_t w[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) w[u] = sel[min(u * kFinThreads + (int)threadIdx.x, (int)a.words - 1)];
+  const uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap;
+  const uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap;
+  const uint32_t* wgc = a.wg_count + (int64_t)t * a.max_select_wgs;
+  // the wave index as a uniform value: branches on it stay scalar and leave t
+  // uniform (a divergent branch here would turn the metadata loads into
+  // vector loads)
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t clen[kPreSlices], cpos[kPreSlices][2], ckey[kPreSlices][2];
+#pragma unroll
+  for (int q = 0; q < kPreSlices; ++q) {
+    const int x = wv + q * kFinWaves;
+    clen[q] = 0;
+    if (x < a.max_select_wgs) {
+      const int64_t o = (int64_t)x * kSelectChunk + lane;
+      clen[q] = wgc[x];
+      cpos[q][0] = gpos[o];
+      ckey[q][0] = gkey[o];
+      cpos[q][1] = gpos[o + 64];
+      ckey[q][1] = gkey[o + 64];
+    }
+  }
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -176,7 +193,6 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   const int words = (n + 31) >> 5;
   const uint32_t d1 = __builtin_amdgcn_readlane(ctrl_word, 0);
   const uint32_t r1 = (uint32_t)a.k - __builtin_amdgcn_readlane(ctrl_word, 1);  // still needed from the candidates
-  if ((int)threadIdx.x >= nsel) cnt = 0;
   for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
     if (i0 > 0) {
 #pragma unroll
@@ -193,61 +209,52 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   }
   for (int b = threadIdx.x; b < kHist3; b += kFinThreads) hist3[b] = 0;
   if (threadIdx.x == 0) *n_few = 0;
-  // slice offsets: an inclusive scan of the counts by the first waves
-  static_assert(kMaxSelectWgs <= kFinThreads, "one count per thread");
-  {
-    const uint32_t x = wave_incl_scan(cnt);
-    uint32_t* wsum = scratch + 48;   // apart from what the cut uses next
-    if (lane == 63 && wave < (kMaxSelectWgs + 63) / 64) wsum[wave] = x;
-    __syncthreads();
-    if (threadIdx.x < kMaxSelectWgs) {
-      uint32_t before = 0;
-      for (int w2 = 0; w2 < wave; ++w2) before += wsum[w2];
-      offs[threadIdx.x + 1] = before + x;
-    }
-    if (threadIdx.x == 0) offs[0] = 0;
-  }
-  // level 2, from the histogram the select kernel counted
+  // level 2, from the histogram the select kernel counted (the cut's barriers
+  // also publish the LDS stores above)
   uint32_t d2, above2, n3;   // n3: candidates with digit d2, usually a handful
   h2.cut(r1, scratch, d2, above2, n3);
   const uint32_t r2 = r1 - above2;
-  const uint32_t m = offs[nsel];
-  const bool staged = m <= (uint32_t)a.lds_cand_cap;
-  const uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap;
-  const uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap;
 
-  // one pass over the slices: stage the candidates in LDS (when they fit) and
-  // gather level 3: the keys with digit d2 into a short list (at most 64) or
-  // their low 8 bits into a histogram
-  auto level3 = [&](uint32_t key) {
+  // Calls f(position, key) for every candidate of this wave's slices x = wave,
+  // wave + kFinWaves, ...: the first 128 entries of the first kPreSlices from
+  // registers, the rest from global memory, four per lane per round.
+  auto each_candidate = [&](auto&& f) {
+    auto from_global = [&](int x, uint32_t j0, uint32_t len) {
+      const uint32_t* sp = gpos + (int64_t)x * kSelectChunk;
+      const uint32_t* sk = gkey + (int64_t)x * kSelectChunk;
+      for (; j0 < len; j0 += 256) {
+        uint32_t pp[4], kk[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t j = min(j0 + 64 * u + lane, len - 1);
+          pp[u] = sp[j];
+          kk[u] = sk[j];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (j0 + 64 * u + lane < len) f(pp[u], kk[u]);
+      }
+    };
+#pragma unroll
+    for (int q = 0; q < kPreSlices; ++q) {
+      const int x = wv + q * kFinWaves;
+      if (x < nsel) {
+        const uint32_t len = clen[q];
+        if ((uint32_t)lane < len) f(cpos[q][0], ckey[q][0]);
+        if ((uint32_t)lane + 64 < len) f(cpos[q][1], ckey[q][1]);
+        from_global(x, 128, len);
+      }
+    }
+    for (int x = wv + kPreSlices * kFinWaves; x < nsel; x += kFinWaves) from_global(x, 0, wgc[x]);
+  };
+
+  // level 3: the keys with digit d2 into a short list (at most 64) or their
+  // low 8 bits into a histogram
+  each_candidate([&](uint32_t, uint32_t key) {
     if (((key >> kDigit3Bits) & (kHist2 - 1)) != d2) return;
     if (n3 <= 64) hist3[atomicAdd(n_few, 1u)] = key;
     else atomicAdd(&hist3[key & (kHist3 - 1)], 1u);
-  };
-  for (int x = wave; x < nsel; x += kFinWaves) {
-    const uint32_t o = offs[x], len = offs[x + 1] - o;
-    const uint32_t* sp = gpos + (int64_t)x * kSelectChunk;
-    const uint32_t* sk = gkey + (int64_t)x * kSelectChunk;
-    for (uint32_t j0 = 0; j0 < len; j0 += 128) {
-      const uint32_t ja = j0 + lane, jb = j0 + 64 + lane;
-      const uint32_t pa = sp[min(ja, len - 1)], ka = sk[min(ja, len - 1)];
-      const uint32_t pb = sp[min(jb, len - 1)], kb = sk[min(jb, len - 1)];
-      if (ja < len) {
-        if (staged) {
-          lpos[o + ja] = pa;
-          lkey[o + ja] = ka;
-        }
-        level3(ka);
-      }
-      if (jb < len) {
-        if (staged) {
-          lpos[o + jb] = pb;
-          lkey[o + jb] = kb;
-        }
-        level3(kb);
-      }
-    }
-  }
+  });
   __syncthreads();
   uint32_t kth, ties_kept;   // the k-th key and how many positions holding it to keep
   if (n3 <= 64) {
@@ -276,18 +283,9 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   }
 
   // candidates above the k-th key join the selection; ties at it are marked apart
-  auto mark = [&](uint32_t p, uint32_t key) {
+  each_candidate([&](uint32_t p, uint32_t key) {
     if (key >= kth) atomicOr(key > kth ? &selL[p >> 5] : &tie[p >> 5], 1u << (p & 31));
-  };
-  if (staged) {
-    for (uint32_t i = threadIdx.x; i < m; i += kFinThreads) mark(lpos[i], lkey[i]);
-  } else {
-    for (int x = wave; x < nsel; x += kFinWaves) {
-      const uint32_t len = offs[x + 1] - offs[x];
-      for (uint32_t j = lane; j < len; j += 64)
-        mark(gpos[(int64_t)x * kSelectChunk + j], gkey[(int64_t)x * kSelectChunk + j]);
-    }
-  }
+  });
   __syncthreads();
   // one ordered pass: thread j owns a run of words; it keeps every selected
   // position and the ties while fewer than ties_kept lower ties were kept
@@ -559,19 +557,13 @@ hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-int topk_finalize_lds_cap(int64_t words) {
-  const int64_t fixed = (int64_t)(kHist2 + kHist3 + 64 + kMaxSelectWgs + 1 + 2 * words) * (int64_t)sizeof(uint32_t);
-  const int64_t cap = ((int64_t)kFinalizeLds - fixed) / (2 * (int64_t)sizeof(uint32_t));
-  return cap > 0 ? (int)cap : 0;
-}
-
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   hipError_t e = hipFuncSetAttribute((const void*)topk_finalize_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + kMaxSelectWgs + 1 + 2 * a.words +
-                              2 * (int64_t)a.lds_cand_cap) * sizeof(uint32_t);
+  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + 2 * a.words) * sizeof(uint32_t);
+  if (lds > kFinalizeLds) return hipErrorInvalidValue;
   topk_finalize_kernel<<<a.num_tokens, kFinThreads, lds, s>>>(a);
   return hipGetLastError();
 }
