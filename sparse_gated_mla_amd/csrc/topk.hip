@@ -132,15 +132,19 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
 }
 
 // Dynamic LDS: staged output (4096 words) | level-3 histogram or short key
-// list (256) | scratch (64) | tie bitmap (words) | selection bitmap (words).
+// list (256) | scratch (64) | per-chunk selected and tie counts
+// (2 * kMaxSelectWgs) | tie bitmap (words) | selection bitmap (words).
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
   constexpr int kFinWaves = kFinThreads / 64;
   constexpr int kPreSlices = 4;   // slices per wave held in registers: 256K positions
+  constexpr int kChunkWords = kSelectChunk / 32;   // bitmap words of one select chunk
+  static_assert(kChunkWords == 128 && kMaxSelectWgs <= 128, "two words and two chunks per lane");
   uint32_t* out_stage = lds;
   uint32_t* hist3 = out_stage + kHist2;
   uint32_t* scratch = hist3 + kHist3;
-  uint32_t* tie = scratch + 64;
+  uint32_t* chunk_cnt = scratch + 64;
+  uint32_t* tie = chunk_cnt + 2 * kMaxSelectWgs;
   uint32_t* selL = tie + a.words;
   uint32_t* n_few = scratch + 40;   // short-list length, then the k-th key and ties kept
   const int t = blockIdx.x;
@@ -282,29 +286,20 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
     kth = (d1 << (32 - kDigit1Bits)) | (d2 << kDigit3Bits) | d3;
   }
 
-  // candidates above the k-th key join the selection; ties at it are marked apart
+  // Candidates above the k-th key join the selection; ties at it are marked
+  // apart. Slice x holds the candidates of bitmap chunk x (kChunkWords words,
+  // positions [x * kSelectChunk, (x + 1) * kSelectChunk)), so wave x mod
+  // kFinWaves marks only inside its own chunks.
   each_candidate([&](uint32_t p, uint32_t key) {
     if (key >= kth) atomicOr(key > kth ? &selL[p >> 5] : &tie[p >> 5], 1u << (p & 31));
   });
-  __syncthreads();
-  // one ordered pass: thread j owns a run of words; it keeps every selected
-  // position and the ties while fewer than ties_kept lower ties were kept
-  const int per = (words + kFinThreads - 1) / kFinThreads;
-  const int w0 = min(words, (int)threadIdx.x * per), w1 = min(words, w0 + per);
-  uint32_t ns = 0, nt = 0;
-  for (int i = w0; i < w1; ++i) {
-    ns += __popc(selL[i]);
-    nt += __popc(tie[i]);
-  }
-  uint32_t s_before, t_before;
-  block_excl_scan2<kFinThreads>(ns, nt, scratch, s_before, t_before);
-  uint32_t o = s_before + min(t_before, ties_kept);
-  uint32_t ties_seen = t_before;
   int32_t* staged_out = reinterpret_cast<int32_t*>(out_stage);   // k <= kHist2: the output goes out coalesced
   const bool stage_out = a.k <= kHist2;
-  for (int i = w0; i < w1; ++i) {
-    const uint32_t sbits = selL[i];
-    uint32_t tbits = tie[i];
+  // Keeps the selected positions of word i and its ties while fewer than
+  // ties_kept lower ties were kept; o is the output slot of the word's first
+  // kept position, ties_seen the ties before it.
+  auto emit_word = [&](int i, uint32_t sbits, uint32_t tbits_all, uint32_t& o, uint32_t& ties_seen) {
+    uint32_t tbits = tbits_all;
     if (ties_seen >= ties_kept) {
       tbits = 0;
     } else if (ties_seen + __popc(tbits) > ties_kept) {
@@ -316,7 +311,7 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
       }
       tbits = nb;
     }
-    ties_seen += __popc(tie[i]);
+    ties_seen += __popc(tbits_all);
     uint32_t bits = sbits | tbits;
     while (bits) {
       const int b = __ffs(bits) - 1;
@@ -327,6 +322,72 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
       }
       ++o;
     }
+  };
+  if (nsel >= kFinWaves) {
+    // Long contexts: the wave that marked a chunk also counts and emits it,
+    // with no barrier in between (a wave's LDS operations complete in order);
+    // lane l holds words 2l and 2l + 1 of the chunk. One barrier publishes the
+    // chunk counts.
+    auto chunk_words = [&](int x, uint32_t (&sw)[2], uint32_t (&tw)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = x * kChunkWords + 2 * lane + u;
+        sw[u] = i < words ? selL[i] : 0u;
+        tw[u] = i < words ? tie[i] : 0u;
+      }
+    };
+    for (int x = wv; x < nsel; x += kFinWaves) {
+      uint32_t sw[2], tw[2];
+      chunk_words(x, sw, tw);
+      const uint32_t ss = wave_incl_scan(__popc(sw[0]) + __popc(sw[1]));
+      const uint32_t ts = wave_incl_scan(__popc(tw[0]) + __popc(tw[1]));
+      if (lane == 63) {
+        chunk_cnt[x] = ss;
+        chunk_cnt[kMaxSelectWgs + x] = ts;
+      }
+    }
+    __syncthreads();
+    // the chunks' exclusive prefix sums, lane l holding chunks 2l and 2l + 1
+    const uint32_t cs0 = 2 * lane < nsel ? chunk_cnt[2 * lane] : 0u;
+    const uint32_t cs1 = 2 * lane + 1 < nsel ? chunk_cnt[2 * lane + 1] : 0u;
+    const uint32_t ct0 = 2 * lane < nsel ? chunk_cnt[kMaxSelectWgs + 2 * lane] : 0u;
+    const uint32_t ct1 = 2 * lane + 1 < nsel ? chunk_cnt[kMaxSelectWgs + 2 * lane + 1] : 0u;
+    const uint32_t cs_excl = wave_incl_scan(cs0 + cs1) - (cs0 + cs1);
+    const uint32_t ct_excl = wave_incl_scan(ct0 + ct1) - (ct0 + ct1);
+    for (int x = wv; x < nsel; x += kFinWaves) {
+      const int L = x >> 1;
+      uint32_t s_before = __builtin_amdgcn_readlane(cs_excl, L);
+      uint32_t t_before = __builtin_amdgcn_readlane(ct_excl, L);
+      if (x & 1) {
+        s_before += __builtin_amdgcn_readlane(cs0, L);
+        t_before += __builtin_amdgcn_readlane(ct0, L);
+      }
+      uint32_t sw[2], tw[2];
+      chunk_words(x, sw, tw);
+      const uint32_t s2 = __popc(sw[0]) + __popc(sw[1]), t2 = __popc(tw[0]) + __popc(tw[1]);
+      s_before += wave_incl_scan(s2) - s2;
+      t_before += wave_incl_scan(t2) - t2;
+      uint32_t o = s_before + min(t_before, ties_kept);
+      uint32_t ties_seen = t_before;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) emit_word(x * kChunkWords + 2 * lane + u, sw[u], tw[u], o, ties_seen);
+    }
+  } else {
+    // Short contexts (fewer chunks than waves): every thread takes a run of
+    // words, and a block scan gives each run its output slot.
+    __syncthreads();
+    const int per = (words + kFinThreads - 1) / kFinThreads;
+    const int w0 = min(words, (int)threadIdx.x * per), w1 = min(words, w0 + per);
+    uint32_t ns = 0, nt = 0;
+    for (int i = w0; i < w1; ++i) {
+      ns += __popc(selL[i]);
+      nt += __popc(tie[i]);
+    }
+    uint32_t s_before, t_before;
+    block_excl_scan2<kFinThreads>(ns, nt, scratch, s_before, t_before);
+    uint32_t o = s_before + min(t_before, ties_kept);
+    uint32_t ties_seen = t_before;
+    for (int i = w0; i < w1; ++i) emit_word(i, selL[i], tie[i], o, ties_seen);
   }
   if (stage_out) {
     __syncthreads();
@@ -562,7 +623,7 @@ hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)topk_finalize_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + 2 * a.words) * sizeof(uint32_t);
+  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + 2 * kMaxSelectWgs + 2 * a.words) * sizeof(uint32_t);
   if (lds > kFinalizeLds) return hipErrorInvalidValue;
   topk_finalize_kernel<<<a.num_tokens, kFinThreads, lds, s>>>(a);
   return hipGetLastError();
