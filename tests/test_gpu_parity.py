@@ -47,6 +47,41 @@ def test_topk_tiny_exact():
     assert np.array_equal(idx.cpu().numpy(), ref["indices"])
 
 
+def test_topk_ties_across_chunks():
+    # contexts of 61,439 to 131,072 positions on synthetic scores: from 16
+    # chunks of 4,096 positions on, the wave that marks a chunk's candidates
+    # also counts and emits it, and ties at the k-th score are kept by lowest
+    # position across chunk boundaries. Past each token's visible rows the
+    # scores are NaN and must not count.
+    wl = si.build("topk_ties", [70001, 131072],
+                  [(0, 70000), (1, 131071), (1, 100000), (1, 65535), (1, 61439)], seed=23)
+    say("[topk] ties across chunks, 61K-128K positions")
+    dev = Dev(wl)
+    rng = np.random.default_rng(23)
+    sc = np.full((wl.num_tokens, wl.max_len), np.nan, dtype=np.float32)
+    # token 0: low scores before 7,001; then zeros of both signs, and 500 high
+    # scores after it, so the kept ties run from 7,001 across the chunk edge at 8,192
+    n0 = 70001
+    s0 = np.where(rng.random(n0) < 0.5, np.float32(0.0), np.float32(-0.0)).astype(np.float32)
+    s0[:7001] = -1.0 - 2.0 * rng.random(7001)
+    s0[rng.choice(np.arange(7001, n0), 500, replace=False)] = 1.0 + rng.random(500)
+    sc[0, :n0] = s0
+    # token 1: every score equal
+    sc[1, :131072] = 0.5
+    # tokens 2-4: scores on a grid of 1/4, so the k-th score is shared by
+    # positions in every chunk (4: 15 chunks, below the threshold)
+    for t, n in ((2, 100001), (3, 65536), (4, 61440)):
+        sc[t, :n] = np.round(rng.standard_normal(n) * 4.0) / 4.0
+    idx = dev.topk(torch.from_numpy(sc).cuda()).cpu().numpy()
+    for t in range(wl.num_tokens):
+        n = int(np.sum(~np.isnan(sc[t])))
+        ref = oracle.select_topk(sc[t, :n].astype(np.float64), wl.k)
+        assert np.array_equal(idx[t], ref), f"token {t} (n={n})"
+    ties0 = idx[0][s0[idx[0]] == 0.0]   # kept zeros, either sign
+    assert ties0.min() < 8192 < ties0.max(), "the kept ties should cross a chunk edge"
+    assert idx[1].tolist() == list(range(2048))
+
+
 def test_attention_tiny_given_indices():
     wl = si.config(0)
     say("[attention] tiny decode, oracle indices")
