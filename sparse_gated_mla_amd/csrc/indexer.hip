@@ -162,6 +162,13 @@ __device__ __forceinline__ f32x4 tile_weight(const float* lds_w, int lane, int k
   return *reinterpret_cast<const f32x4*>(lds_w + 32 * (k & 1) + 8 * (k >> 1) + 4 * (lane >> 5));
 }
 
+// max(x, 0) in one integer instruction: read as a signed integer, every
+// negative float (-0 included) is negative and every positive one keeps its
+// order, so max(bits, 0) gives +0 for the former and x for the latter.
+// (fmaxf on an MFMA result costs a second instruction, which quiets a
+// signalling NaN first.)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 // Scores one staged tile. Returns, in lanes 0..31, the score of tile row
 // `lane` (lanes 32..63 hold the same values). wt(k): weight vector k of the
 // lane (tile_weight, or a copy held in registers). sw: the scale word of row
@@ -172,26 +179,43 @@ __device__ __forceinline__ float score_tile(const uint8_t* lds, uint32_t sw, int
   u32x4 b[8];
   KeyTile<kFmt>::operands(lds, lane, sw, b);
   const float kscale = __uint_as_float(sw);
+  // heads 0..31 first, then heads 32..63; the first block's ReLU and weighted
+  // sum are scheduled between the second block's MFMAs, so the vector ALU
+  // works while the matrix pipe runs
   f32x16 acc0 = {}, acc1 = {};
 #pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    acc0 = mfma32x32x16(qa[0][s], b[s], acc0);
-    acc1 = mfma32x32x16(qa[1][s], b[s], acc1);
-  }
-  float sc = 0.0f;
+  for (int s = 0; s < 8; ++s) acc0 = mfma32x32x16(qa[0][s], b[s], acc0);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc1 = mfma32x32x16(qa[1][s], b[s], acc1);
+  // accumulator rows 4q..4q+3 of block mb are heads 32mb + 8q + 4g + 0..3
+  float sc0 = 0.0f, sc1 = 0.0f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    // accumulator rows 4q..4q+3 of block mb are heads 32mb + 8q + 4g + 0..3
-    const f32x4 w0 = wt(2 * q), w1 = wt(2 * q + 1);
+    const f32x4 w0 = wt(2 * q);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float d0 = acc0[4 * q + j], d1 = acc1[4 * q + j];
-      if constexpr (kFmt == kFmtFp8) { d0 *= kscale; d1 *= kscale; }
-      sc = fmaf(w0[j], fmaxf(d0, 0.0f), sc);
-      sc = fmaf(w1[j], fmaxf(d1, 0.0f), sc);
+      float d0 = acc0[4 * q + j];
+      if constexpr (kFmt == kFmtFp8) d0 *= kscale;
+      sc0 = fmaf(w0[j], relu(d0), sc0);
     }
   }
-  return sum_xor32(sc);
+  __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);     // block 0's MFMAs
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA of block 1
+    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // then four VALU ops of block 0
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x4 w1 = wt(2 * q + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float d1 = acc1[4 * q + j];
+      if constexpr (kFmt == kFmtFp8) d1 *= kscale;
+      sc1 = fmaf(w1[j], relu(d1), sc1);
+    }
+  }
+  return sum_xor32(sc0 + sc1);
 }
 
 // query heads as MFMA A operands: qa[mb][s] = q[32mb + l%32][64g + 8s .. +7]
@@ -335,12 +359,17 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
 
   uint32_t done = 0;
   while (true) {
-    // the next sequence among the eight tokens, its tokens and their longest context
+    // the next sequence among the eight tokens, its tokens and their longest
+    // context. These come from LDS, so they are made uniform explicitly: the
+    // key buffer's descriptor then stays in scalar registers (a descriptor
+    // the compiler takes for divergent costs a readfirstlane loop around every
+    // load).
     int lead = -1;
     for (int g = 0; g < kPfTokens; ++g)
       if (lead < 0 && !((done >> g) & 1u) && lds_seq[g] >= 0) lead = g;
+    lead = __builtin_amdgcn_readfirstlane(lead);
     if (lead < 0) break;
-    const int seq = lds_seq[lead];
+    const int seq = __builtin_amdgcn_readfirstlane(lds_seq[lead]);
     uint32_t members = 0;
     int N = 0;
     for (int g = 0; g < kPfTokens; ++g)
@@ -348,9 +377,13 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
         members |= 1u << g;
         N = max(N, lds_n[g]);
       }
+    members = __builtin_amdgcn_readfirstlane(members);
+    N = __builtin_amdgcn_readfirstlane(N);
     done |= members;
     const bool mine = (members >> wave) & 1u;
-    const int64_t sbase = lds_base[lead];
+    const int64_t base_l = lds_base[lead];
+    const int64_t sbase = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(base_l >> 32)) << 32) |
+                                    (uint32_t)__builtin_amdgcn_readfirstlane((int)base_l));
     const rsrc_t keys = make_rsrc(a.k_idx + sbase * Tile::kRowBytes, (uint32_t)N * Tile::kRowBytes);
     const rsrc_t scales = make_rsrc(
         kFp8 ? (const void*)(static_cast<const uint32_t*>(a.k_scale) + sbase) : (const void*)a.k_idx,
@@ -379,19 +412,21 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
     };
 #pragma unroll
     for (int j = 0; j < kPfStages; ++j) issue(j, j);
+    static_assert(kPfStages % 2 == 0, "tile i uses LDS slot i & 1 == j & 1");
     for (int i0 = 0; i0 < ntiles; i0 += kPfStages) {
 #pragma unroll
       for (int j = 0; j < kPfStages; ++j) {
         const int i = i0 + j;
+        const int slot = j & 1;   // == i & 1, known at compile time
         // slot i & 1 was last read two tiles ago, before the previous barrier
-        if (loader) *reinterpret_cast<u32x4*>(&lds_tiles[i & 1][lds_off]) = stv[j];
+        if (loader) *reinterpret_cast<u32x4*>(&lds_tiles[slot][lds_off]) = stv[j];
         if constexpr (kFp8)
-          if (scale_loader) lds_scale[i & 1][threadIdx.x - kUnits] = sts[j];
+          if (scale_loader) lds_scale[slot][threadIdx.x - kUnits] = sts[j];
         issue(j, i + kPfStages);
         __syncthreads();
         if (mine && i < ntiles) {
-          const uint32_t ks = kFp8 ? lds_scale[i & 1][lane & 31] : 0u;
-          const float sc = score_tile<kFmt>(lds_tiles[i & 1], ks, lane, qa, [&](int k) { return wv[k]; });
+          const uint32_t ks = kFp8 ? lds_scale[slot][lane & 31] : 0u;
+          const float sc = score_tile<kFmt>(lds_tiles[slot], ks, lane, qa, [&](int k) { return wv[k]; });
           // tile row r is position 32i + r in this layout
           const int p = i * kTile + lane;
           if (lane < 32 && p < n) {
