@@ -124,7 +124,9 @@ struct RowStage {
   }
 
   // Stores the tile into an LDS region (bf16 rows of kRowStride elements) and
-  // each row's flag: its scale (fp8), 1 (bf16, MX), or -1 for a skipped row.
+  // each row's flags: flags[r] is the bias added to the row's logit (0, or
+  // -inf for a skipped row, whose zero data then gives a -inf logit), and for
+  // fp8 flags[kAttnTileRows + r] is the row's scale (0 for a skipped row).
   __device__ __forceinline__ void store(uint8_t* region, float* flags) const {
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -159,7 +161,11 @@ struct RowStage {
           dst[0] = u32x4{a0.x, a0.y, a1.x, a1.y};
           dst[1] = u32x4{a2.x, a2.y, a3.x, a3.y};
         }
-        if (c == 0) flags[r] = (ok >> q) & 1u ? (kFmt == kFmtFp8 ? __uint_as_float(s[q]) : 1.0f) : -1.0f;
+        if (c == 0) {
+          const bool real = (ok >> q) & 1u;
+          flags[r] = real ? 0.0f : -INFINITY;
+          if constexpr (kFmt == kFmtFp8) flags[kAttnTileRows + r] = real ? __uint_as_float(s[q]) : 0.0f;
+        }
       }
     }
   }
@@ -197,8 +203,8 @@ __device__ __forceinline__ void tile_partial_logits(const uint16_t* __restrict__
 }
 
 // Second half of a tile, after the barrier: the full logits (own partial plus
-// the partner's), the online softmax and the value product. flags[r] is the
-// row's scale (fp8), 1 (bf16, MX), or negative for a skipped row.
+// the partner's), the online softmax and the value product. flags: the rows'
+// logit biases (0, or -inf for a skipped row) and, for fp8, their scales.
 template <bool kFp8>
 __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
                                             const float* __restrict__ flags,
@@ -214,11 +220,13 @@ __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float rs = flags[16 * b + 4 * g + r];
-      rsc[b][r] = rs;
-      float v = full[b][r] * zscale;
-      if constexpr (kFp8) v *= rs;
-      z[b][r] = rs < 0.0f ? -INFINITY : v;
+      const int row = 16 * b + 4 * g + r;
+      float v = full[b][r];
+      if constexpr (kFp8) {
+        rsc[b][r] = flags[kAttnTileRows + row];
+        v *= rsc[b][r];
+      }
+      z[b][r] = fmaf(v, zscale, flags[row]);
       tmax = fmaxf(tmax, z[b][r]);
     }
   tmax = max_xor32(max_xor16(tmax));
@@ -229,15 +237,18 @@ __device__ __forceinline__ void tile_finish(const uint16_t* __restrict__ tile,
   const float m_new = tmax > st.m_run + kLazyMax ? tmax : st.m_run;
   const float alpha = (st.m_run == -INFINITY || m_new == st.m_run)
                           ? 1.0f : __builtin_amdgcn_exp2f(st.m_run - m_new);
+  // exp2(-inf - m) = 0 gives the skipped rows; a max that is still -inf (every
+  // row so far skipped) is replaced by 0, so no -inf - -inf arises
+  const float m_ref = m_new == -INFINITY ? 0.0f : m_new;
   float p[2][4];
   float psum = 0.0f;
 #pragma unroll
   for (int b = 0; b < 2; ++b)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float e = (z[b][r] == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(z[b][r] - m_new);
+      float e = __builtin_amdgcn_exp2f(z[b][r] - m_ref);
       psum += e;
-      if constexpr (kFp8) e *= fmaxf(rsc[b][r], 0.0f);
+      if constexpr (kFp8) e *= rsc[b][r];
       p[b][r] = e;
     }
   st.l_run = st.l_run * alpha + psum;
@@ -341,10 +352,10 @@ __device__ __forceinline__ void tile_probs(const float* __restrict__ flags,
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float rs = flags[16 * b + 4 * g + r];
+        const int row = 16 * b + 4 * g + r;
         float v = full[b][r] * zscale;
-        if constexpr (kFp8) v *= rs;
-        float e = rs < 0.0f ? 0.0f : __builtin_amdgcn_exp2f(v - lse2);
+        if constexpr (kFp8) v *= flags[kAttnTileRows + row];
+        float e = flags[row] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(v - lse2);
         // sum over the 16 heads of this lane group
         e += __shfl_xor(e, 1);
         e += __shfl_xor(e, 2);
@@ -366,7 +377,7 @@ template <int kFmt, bool kProbs>
 __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   constexpr bool kRowScale = kFmt == kFmtFp8;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tile[3][kRegionBytes];
-  __shared__ float lds_flags[3][kAttnTileRows];
+  __shared__ __attribute__((aligned(16))) float lds_flags[3][2 * kAttnTileRows];
   __shared__ __attribute__((aligned(16))) float xbuf[2][kAttnWaves * 64 * 8];
   __shared__ float psum[kProbs ? 2 : 1][kProbs ? 4 * kAttnTileRows : 1];
   using Stage = RowStage<kFmt>;
