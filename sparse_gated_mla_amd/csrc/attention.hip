@@ -54,14 +54,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLazyMax = 8.0f;  // base-2 headroom of the running max (probabilities <= 256)
 constexpr int kNonTemporal = 2;   // cache-policy bit: rows are read once per token
-constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
-}
 
 __device__ __forceinline__ float gate_factor(const float* gate, int64_t idx) {
   if (!gate) return 1.0f;

@@ -43,14 +43,7 @@ constexpr int kTile = 32;
 // key tiles in flight per wave (more did not help the fp8 variant)
 constexpr int kStages = 3;
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer: 32-bit data format, no swizzle
 constexpr int kNonTemporal = 2;         // cache-policy bit: streaming (read-once) data
-
-// A buffer resource over [p, p + bytes): loads past the end return zeros.
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
-}
 
 // A wave's key tile: 32 rows of one 128-row group of the chunk. The four
 // waves share each group: load step s of wave w reads the 1 KiB block

@@ -38,6 +38,15 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// ---------------------------------------------------------------- buffer loads
+// A gfx9 raw buffer resource over [p, p + bytes) (32-bit data format, no
+// swizzle): loads past the end return zeros, and offsets are 32-bit.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, kRsrcWord3);
+}
+
 // ---------------------------------------------------------------- conversions
 // Four OCP E4M3FN bytes -> four bf16, packed two per dword: the scaled
 // conversion (v_cvt_scalef32_pk_bf16_fp8) with scale 1, two instructions for

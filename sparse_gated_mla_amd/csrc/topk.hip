@@ -71,10 +71,11 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   // row) are read and then masked.
   HistRun<kSelThreads, kHist1> h1;
   h1.load(a.hist + (int64_t)t * kHist1);
-  const int c_end = min(a.batch.max_len, c0 + kSelectChunk);
+  const rsrc_t srs = make_rsrc(srow + c0, (uint32_t)(min(a.batch.max_len, c0 + kSelectChunk) - c0) * 4u);
   float v[kSteps];
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) v[i] = srow[min(c0 + i * kSelThreads + wave * 64 + lane, c_end - 1)];
+  for (int i = 0; i < kSteps; ++i)
+    v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (i * kSelThreads + wave * 64 + lane) * 4, 0, 0));
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -405,9 +406,10 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
 constexpr int kTokThreads = 1024;
 constexpr int kTokWaves = kTokThreads / 64;
 constexpr int kTokUnroll = 16;   // score loads in flight per lane
+constexpr int kTokenHalfLdsMinCand = 2048;   // staged candidates that justify half the LDS
 static_assert(kHist1 == kHist2, "one LDS histogram serves both levels");
 
-__global__ __launch_bounds__(kTokThreads) void topk_token_kernel(TopkArgs a) {
+__global__ __launch_bounds__(kTokThreads) __attribute__((amdgpu_waves_per_eu(8, 8))) void topk_token_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
   const int C = a.lds_cand_cap;
   uint32_t* hist = lds;
@@ -448,13 +450,21 @@ __global__ __launch_bounds__(kTokThreads) void topk_token_kernel(TopkArgs a) {
   const uint32_t r1 = (uint32_t)a.k - res[1];   // still needed from the candidates
   __syncthreads();
 
-  // 2. one pass over the scores: 64-position groups, kTokUnroll per lane in flight
+  // 2. one pass over the scores: 64-position groups in batches of kTokUnroll
+  // per lane; the next batch's loads are in flight while a batch is
+  // classified
   const int ngroups = (n + 63) >> 6;
-  for (int gb = 0; gb < ngroups; gb += kTokWaves * kTokUnroll) {
-    float v[kTokUnroll];
+  constexpr int kBatch = kTokWaves * kTokUnroll;   // groups per batch
+  // buffer loads: positions past n read zeros (and are masked below), and no
+  // 64-bit address is formed per load
+  const rsrc_t srs = make_rsrc(srow, (uint32_t)n * 4u);
+  auto load_batch = [&](int gb, float (&v)[kTokUnroll]) {
 #pragma unroll
     for (int u = 0; u < kTokUnroll; ++u)
-      v[u] = srow[min(((gb + u * kTokWaves + wave) << 6) + lane, n - 1)];
+      v[u] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+          srs, (((gb + u * kTokWaves + wave) << 6) + lane) * 4, 0, 0));
+  };
+  auto classify = [&](int gb, const float (&v)[kTokUnroll]) {
 #pragma unroll
     for (int u = 0; u < kTokUnroll; ++u) {
       const int gidx = gb + u * kTokWaves + wave;
@@ -484,6 +494,17 @@ __global__ __launch_bounds__(kTokThreads) void topk_token_kernel(TopkArgs a) {
           }
         }
       }
+    }
+  };
+  {
+    float va[kTokUnroll], vb[kTokUnroll];
+    load_batch(0, va);
+    for (int gb = 0; gb < ngroups; gb += 2 * kBatch) {
+      if (gb + kBatch < ngroups) load_batch(gb + kBatch, vb);
+      classify(gb, va);
+      if (gb + kBatch >= ngroups) break;
+      if (gb + 2 * kBatch < ngroups) load_batch(gb + 2 * kBatch, va);
+      classify(gb + kBatch, vb);
     }
   }
   __syncthreads();
@@ -597,6 +618,11 @@ hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {
 int topk_token_lds_cap(int64_t words) {
   if (words > kMaxTokenWords) return 0;
   const int64_t fixed = (int64_t)(kHist1 + 32 + 2 * words) * (int64_t)sizeof(uint32_t);
+  // two workgroups per CU when half the LDS still stages a few thousand
+  // candidates (at 128K about 4,000; more spill to the workspace), else one
+  // workgroup with all of it
+  const int64_t half = ((int64_t)kFinalizeLds / 2 - fixed) / (2 * (int64_t)sizeof(uint32_t));
+  if (half >= kTokenHalfLdsMinCand) return (int)half;
   const int64_t cap = ((int64_t)kFinalizeLds - fixed) / (2 * (int64_t)sizeof(uint32_t));
   return cap > 0 ? (int)cap : 0;
 }

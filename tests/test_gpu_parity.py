@@ -82,6 +82,31 @@ def test_topk_ties_across_chunks():
     assert idx[1].tolist() == list(range(2048))
 
 
+def test_topk_one_kernel_ties_and_spill():
+    # 512 tokens: one workgroup per token selects. Rows of equal scores, and
+    # scores on a 1/4 grid, put thousands of candidates at the cut, more than
+    # the workgroup stages in LDS, so the rest spill to the workspace.
+    rng = np.random.default_rng(29)
+    n_seq = 20000
+    pos = np.sort(rng.integers(0, n_seq, 512))
+    pos[-1] = n_seq - 1
+    wl = si.build("topk_one_kernel", [n_seq], [(0, int(p)) for p in pos], seed=29)
+    say("[topk] one workgroup per token, 512 tokens, ties spilling from LDS")
+    dev = Dev(wl)
+    sc = np.full((wl.num_tokens, wl.max_len), np.nan, dtype=np.float32)
+    for t, p in enumerate(pos):
+        n = int(p) + 1
+        if t % 2 == 0:
+            sc[t, :n] = 1.25
+        else:
+            sc[t, :n] = np.round(rng.standard_normal(n) * 4.0) / 4.0
+    idx = dev.topk(torch.from_numpy(sc).cuda()).cpu().numpy()
+    for t, p in enumerate(pos):
+        n = int(p) + 1
+        ref = oracle.select_topk(sc[t, :n].astype(np.float64), wl.k)
+        assert np.array_equal(idx[t], ref), f"token {t} (n={n})"
+
+
 def test_attention_tiny_given_indices():
     wl = si.config(0)
     say("[attention] tiny decode, oracle indices")
@@ -253,7 +278,7 @@ def test_repeat_calls_are_deterministic():
 
 
 def test_all_equal_scores_spill_past_lds():
-    # 50000 tied candidates: more than the one-kernel top-k keeps in LDS
+    # 50000 tied candidates, two tokens (the cut / select / finalize kernels)
     wl = si.build("equal_spill", [50000], [(0, 49999), (0, 30000)], seed=14)
     wl.q_idx.zero_()
     _, (idx, _, _), _ = _check_forward(wl)
