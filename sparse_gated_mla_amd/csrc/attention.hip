@@ -94,23 +94,27 @@ struct RowStage {
   // rows of tile `tile`, from the indices loaded for it
   __device__ __forceinline__ void load_rows(rsrc_t rows, rsrc_t scales, int tile, int nrows, int n) {
     uint32_t m = 0;
+    const int t0 = tile * kAttnTileRows;
+    constexpr int kSkip = (int)0x80000000;   // an offset past the end of every buffer
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
       const int u = unit(q);
       const int r = u / kUnitsPerRow;
       const int c = u - r * kUnitsPerRow;
       const int id = idx[q];
-      const bool real = (r < kAttnTileRows) & (tile * kAttnTileRows + r < nrows) & (id >= 0) & (id < n);
+      // row t0 + r lies inside the split, and its index inside [0, n) (n >= 0;
+      // a negative index compares unsigned as at least n)
+      const bool real = (r < kAttnTileRows) & (t0 < nrows - r) & ((uint32_t)id < (uint32_t)n);
       m |= (uint32_t)real << q;
-      const uint32_t skip = real ? 0u : 0x80000000u;
       v[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rows, (int)(((uint32_t)id * kRowBytes + 16u * c) | skip), 0, kNonTemporal));
+                                           rows, real ? (int)((uint32_t)id * kRowBytes + 16u * c) : kSkip,
+                                           0, kNonTemporal));
       if constexpr (kFmt == kFmtFp8)
-        s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, (int)(((uint32_t)id * 4u) | skip), 0, 0);
+        s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(scales, real ? (int)((uint32_t)id * 4u) : kSkip, 0, 0);
       if constexpr (kMx)   // the unit's block: c/2 (16 E4M3FN bytes) or c (32 E2M1 nibbles)
         s[q] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(
-            scales, (int)(((uint32_t)id * (kDQK / 32) + (uint32_t)(kFmt == kFmtMx ? c >> 1 : c)) | skip),
-            0, 0);
+            scales,
+            real ? (int)((uint32_t)id * (kDQK / 32) + (uint32_t)(kFmt == kFmtMx ? c >> 1 : c)) : kSkip, 0, 0);
     }
     ok = m;
     // keep each tile's loads together, in program order
