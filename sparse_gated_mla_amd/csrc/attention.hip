@@ -177,24 +177,25 @@ struct HalfState {
 };
 
 // First half of a tile for the wave's 16 heads: its partial logits^T over
-// this half's 9 k-steps (two chains per row block), posted to its slot of
+// this half's 9 k-steps (one chain per row block), posted to its slot of
 // xbuf for the partner wave and returned.
 __device__ __forceinline__ void tile_partial_logits(const uint16_t* __restrict__ tile,
                                                     float* __restrict__ xbuf, const u32x4 (&qb)[9],
                                                     int lane, int wave, int half, f32x4 (&part)[2]) {
   const int n16 = lane & 15, g = lane >> 4;
-  f32x4 acc[2][2] = {};
+  // one chain per row block; the two blocks' MFMAs alternate
+  f32x4 acc[2] = {};
+  const uint16_t* rowp0 = tile + n16 * kRowStride + 8 * g + 288 * half;
+  const uint16_t* rowp1 = rowp0 + 16 * kRowStride;
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint16_t* rowp = tile + (16 * b + n16) * kRowStride + 8 * g + 288 * half;
-#pragma unroll
-    for (int s = 0; s < 9; ++s) {
-      u32x4 av = *reinterpret_cast<const u32x4*>(rowp + 32 * s);
-      acc[b][s & 1] = mfma16x16x32(av, qb[s], acc[b][s & 1]);
-    }
+  for (int s = 0; s < 9; ++s) {
+    const u32x4 a0 = *reinterpret_cast<const u32x4*>(rowp0 + 32 * s);
+    const u32x4 a1 = *reinterpret_cast<const u32x4*>(rowp1 + 32 * s);
+    acc[0] = mfma16x16x32(a0, qb[s], acc[0]);
+    acc[1] = mfma16x16x32(a1, qb[s], acc[1]);
   }
-  part[0] = acc[0][0] + acc[0][1];
-  part[1] = acc[1][0] + acc[1][1];
+  part[0] = acc[0];
+  part[1] = acc[1];
   f32x4* mine = reinterpret_cast<f32x4*>(xbuf + (wave * 64 + lane) * 8);
   mine[0] = part[0];
   mine[1] = part[1];
