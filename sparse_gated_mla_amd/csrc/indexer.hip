@@ -156,10 +156,11 @@ __device__ __forceinline__ f32x4 tile_weight(const float* lds_w, int lane, int k
 }
 
 // max(x, 0) in one integer instruction: read as a signed integer, every
-// negative float (-0 included) is negative and every positive one keeps its
-// order, so max(bits, 0) gives +0 for the former and x for the latter.
-// (fmaxf on an MFMA result costs a second instruction, which quiets a
-// signalling NaN first.)
+// negative float (-0 included) is negative and every positive one positive,
+// so max(bits, 0) gives +0 for the former and x for the latter (a NaN with
+// its sign bit clear passes through, where fmaxf would give 0). fmaxf on an
+// MFMA result costs a second instruction, which quiets a signalling NaN
+// first.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
 // Scores one staged tile. Returns, in lanes 0..31, the score of tile row

@@ -158,6 +158,8 @@ __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) 
   // loaded and not used.
   // (The cut is a per-lane vector load, lanes 0 and 1 reading its two words:
   // a uniform scalar load would be sunk past the metadata's branch.)
+  static_assert(offsetof(TopkCtrl, above1) == offsetof(TopkCtrl, digit1) + sizeof(uint32_t),
+                "the cut's two words are adjacent");
   const uint32_t ctrl_word = (&a.ctrl[t].digit1)[threadIdx.x & 1];
   HistRun<kFinThreads, kHist2> h2;
   h2.load(a.hist2 + (int64_t)t * kHist2);
