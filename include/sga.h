@@ -136,7 +136,8 @@ typedef struct sga_trace {
  * where key = k_idx (bf16), payload * k_idx_scale[row] (fp8), or payload
  * times its 32-element block's E8M0 scale (MX).
  *   q_idx       [T,64,128] bf16, row-major.
- *   w           [T,64] fp32 head weights.
+ *   w           [T,64] fp32 head weights, 16-byte aligned (read as 16-byte
+ *               vectors).
  *   k_idx       [cache_rows,128] bf16, E4M3FN or packed E2M1 payload, row-major
  *               (256, 128 or 64 B per row).
  *   k_idx_scale [cache_rows] fp32 (fp8), [cache_rows,4] uint8 E8M0 (MX, both
@@ -205,8 +206,15 @@ SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs
 
 /*
  * sga_forward: the whole path, indexer -> top-k -> attention -> gate, for one
- * batch. Its results equal sga_index_scores, then sga_topk, then
- * sga_sparse_mla_attn, called with the same arguments.
+ * batch.
+ * Source: the fact sheet's token-selection fact (a DSA-style indexer scores
+ * the cached positions and the top 2,048 are attended), its attention facts
+ * (absorbed MLA over the 576-wide latent rows, 64 heads) and its gate fact
+ * (a head-specific sigmoid gate before o_proj); the technical report abstract
+ * and the rebasdaily article (at most 2,048 positions read per query).
+ * Its results equal sga_index_scores, then sga_topk, then
+ * sga_sparse_mla_attn, called with the same arguments (w, q_idx, q_abs and
+ * out 16-byte aligned, as there).
  * indices_out [T,k] receives the selected positions when non-NULL.
  * trace may be NULL.
  */

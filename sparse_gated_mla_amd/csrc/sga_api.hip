@@ -301,7 +301,7 @@ SGA_API sga_status sga_index_scores(const sga_batch* batch, const void* q_idx, c
                                     hipStream_t stream) {
   SGA_TRY(check_batch(batch));
   if (batch->num_tokens == 0) return SGA_OK;
-  if (!q_idx || !w || !scores || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
+  if (!q_idx || !w || !scores || !aligned16(q_idx) || !aligned16(w)) return SGA_ERR_INVALID_ARG;
   SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype, 4));
   if (ld < batch->max_len) return SGA_ERR_INVALID_ARG;
   IndexerArgs a;
@@ -387,7 +387,7 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
   if (!isfinite(sm_scale)) return SGA_ERR_INVALID_ARG;
   if (batch->num_tokens == 0) return SGA_OK;
-  if (!q_idx || !w || !aligned16(q_idx)) return SGA_ERR_INVALID_ARG;
+  if (!q_idx || !w || !aligned16(q_idx) || !aligned16(w)) return SGA_ERR_INVALID_ARG;
   if (!q_abs || !out || !aligned16(q_abs) || !aligned16(out)) return SGA_ERR_INVALID_ARG;
   SGA_TRY(check_store(k_idx, k_idx_scale, k_idx_dtype, 4));
   SGA_TRY(check_store(kv, kv_scale, kv_dtype, 1));

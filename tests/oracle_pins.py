@@ -644,6 +644,111 @@ def check_indexer_loss_properties(orc):
     assert abs(orc.sparse_indexer_loss(q, rows[perm], tau, sc[perm]) - got) < 1e-12
 
 
+# ---------------------------------------------------------------- ragged batches
+def _flat_batch(rng, lens, gap=3):
+    """Sequences of the given lengths stored back to back in flat caches, with
+    `gap` junk rows before each (large values, so a row read from the wrong
+    place changes every result). Returns the flat bf16 latent rows (float64
+    values and raw bits), integer indexer keys (int64 and raw bits) and
+    seq_start."""
+    starts, rows = [], 0
+    for n in lens:
+        rows += gap
+        starts.append(rows)
+        rows += n
+    kv = rng.standard_normal((rows, 576)) / 24
+    k_int = rng.integers(-2, 3, (rows, 128))
+    for s0, n in zip(starts, lens):          # junk in the gaps
+        kv[s0 - gap:s0] = 5.0 + rng.standard_normal((gap, 576))
+        k_int[s0 - gap:s0] = 3
+    kv_bits = torch.from_numpy(kv.astype(np.float32)).to(torch.bfloat16)
+    k_bits = torch.from_numpy(k_int.astype(np.float32)).to(torch.bfloat16)
+    return (kv_bits.to(torch.float64).numpy(), kv_bits.view(torch.int16).numpy().view(np.uint16),
+            k_int, k_bits.view(torch.int16).numpy().view(np.uint16), np.array(starts, np.int64))
+
+
+def _int_scores(k_int, q_int, w_int):
+    """Exact integer indexer scores of integer keys [n, 128] for one token."""
+    d = k_int.astype(np.int64) @ q_int.astype(np.int64).T            # [n, 64]
+    return (np.where(d > 0, d, 0) * w_int.astype(np.int64)[None, :]).sum(axis=1)
+
+
+def check_forward_multi_sequence(orc):
+    """Three sequences at nonzero offsets of the flat caches: each token sees only
+    rows seq_start[b] .. seq_start[b] + p. A token with k at least its visible
+    count gets dense causal attention over its own sequence (torch SDPA); a
+    token with fewer gets the rank-defined top-k of its exact integer scores
+    and SDPA over exactly those rows."""
+    rng = np.random.default_rng(16)
+    lens = [9, 14, 6]
+    kv, kv_bits, k_int, k_bits, starts = _flat_batch(rng, lens)
+    token_seq = np.array([0, 1, 1, 2, 0], np.int32)
+    token_pos = np.array([8, 13, 4, 5, 2], np.int32)
+    T, k = len(token_seq), 5
+    q_int = rng.integers(-2, 3, (T, 64, 128))
+    w_int = rng.integers(0, 4, (T, 64))
+    q_abs = rng.standard_normal((T, 64, 576))
+    gate = rng.standard_normal((T, 64)) * 2
+    tau = 1 / math.sqrt(192)
+    ks = orc.Store(k_bits, "bf16")
+    vs = orc.Store(kv_bits, "bf16")
+    res = orc.forward(token_seq, token_pos, starts, np.array(lens, np.int32), q_int.astype(float),
+                      w_int.astype(float), ks, q_abs, vs, gate, k, tau)
+    for t in range(T):
+        b, p = int(token_seq[t]), int(token_pos[t])
+        rows = np.arange(starts[b], starts[b] + p + 1)
+        want = _rank_select(list(_int_scores(k_int[rows], q_int[t], w_int[t])), k)
+        assert res["indices"][t].tolist() == want, (t, res["indices"][t], want)
+        kept = rows[[s for s in want if s >= 0]]
+        if p + 1 <= k:
+            assert len(kept) == p + 1
+        Q = torch.from_numpy(q_abs[t])[None, :, None, :]
+        K = torch.from_numpy(kv[kept])[None, None].expand(1, 64, len(kept), 576)
+        V = torch.from_numpy(kv[kept, :512])[None, None].expand(1, 64, len(kept), 512)
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, scale=tau)[0, :, 0]
+        ref = (o * torch.sigmoid(torch.from_numpy(gate[t]))[:, None]).numpy()
+        assert np.allclose(res["out"][t], ref, rtol=1e-11, atol=1e-14), t
+        z = torch.from_numpy(tau * (q_abs[t] @ kv[kept].T))
+        assert np.allclose(res["lse"][t], torch.logsumexp(z, dim=1).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def check_indexer_loss_multi_sequence(orc):
+    """The per-token wrapper of the loss over a ragged batch at nonzero offsets:
+    one token keeping fewer rows than it sees, one keeping all of them (its
+    index row is padded with -1, which must not count), one in an empty
+    sequence (loss 0). Composed independently: exact integer scores, the rank
+    definition of the top-k, each head's torch softmax over the kept rows,
+    their mean, then torch's kl_div against the log-softmax of the scores."""
+    rng = np.random.default_rng(17)
+    lens = [12, 5, 0]
+    kv, kv_bits, k_int, k_bits, starts = _flat_batch(rng, lens)
+    token_seq = np.array([0, 1, 2, 0], np.int32)
+    token_pos = np.array([11, 4, 0, 3], np.int32)
+    T, k = len(token_seq), 6
+    q_int = rng.integers(-2, 3, (T, 64, 128))
+    w_int = rng.integers(0, 4, (T, 64))
+    q_abs = rng.standard_normal((T, 64, 576)) * 3
+    tau = 1 / math.sqrt(192)
+    got = orc.indexer_loss(token_seq, token_pos, starts, np.array(lens, np.int32), q_int.astype(float),
+                           w_int.astype(float), orc.Store(k_bits, "bf16"), q_abs,
+                           orc.Store(kv_bits, "bf16"), k, tau)
+    assert got.shape == (T,)
+    for t in range(T):
+        b, p = int(token_seq[t]), int(token_pos[t])
+        n = min(p + 1, lens[b])
+        if n == 0:
+            assert got[t] == 0.0, (t, got[t])
+            continue
+        rows = np.arange(starts[b], starts[b] + n)
+        sc = _int_scores(k_int[rows], q_int[t], w_int[t])
+        sel = [s for s in _rank_select(list(sc), k) if s >= 0]
+        z = torch.from_numpy(tau * (q_abs[t] @ kv[rows[sel]].T))                # [64, m]
+        target = torch.softmax(z, dim=1).mean(dim=0)
+        logq = torch.log_softmax(torch.from_numpy(sc[sel].astype(np.float64)), dim=0)
+        ref = torch.nn.functional.kl_div(logq, target, reduction="sum").item()
+        assert abs(got[t] - ref) < 1e-12 * max(1.0, abs(ref)), (t, got[t], ref)
+
+
 ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_example,
               check_indexer_exact_integer, check_topk_worked_example, check_topk_rank_definition,
               check_topk_enumeration, check_topk_special_cases, check_attention_closed_form,
@@ -654,4 +759,5 @@ ALL_CHECKS = [check_bf16_decode, check_e4m3fn_table, check_indexer_worked_exampl
               check_forward_mxfp8_store, check_output_projection_unabsorbed,
               check_output_projection_selection, check_e2m1_table, check_mxfp4_worked_example,
               check_mxfp4_brute_force, check_mxfp4_scale_invariance, check_forward_mxfp4_store,
-              check_indexer_loss_worked_example, check_indexer_loss_properties]
+              check_indexer_loss_worked_example, check_indexer_loss_properties,
+              check_forward_multi_sequence, check_indexer_loss_multi_sequence]

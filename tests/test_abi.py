@@ -68,6 +68,7 @@ def test_index_scores_rejects_bad_arguments(lib):
     assert call(b, k=None) == 1
     assert call(b, s=None) == 1
     assert call(b, q=FAKE_ODD) == 1
+    assert call(b, w=FAKE_ODD) == 1            # head weights are read as 16-byte vectors
     assert call(b, ld=99) == 1                 # ld < max_len
     assert call(b, ks=FAKE, dt=0) == 1         # bf16 keys take no scale
     assert call(b, ks=None, dt=1) == 1         # fp8 keys need scales
@@ -121,9 +122,11 @@ def test_forward_rejects_bad_arguments(lib):
     need = lib.sga_forward_workspace_size(2, 100, 8)
     assert need > 0
 
-    def call(ws=FAKE, nb=need, tau=0.07, k=8, kscale=None, kdt=0):
-        return lib.sga_forward(ctypes.byref(b), FAKE, FAKE, FAKE, kscale, kdt, FAKE, FAKE, None, 0,
+    def call(ws=FAKE, nb=need, tau=0.07, k=8, kscale=None, kdt=0, w=FAKE, q=FAKE):
+        return lib.sga_forward(ctypes.byref(b), q, w, FAKE, kscale, kdt, FAKE, FAKE, None, 0,
                                k, tau, None, FAKE, None, None, ws, nb, None, None)
+    assert call(w=FAKE_ODD) == 1
+    assert call(q=FAKE_ODD) == 1
     assert call(ws=None) == 3
     assert call(nb=need - 1) == 3
     assert call(tau=math.inf) == 1

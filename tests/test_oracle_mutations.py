@@ -188,6 +188,46 @@ def _loss_pooled_logits(q_abs, rows, sm_scale, scores_sel):
     log_q = i - (i.max() + np.log(np.exp(i - i.max()).sum()))
     return float(np.sum(p * (np.log(p) - log_q)))
 
+
+def _forward_base_dropped(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store, q_abs,
+                          kv_store, gate, k, sm_scale, tokens=None, keep_scores=False):
+    # every sequence addressed as if it started at flat row 0
+    return _ORIG_FORWARD(token_seq, token_pos, np.zeros_like(np.asarray(seq_start)), seq_len, q_idx,
+                         w, k_store, q_abs, kv_store, gate, k, sm_scale, tokens=tokens,
+                         keep_scores=keep_scores)
+
+
+_ORIG_FORWARD = base.forward
+
+
+def _loss_keeps_padding(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store, q_abs,
+                        kv_store, k, sm_scale, tokens=None):
+    # the -1 padding of a short selection is not dropped (it reads the row
+    # before the sequence and the last score)
+    sel = range(len(token_seq)) if tokens is None else tokens
+    out = []
+    for t in sel:
+        b, p = int(token_seq[t]), int(token_pos[t])
+        n = min(p + 1, int(seq_len[b]))
+        b0 = int(seq_start[b])
+        scores = base.index_scores(q_idx[t], w[t], k_store.rows(np.arange(b0, b0 + n)))
+        idx = base.select_topk(scores, k)
+        if n == 0:
+            out.append(0.0)
+            continue
+        out.append(base.sparse_indexer_loss(q_abs[t], kv_store.rows(b0 + idx), sm_scale, scores[idx]))
+    return np.asarray(out, dtype=np.float64)
+
+
+def _loss_visible_off_by_one(token_seq, token_pos, seq_start, seq_len, q_idx, w, k_store, q_abs,
+                             kv_store, k, sm_scale, tokens=None):
+    # the token's own row left out of the visible rows
+    return _ORIG_LOSS(token_seq, np.maximum(np.asarray(token_pos) - 1, 0), seq_start, seq_len, q_idx,
+                      w, k_store, q_abs, kv_store, k, sm_scale, tokens=tokens)
+
+
+_ORIG_LOSS = base.indexer_loss
+
 MUTANTS = {
     "relu_after_weighting": dict(index_scores=_relu_after_weight),
     "weight_inside_relu": dict(index_scores=_weight_then_relu),
@@ -211,6 +251,9 @@ MUTANTS = {
     "mx4_exponent_offset_8": dict(quantize_blocks_mxfp4=_mx4_exponent_like_fp8),
     "loss_reversed_kl": dict(sparse_indexer_loss=_loss_reversed_kl),
     "loss_pooled_logits": dict(sparse_indexer_loss=_loss_pooled_logits),
+    "forward_seq_start_dropped": dict(forward=_forward_base_dropped),
+    "loss_padding_kept": dict(indexer_loss=_loss_keeps_padding),
+    "loss_visible_off_by_one": dict(indexer_loss=_loss_visible_off_by_one),
 }
 
 
@@ -229,3 +272,17 @@ def test_pins_catch_mutant(name):
 def test_real_oracle_passes_all_pins():
     for check in oracle_pins.ALL_CHECKS:
         check(oracle)
+
+
+@pytest.mark.parametrize("name,pin", [("forward_seq_start_dropped", "check_forward_multi_sequence"),
+                                      ("loss_padding_kept", "check_indexer_loss_multi_sequence"),
+                                      ("loss_visible_off_by_one", "check_indexer_loss_multi_sequence")])
+def test_multi_sequence_pins_catch(name, pin):
+    mutant = _clone(**MUTANTS[name])
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mutant)
+        except AssertionError:
+            caught.append(check.__name__)
+    assert pin in caught, (name, caught)
