@@ -229,6 +229,34 @@ SGA_API sga_status sga_forward(const sga_batch* batch,
                                const sga_trace* trace, hipStream_t stream);
 
 /*
+ * sga_forward_noalloc: sga_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). It takes no workspace: its scratch is a device array of
+ * SGA_NOALLOC_SCRATCH_BYTES bytes inside the library, which each GPU holds
+ * from the library's first use on it until the process ends. The call itself
+ * allocates and frees nothing.
+ * Arguments and results are those of sga_forward (same kernels, same results).
+ * A problem whose sga_forward_workspace_size(T, max_len, k) exceeds
+ * SGA_NOALLOC_SCRATCH_BYTES returns SGA_ERR_WORKSPACE before anything is
+ * launched. The first call on a device looks up the array's address on that
+ * device (the device of `stream`).
+ * Every call on one GPU shares that GPU's array and leaves its last contents
+ * there: calls that overlap on one GPU (different streams, or host threads
+ * racing on one stream) race on the scratch and must be serialised by the
+ * caller.
+ */
+#define SGA_NOALLOC_SCRATCH_BYTES (64u << 20)   /* 64 MiB per GPU */
+SGA_API size_t sga_forward_noalloc_scratch_bytes(void);
+SGA_API sga_status sga_forward_noalloc(const sga_batch* batch,
+                                       const void* q_idx, const float* w, const void* k_idx,
+                                       const void* k_idx_scale, sga_dtype k_idx_dtype,
+                                       const void* q_abs, const void* kv, const void* kv_scale,
+                                       sga_dtype kv_dtype, int32_t k, float sm_scale,
+                                       const float* gate_logits, float* out, float* lse,
+                                       int32_t* indices_out, const sga_trace* trace,
+                                       hipStream_t stream);
+
+/*
  * sga_cache_append: writes each token's new cached rows (the step just before
  * the path in decode).
  * Source: the FP8 model card (nlp.com.ai, "A.X K2 FP8": FP8 with dynamic

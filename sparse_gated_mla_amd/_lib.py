@@ -24,6 +24,7 @@ HEADS, IDX_HEADS, IDX_DIM, D_LATENT, D_QK, D_V = 64, 64, 128, 512, 576, 128
 
 EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_workspace_size",
            "sga_sparse_mla_attn", "sga_forward_workspace_size", "sga_forward",
+           "sga_forward_noalloc_scratch_bytes", "sga_forward_noalloc",
            "sga_cache_append", "sga_output_proj_workspace_size", "sga_output_proj",
            "sga_indexer_loss_workspace_size", "sga_indexer_loss",
            "sga_status_string", "sga_version")
@@ -74,6 +75,9 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "sga_forward_workspace_size": ([i32, i32, i32], sz),
         "sga_forward": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, f32, vp, vp,
                          vp, vp, vp, sz, tp, vp], ctypes.c_int),
+        "sga_forward_noalloc_scratch_bytes": ([], sz),
+        "sga_forward_noalloc": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, vp, ctypes.c_int, i32, f32, vp,
+                                 vp, vp, vp, tp, vp], ctypes.c_int),
         "sga_cache_append": ([bp, vp, vp, vp, vp, ctypes.c_int, vp, vp, ctypes.c_int, vp], ctypes.c_int),
         "sga_output_proj_workspace_size": ([i32, i32], sz),
         "sga_indexer_loss_workspace_size": ([i32, i32], sz),
@@ -271,6 +275,35 @@ def sga_forward(batch: Batch, q_idx, w, k_idx, k_idx_scale, q_abs, kv, kv_scale,
         _ptr(kv), _ptr(kv_scale), vdt, k, float(sm_scale), _ptr(gate), _ptr(out), _ptr(lse),
         _ptr(indices_out), _ptr(ws), ws.numel(), None if trace is None else ctypes.byref(trace),
         _stream(q_abs)))
+
+
+def sga_forward_noalloc_scratch_bytes() -> int:
+    return int(load().sga_forward_noalloc_scratch_bytes())
+
+
+def sga_forward_noalloc(batch: Batch, q_idx, w, k_idx, k_idx_scale, q_abs, kv, kv_scale, k: int,
+                        sm_scale: float, gate, out, lse=None, indices_out=None,
+                        trace: Optional[SgaTrace] = None) -> None:
+    """sga_forward with the library's own per-GPU scratch instead of a workspace:
+    allocates nothing (for callers that cannot allocate)."""
+    T = batch.num_tokens
+    _check(q_idx, "q_idx", (torch.bfloat16,), (T, IDX_HEADS, IDX_DIM))
+    _check(w, "w", (torch.float32,), (T, IDX_HEADS))
+    kdt = _cache_dtype(k_idx, k_idx_scale, "k_idx", batch.cache_rows, IDX_DIM)
+    _check(q_abs, "q_abs", (torch.bfloat16,), (T, HEADS, D_QK))
+    vdt = _cache_dtype(kv, kv_scale, "kv", batch.cache_rows, D_QK)
+    if gate is not None:
+        _check(gate, "gate", (torch.float32,), (T, HEADS))
+    _check(out, "out", (torch.float32,), (T, HEADS, D_LATENT))
+    if lse is not None:
+        _check(lse, "lse", (torch.float32,), (T, HEADS))
+    if indices_out is not None:
+        _check(indices_out, "indices_out", (torch.int32,), (T, k))
+    b = batch.c()
+    _raise("sga_forward_noalloc", load().sga_forward_noalloc(
+        ctypes.byref(b), _ptr(q_idx), _ptr(w), _ptr(k_idx), _ptr(k_idx_scale), kdt, _ptr(q_abs),
+        _ptr(kv), _ptr(kv_scale), vdt, k, float(sm_scale), _ptr(gate), _ptr(out), _ptr(lse),
+        _ptr(indices_out), None if trace is None else ctypes.byref(trace), _stream(q_abs)))
 
 
 def sga_cache_append(batch: Batch, latent=None, idx_key=None, kv=None, kv_scale=None,

@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "sga.h"
 #include "sga_kernels.h"
 
@@ -276,6 +278,50 @@ size_t attn_ws(int32_t T, int32_t k) {
 
 }  // namespace
 
+// ---------------------------------------------------------------- no-allocation scratch
+// The workspace of sga_forward_noalloc: a file-scope device array that each
+// GPU holds from module load until the process ends. In host code its name
+// stands for a host-side symbol, not a device address, so the address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that pointer is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SGA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device that runs work queued on `stream` (the current device for the
+// null stream).
+hipError_t stream_device(hipStream_t stream, int* dev) {
+  if (!stream) return hipGetDevice(dev);
+  hipDevice_t d;
+  const hipError_t e = hipStreamGetDevice(stream, &d);
+  if (e == hipSuccess) *dev = (int)d;
+  return e;
+}
+
+// The device address of `scratch` on device dev; found once per device.
+sga_status scratch_on(int dev, void** out) {
+  if (dev < 0 || dev >= kMaxDevices) return SGA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return SGA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return SGA_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return SGA_ERR_HIP;
+    if (e != hipSuccess || !p) return SGA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SGA_OK;
+}
+
+}  // namespace
+
 static_assert(SGA_BF16 == sga::kFmtBf16 && SGA_FP8_E4M3 == sga::kFmtFp8 &&
                   SGA_MXFP8_E4M3 == sga::kFmtMx && SGA_MXFP4_E2M1 == sga::kFmtMx4,
               "cache formats are passed to the kernels as their sga_dtype values");
@@ -428,6 +474,31 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
                         out, lse, plan, AL, stream));
   if (trace) SGA_TRY(record(trace->attn_end, stream));
   return SGA_OK;
+}
+
+SGA_API size_t sga_forward_noalloc_scratch_bytes(void) { return SGA_NOALLOC_SCRATCH_BYTES; }
+
+SGA_API sga_status sga_forward_noalloc(const sga_batch* batch, const void* q_idx, const float* w,
+                                       const void* k_idx, const void* k_idx_scale,
+                                       sga_dtype k_idx_dtype, const void* q_abs, const void* kv,
+                                       const void* kv_scale, sga_dtype kv_dtype, int32_t k,
+                                       float sm_scale, const float* gate_logits, float* out,
+                                       float* lse, int32_t* indices_out, const sga_trace* trace,
+                                       hipStream_t stream) {
+  // the size limit is checked before the device is touched
+  SGA_TRY(check_batch(batch));
+  if (k < 1) return SGA_ERR_INVALID_ARG;
+  if (k > SGA_MAX_K) return SGA_ERR_UNSUPPORTED;
+  if (batch->num_tokens == 0) return SGA_OK;
+  const size_t need = sga_forward_workspace_size(batch->num_tokens, batch->max_len, k);
+  if (need > SGA_NOALLOC_SCRATCH_BYTES) return SGA_ERR_WORKSPACE;
+  int dev = -1;
+  SGA_HIP(stream_device(stream, &dev));
+  void* ws = nullptr;
+  SGA_TRY(scratch_on(dev, &ws));
+  return sga_forward(batch, q_idx, w, k_idx, k_idx_scale, k_idx_dtype, q_abs, kv, kv_scale, kv_dtype,
+                     k, sm_scale, gate_logits, out, lse, indices_out, ws, SGA_NOALLOC_SCRATCH_BYTES,
+                     trace, stream);
 }
 
 SGA_API sga_status sga_cache_append(const sga_batch* batch, const void* latent, const void* idx_key,

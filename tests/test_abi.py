@@ -134,6 +134,24 @@ def test_forward_rejects_bad_arguments(lib):
     assert call(kdt=1) == 1
 
 
+def test_forward_noalloc_rejects_oversize_before_touching_the_device(lib):
+    # the scratch limit is checked on the host first: these calls return without
+    # any HIP call, so they run without a GPU
+    limit = lib.sga_forward_noalloc_scratch_bytes()
+    assert limit == 64 << 20
+
+    def call(bb, k=2048):
+        return lib.sga_forward_noalloc(ctypes.byref(bb), FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, None,
+                                       0, k, 0.07, None, FAKE, None, None, None, None)
+    big = _batch(T=64, max_len=1 << 19, rows=1 << 19)
+    assert lib.sga_forward_workspace_size(64, 1 << 19, 2048) > limit
+    assert call(big) == 3                      # needs more scratch than the library holds
+    assert call(_batch(), k=0) == 1
+    assert call(_batch(), k=(1 << 16) + 1) == 2
+    assert call(_batch(T=-1)) == 1
+    assert call(_batch(T=0, ptr=0)) == 0       # empty batch: nothing to do
+
+
 def test_cache_append_rejects_bad_arguments(lib):
     b = _batch()
 
