@@ -122,7 +122,8 @@ typedef struct sga_batch {
 typedef struct sga_trace {
   hipEvent_t indexer_begin;  /* before the indexer kernel */
   hipEvent_t indexer_end;    /* after the indexer kernel */
-  hipEvent_t topk_end;       /* after the last top-k kernel */
+  hipEvent_t topk_end;       /* after the last top-k kernel launched before the attention
+                                (the top-k's final stage may run inside the attention kernel) */
   hipEvent_t attn_end;       /* after the attention (and combine) kernels */
 } sga_trace;
 

@@ -41,6 +41,9 @@
 // With several splits per token, each split writes its output normalised by
 // its own exp-sum, in fp16 with a per-half scale, plus (max, exp-sum);
 // combine_kernel merges the splits by log-sum-exp and applies the gate.
+#include <string.h>
+
+#include "sga_finalize.h"
 #include "sga_kernels.h"
 
 namespace sga {
@@ -89,6 +92,14 @@ struct RowStage {
     for (int q = 0; q < kPer; ++q)
       idx[q] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(
           idx_rs, (tile * kAttnTileRows + unit(q) / kUnitsPerRow) * 4, 0, 0);
+  }
+
+  // indices of tile `tile` from the split's indices in LDS (rows past the
+  // split read some entry and are masked by the row count)
+  __device__ __forceinline__ void load_idx_lds(const int32_t* lidx, int tile) {
+#pragma unroll
+    for (int q = 0; q < kPer; ++q)
+      idx[q] = lidx[min(tile * kAttnTileRows + unit(q) / kUnitsPerRow, kSelectMaxRows - 1)];
   }
 
   // rows of tile `tile`, from the indices loaded for it
@@ -372,13 +383,29 @@ __device__ __forceinline__ void tile_probs(const float* __restrict__ flags,
   }
 }
 
-template <int kFmt, bool kProbs>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
+// LDS of the attention kernel: three row regions, their flags, and the
+// partial-logit exchange buffers, in one array (the selecting variant first
+// runs the top-k's final stage in the same bytes).
+constexpr int kFlagsOffset = 3 * kRegionBytes;
+constexpr int kXbufOffset = kFlagsOffset + 3 * 2 * kAttnTileRows * 4;
+constexpr int kAttnLdsBytes = kXbufOffset + 2 * kAttnWaves * 64 * 8 * 4;
+static_assert(finalize_lds_words((kMaxLenRows + 63) / 64 * 2) * 4 <= kAttnLdsBytes,
+              "the top-k's final stage fits in the attention's LDS at the longest context");
+
+// kSelect: the kernel first finds its own rows of the token's top-k: every
+// split of the token runs the top-k's final stage (sga_finalize.h) on the
+// select kernel's output, keeps the ranks of its split in LDS (and writes them
+// to indices_out when asked), then attends over them. The final stage's reads
+// are a few tens of KB per token, served by L2.
+template <int kFmt, bool kProbs, bool kSelect>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs ta) {
   constexpr bool kRowScale = kFmt == kFmtFp8;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_tile[3][kRegionBytes];
-  __shared__ __attribute__((aligned(16))) float lds_flags[3][2 * kAttnTileRows];
-  __shared__ __attribute__((aligned(16))) float xbuf[2][kAttnWaves * 64 * 8];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_main[kAttnLdsBytes];
   __shared__ float psum[kProbs ? 2 : 1][kProbs ? 4 * kAttnTileRows : 1];
+  __shared__ int32_t lds_idx[kSelect ? kSelectMaxRows : 1];
+  auto lds_tile = reinterpret_cast<uint8_t(*)[kRegionBytes]>(lds_main);
+  auto lds_flags = reinterpret_cast<float(*)[2 * kAttnTileRows]>(lds_main + kFlagsOffset);
+  auto xbuf = reinterpret_cast<float(*)[kAttnWaves * 64 * 8]>(lds_main + kXbufOffset);
   using Stage = RowStage<kFmt>;
   const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int t = wg / a.splits, split = wg % a.splits;
@@ -397,14 +424,39 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
 
   // the indices and the query do not depend on the batch metadata: their
   // loads go out first and travel while the metadata's two scalar rounds run
+  // (the selecting variant issues the final stage's loads instead of the
+  // indices)
   Stage s0, s1;
-  s0.load_idx(idx_rs, 0);
-  s1.load_idx(idx_rs, 1);
+  TokenFinalize<kAttnThreads> fin;
+  if constexpr (kSelect) {
+    fin.prefetch(ta, t);
+  } else {
+    s0.load_idx(idx_rs, 0);
+    s1.load_idx(idx_rs, 1);
+  }
   u32x4 qb[9];
   {
     const uint16_t* q = a.q_abs + ((int64_t)t * kHeads + head) * kDQK + 288 * half + 8 * g;
 #pragma unroll
     for (int s = 0; s < 9; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
+  }
+  if constexpr (kSelect) {
+    // this split's ranks [j_begin, j_begin + nrows) of the token's selection;
+    // the visible count comes with the cut, so the stage does not wait for the
+    // batch metadata (needed only for the row gathers)
+    const int nv = fin.visible();
+    if (nv <= a.k) {   // every visible position is kept: rank r is position r
+      for (int j = threadIdx.x; j < nrows; j += kAttnThreads) lds_idx[j] = j_begin + j < nv ? j_begin + j : -1;
+    } else {
+      fin.run(ta, nv, reinterpret_cast<uint32_t*>(lds_main), (uint32_t)j_begin, (uint32_t)(j_begin + nrows),
+              [&](uint32_t o, uint32_t p) { lds_idx[o - j_begin] = (int32_t)p; });
+    }
+    __syncthreads();   // the indices are in LDS, and the stage's LDS is free again
+    if (a.indices_out)
+      for (int j = threadIdx.x; j < nrows; j += kAttnThreads)
+        a.indices_out[(int64_t)t * a.k + j_begin + j] = lds_idx[j];
+    s0.load_idx_lds(lds_idx, 0);
+    s1.load_idx_lds(lds_idx, 1);
   }
   int64_t base;
   int n;
@@ -416,10 +468,14 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
       : Stage::kMx ? make_rsrc(static_cast<const uint8_t*>(a.kv_scale) + base * (kDQK / 32),
                                (uint32_t)max(n, 0) * (kDQK / 32))
                        : make_rsrc(a.kv, 0u);
+  auto load_idx = [&](Stage& sg, int tile) {
+    if constexpr (kSelect) sg.load_idx_lds(lds_idx, tile);
+    else sg.load_idx(idx_rs, tile);
+  };
   s0.load_rows(rows, scales, 0, nrows, n);
-  s0.load_idx(idx_rs, 2);
+  load_idx(s0, 2);
   s1.load_rows(rows, scales, 1, nrows, n);
-  s1.load_idx(idx_rs, 3);
+  load_idx(s1, 3);
 
   HalfState st;
   st.m_run = -INFINITY;
@@ -433,7 +489,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
   // tile 0 into region 0; its stage is refilled with tile 2
   s0.store(lds_tile[0], lds_flags[0]);
   s0.load_rows(rows, scales, 2, nrows, n);
-  s0.load_idx(idx_rs, 4);
+  load_idx(s0, 4);
   __syncthreads();
 
   // step i: store tile i+1 from its stage into region (i+1) % 3, refill the
@@ -444,7 +500,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a) {
     const int nxt = cur == 2 ? 0 : cur + 1;
     sg.store(lds_tile[nxt], lds_flags[nxt]);
     sg.load_rows(rows, scales, i + 3, nrows, n);
-    sg.load_idx(idx_rs, i + 5);
+    load_idx(sg, i + 5);
     const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds_tile[cur]);
     f32x4 part[2];
     if (i < ntiles) tile_partial_logits(tile, xbuf[i & 1], qb, lane, wave, half, part);
@@ -573,24 +629,32 @@ __global__ __launch_bounds__(256) void indexer_loss_kernel(LossArgs a) {
 
 }  // namespace
 
-hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s) {
+template <bool kProbs, bool kSelect>
+hipError_t launch_attn(const AttnArgs& a, const TopkArgs& ta, int fmt, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   dim3 grid(a.splits, a.num_tokens);
-  if (fmt == kFmtFp8) attn_kernel<kFmtFp8, false><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx) attn_kernel<kFmtMx, false><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4, false><<<grid, kAttnThreads, 0, s>>>(a);
-  else attn_kernel<kFmtBf16, false><<<grid, kAttnThreads, 0, s>>>(a);
+  if (fmt == kFmtFp8) attn_kernel<kFmtFp8, kProbs, kSelect><<<grid, kAttnThreads, 0, s>>>(a, ta);
+  else if (fmt == kFmtMx) attn_kernel<kFmtMx, kProbs, kSelect><<<grid, kAttnThreads, 0, s>>>(a, ta);
+  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4, kProbs, kSelect><<<grid, kAttnThreads, 0, s>>>(a, ta);
+  else attn_kernel<kFmtBf16, kProbs, kSelect><<<grid, kAttnThreads, 0, s>>>(a, ta);
   return hipGetLastError();
 }
 
+hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s) {
+  TopkArgs unused;
+  memset(&unused, 0, sizeof(unused));
+  return launch_attn<false, false>(a, unused, fmt, s);
+}
+
+hipError_t launch_attention_select(const AttnArgs& a, const TopkArgs& ta, int fmt, hipStream_t s) {
+  if (a.rows_per_split > kSelectMaxRows) return hipErrorInvalidValue;
+  return launch_attn<false, true>(a, ta, fmt, s);
+}
+
 hipError_t launch_attention_probs(const AttnArgs& a, int fmt, hipStream_t s) {
-  if (a.num_tokens == 0) return hipSuccess;
-  dim3 grid(a.splits, a.num_tokens);
-  if (fmt == kFmtFp8) attn_kernel<kFmtFp8, true><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx) attn_kernel<kFmtMx, true><<<grid, kAttnThreads, 0, s>>>(a);
-  else if (fmt == kFmtMx4) attn_kernel<kFmtMx4, true><<<grid, kAttnThreads, 0, s>>>(a);
-  else attn_kernel<kFmtBf16, true><<<grid, kAttnThreads, 0, s>>>(a);
-  return hipGetLastError();
+  TopkArgs unused;
+  memset(&unused, 0, sizeof(unused));
+  return launch_attn<true, false>(a, unused, fmt, s);
 }
 
 hipError_t launch_indexer_loss(const LossArgs& a, hipStream_t s) {

@@ -88,7 +88,10 @@ AttnPlan plan_attention(int32_t T, int32_t k) {
   const int tile = sga::kAttnTileRows;
   const int tiles = (k + tile - 1) / tile;
   int want = (T > 0) ? (256 + T - 1) / T : 1;   // aim for about 256 workgroups
-  int max_splits = tiles / 4 > 0 ? tiles / 4 : 1;  // at least 4 tiles per split
+  // at least 2 tiles per split: with fewer tokens than CUs the splits fill the
+  // GPU (measured: 2-tile splits beat 4-tile ones at 4 and 8 tokens; single
+  // tiles gain nothing and double the partials)
+  int max_splits = tiles / 2 > 0 ? tiles / 2 : 1;
   if (max_splits > 64) max_splits = 64;          // the combine merges at most 64 partials
   int splits = want < max_splits ? want : max_splits;
   if (splits < 1) splits = 1;
@@ -164,9 +167,10 @@ sga_status record(hipEvent_t e, hipStream_t s) {
   return hip_status(hipEventRecord(e, s));
 }
 
-sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
-                    int32_t* indices, const TopkLayout& L, bool hist_ready, hipStream_t stream) {
+TopkArgs topk_args(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
+                   int32_t* indices, const TopkLayout& L) {
   TopkArgs a;
+  memset(&a, 0, sizeof(a));
   a.batch = view_of(batch);
   a.num_tokens = batch->num_tokens;
   a.scores = scores;
@@ -183,14 +187,23 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
   a.cand_cap = L.cand_cap;
   a.wg_count = L.wg_count;
   a.max_select_wgs = L.max_select_wgs;
+  return a;
+}
+
+// One workgroup per token only when the batch alone fills the GPU.
+bool use_token_topk(int32_t T, const TopkLayout& L) {
+  return T >= kTokenTopkMinTokens && sga::topk_token_lds_cap(L.words) > 0;
+}
+
+sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
+                    int32_t* indices, const TopkLayout& L, bool hist_ready, hipStream_t stream) {
+  TopkArgs a = topk_args(batch, scores, ld, k, indices, L);
   if (!hist_ready) {
     SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
     SGA_HIP(sga::launch_topk_hist(a, stream));
   }
-  // one workgroup per token only when the batch alone fills the GPU
-  const int token_cap = batch->num_tokens >= kTokenTopkMinTokens ? sga::topk_token_lds_cap(L.words) : 0;
-  if (token_cap > 0) {
-    a.lds_cand_cap = token_cap;
+  if (use_token_topk(batch->num_tokens, L)) {
+    a.lds_cand_cap = sga::topk_token_lds_cap(L.words);
     SGA_HIP(sga::launch_topk_token(a, stream));
   } else {
     a.lds_cand_cap = 0;
@@ -200,11 +213,11 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
   return SGA_OK;
 }
 
-sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* kv,
-                         const void* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
-                         int32_t k, float sm_scale, const float* gate, float* out, float* lse,
-                         const AttnPlan& plan, const AttnLayout& L, hipStream_t stream) {
+AttnArgs attn_args(const sga_batch* batch, const void* q_abs, const void* kv, const void* kv_scale,
+                   const int32_t* indices, int32_t k, float sm_scale, const float* gate, float* out,
+                   float* lse, const AttnPlan& plan, const AttnLayout& L) {
   AttnArgs a;
+  memset(&a, 0, sizeof(a));
   a.batch = view_of(batch);
   a.num_tokens = batch->num_tokens;
   a.q_abs = static_cast<const uint16_t*>(q_abs);
@@ -220,6 +233,14 @@ sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* 
   a.rows_per_split = plan.rows_per_split;
   a.part_o = L.part_o;
   a.part_ml = L.part_ml;
+  return a;
+}
+
+sga_status run_attention(const sga_batch* batch, const void* q_abs, const void* kv,
+                         const void* kv_scale, sga_dtype kv_dtype, const int32_t* indices,
+                         int32_t k, float sm_scale, const float* gate, float* out, float* lse,
+                         const AttnPlan& plan, const AttnLayout& L, hipStream_t stream) {
+  const AttnArgs a = attn_args(batch, q_abs, kv, kv_scale, indices, k, sm_scale, gate, out, lse, plan, L);
   SGA_HIP(sga::launch_attention(a, (int)kv_dtype, stream));
   SGA_HIP(sga::launch_combine(a, stream));
   return SGA_OK;
@@ -468,10 +489,24 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   else
     SGA_HIP(sga::launch_indexer(ia, (int)k_idx_dtype, true, stream));
   if (trace) SGA_TRY(record(trace->indexer_end, stream));
-  SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
-  if (trace) SGA_TRY(record(trace->topk_end, stream));
-  SGA_TRY(run_attention(batch, q_abs, kv, kv_scale, kv_dtype, indices, k, sm_scale, gate_logits,
-                        out, lse, plan, AL, stream));
+  if (!use_token_topk(T, TL) && plan.rows_per_split <= sga::kSelectMaxRows &&
+      TL.words <= sga::kSelectMaxWords) {
+    // the top-k's final stage runs inside the attention kernel: each split
+    // takes its own rows of the selection (and writes them to indices_out)
+    const TopkArgs ta = topk_args(batch, scores, batch->max_len, k, nullptr, TL);
+    SGA_HIP(sga::launch_topk_select(ta, stream));
+    if (trace) SGA_TRY(record(trace->topk_end, stream));
+    AttnArgs aa = attn_args(batch, q_abs, kv, kv_scale, nullptr, k, sm_scale, gate_logits, out, lse,
+                            plan, AL);
+    aa.indices_out = indices_out;
+    SGA_HIP(sga::launch_attention_select(aa, ta, (int)kv_dtype, stream));
+    SGA_HIP(sga::launch_combine(aa, stream));
+  } else {
+    SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
+    if (trace) SGA_TRY(record(trace->topk_end, stream));
+    SGA_TRY(run_attention(batch, q_abs, kv, kv_scale, kv_dtype, indices, k, sm_scale, gate_logits,
+                          out, lse, plan, AL, stream));
+  }
   if (trace) SGA_TRY(record(trace->attn_end, stream));
   return SGA_OK;
 }

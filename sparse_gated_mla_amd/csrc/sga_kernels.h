@@ -9,10 +9,12 @@
 namespace sga {
 
 // Per-token top-k control block in the workspace, written by the first select
-// workgroup of the token.
+// workgroup of the token (16 bytes: the final stage reads it in one vector load).
 struct TopkCtrl {
   uint32_t digit1;      // top 12 key bits of the k-th largest score
   uint32_t above1;      // scores whose top 12 key bits exceed digit1
+  uint32_t visible;     // the token's visible positions n (written even when n <= k)
+  uint32_t pad;
 };
 
 // Cache element formats (the values of sga_dtype).
@@ -33,6 +35,7 @@ __host__ __device__ constexpr int indexer_chunk(bool fp8) { return fp8 ? 2 * kIn
 constexpr int kSelectChunk = 4096;    // positions per select workgroup
 constexpr int kMaxSelectWgs = 128;    // select workgroups of the longest context (512K)
 constexpr int kAttnTileRows = 32;     // latent rows per attention tile
+constexpr int kMaxLenRows = 1 << 19;  // longest visible context (SGA_MAX_LEN)
 
 struct IndexerArgs {
   BatchView batch;
@@ -83,6 +86,7 @@ struct AttnArgs {
   const float* gate;       // [T,64] or null
   float* out;              // [T,64,512]
   float* lse;              // [T,64] or null
+  int32_t* indices_out;    // [T,k] or null: the selecting kernel writes the rows it attends
   int splits;              // row splits per token
   int rows_per_split;      // multiple of kAttnTileRows
   uint16_t* part_o;        // [T,splits,32 column blocks,64 heads,16] fp16, normalised
@@ -163,6 +167,15 @@ int topk_token_lds_cap(int64_t words);       // 0: use the multi-kernel top-k
 hipError_t launch_topk_token(const TopkArgs& a, hipStream_t s);
 hipError_t launch_attention(const AttnArgs& a, int fmt, hipStream_t s);
 hipError_t launch_combine(const AttnArgs& a, hipStream_t s);
+// The attention kernel that first takes its own rows of each token's top-k
+// from the select kernel's output (the top-k's final stage runs inside it).
+constexpr int kSelectMaxRows = 2048;   // split rows whose indices it holds in LDS
+// Used up to 4,096 bitmap words (contexts of 128K): the final stage's work grows
+// with the context, and beyond that the separate finalize kernel, with twice the
+// threads per token, was measured faster (256K: 23.3 us for the two kernels
+// against 25.0 us fused).
+constexpr int64_t kSelectMaxWords = 4096;
+hipError_t launch_attention_select(const AttnArgs& a, const TopkArgs& ta, int fmt, hipStream_t s);
 hipError_t launch_attention_probs(const AttnArgs& a, int fmt, hipStream_t s);
 hipError_t launch_indexer_loss(const LossArgs& a, hipStream_t s);
 

@@ -26,6 +26,7 @@
 //      positions in ascending order, ties at the k-th key lowest position first.
 // Every decision depends only on the score values, so the result is exact.
 #include "sga_block.h"
+#include "sga_finalize.h"
 #include "sga_kernels.h"
 
 namespace sga {
@@ -79,6 +80,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   int64_t base;
   int n;
   a.batch.token(t, base, n);
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.ctrl[t].visible = (uint32_t)n;
   if (n <= a.k) return;  // every visible position is kept; finalize writes them
   if (c0 >= n) return;
   const int c1 = min(n, c0 + kSelectChunk);
@@ -132,266 +134,27 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
 }
 
-// Dynamic LDS: staged output (4096 words) | level-3 histogram or short key
-// list (256) | scratch (64) | per-chunk selected and tie counts
-// (2 * kMaxSelectWgs) | tie bitmap (words) | selection bitmap (words).
+// One workgroup per token runs the final stage (sga_finalize.h) and writes the
+// k kept positions, staged in LDS for coalesced stores when k <= 4096.
+// Dynamic LDS: staged output (4096 words) | the stage's finalize_lds_words.
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
-  constexpr int kFinWaves = kFinThreads / 64;
-  constexpr int kPreSlices = 4;   // slices per wave held in registers: 256K positions
-  constexpr int kChunkWords = kSelectChunk / 32;   // bitmap words of one select chunk
-  static_assert(kChunkWords == 128 && kMaxSelectWgs <= 128, "two words and two chunks per lane");
   uint32_t* out_stage = lds;
-  uint32_t* hist3 = out_stage + kHist2;
-  uint32_t* scratch = hist3 + kHist3;
-  uint32_t* chunk_cnt = scratch + 64;
-  uint32_t* tie = chunk_cnt + 2 * kMaxSelectWgs;
-  uint32_t* selL = tie + a.words;
-  uint32_t* n_few = scratch + 40;   // short-list length, then the k-th key and ties kept
   const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  // One round of loads, issued before the batch metadata (scalar loads): the
-  // cut, the digit-2 histogram, the first 4 * kFinThreads words of the
-  // selection bitmap and, for wave w, the lengths of candidate slices
-  // w + q * kFinWaves (q < kPreSlices) with their first 128 entries. All lie
-  // inside this token's workspace rows; entries past the token's own are
-  // loaded and not used.
-  // (The cut is a per-lane vector load, lanes 0 and 1 reading its two words:
-  // a uniform scalar load would be sunk past the metadata's branch.)
-  static_assert(offsetof(TopkCtrl, above1) == offsetof(TopkCtrl, digit1) + sizeof(uint32_t),
-                "the cut's two words are adjacent");
-  const uint32_t ctrl_word = (&a.ctrl[t].digit1)[threadIdx.x & 1];
-  HistRun<kFinThreads, kHist2> h2;
-  h2.load(a.hist2 + (int64_t)t * kHist2);
-  const uint32_t* sel = a.sel + (int64_t)t * a.words;
-  uint32_t w[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) w[u] = sel[min(u * kFinThreads + (int)threadIdx.x, (int)a.words - 1)];
-  const uint32_t* gpos = a.cand + (int64_t)t * a.cand_cap;
-  const uint32_t* gkey = a.cand_key + (int64_t)t * a.cand_cap;
-  const uint32_t* wgc = a.wg_count + (int64_t)t * a.max_select_wgs;
-  // the wave index as a uniform value: branches on it stay scalar and leave t
-  // uniform (a divergent branch here would turn the metadata loads into
-  // vector loads)
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t clen[kPreSlices], cpos[kPreSlices][2], ckey[kPreSlices][2];
-#pragma unroll
-  for (int q = 0; q < kPreSlices; ++q) {
-    const int x = wv + q * kFinWaves;
-    clen[q] = 0;
-    if (x < a.max_select_wgs) {
-      const int64_t o = (int64_t)x * kSelectChunk + lane;
-      clen[q] = wgc[x];
-      cpos[q][0] = gpos[o];
-      ckey[q][0] = gkey[o];
-      cpos[q][1] = gpos[o + 64];
-      ckey[q][1] = gkey[o + 64];
-    }
-  }
-  int64_t base;
-  int n;
-  a.batch.token(t, base, n);
+  TokenFinalize<kFinThreads> fin;
+  fin.prefetch(a, t);
+  const int n = fin.visible();   // recorded by the select kernel
   int32_t* out = a.indices + (int64_t)t * a.k;
   if (n <= a.k) {
     for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = i < n ? i : -1;
     return;
   }
-  const int nsel = (n + kSelectChunk - 1) / kSelectChunk;
-  const int words = (n + 31) >> 5;
-  const uint32_t d1 = __builtin_amdgcn_readlane(ctrl_word, 0);
-  const uint32_t r1 = (uint32_t)a.k - __builtin_amdgcn_readlane(ctrl_word, 1);  // still needed from the candidates
-  for (int i0 = 0; i0 < words; i0 += 4 * kFinThreads) {
-    if (i0 > 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = sel[min(i0 + u * kFinThreads + (int)threadIdx.x, words - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + u * kFinThreads + threadIdx.x;
-      if (i < words) {
-        selL[i] = w[u];
-        tie[i] = 0;
-      }
-    }
-  }
-  for (int b = threadIdx.x; b < kHist3; b += kFinThreads) hist3[b] = 0;
-  if (threadIdx.x == 0) *n_few = 0;
-  // level 2, from the histogram the select kernel counted (the cut's barriers
-  // also publish the LDS stores above)
-  uint32_t d2, above2, n3;   // n3: candidates with digit d2, usually a handful
-  h2.cut(r1, scratch, d2, above2, n3);
-  const uint32_t r2 = r1 - above2;
-
-  // Calls f(position, key) for every candidate of this wave's slices x = wave,
-  // wave + kFinWaves, ...: the first 128 entries of the first kPreSlices from
-  // registers, the rest from global memory, four per lane per round.
-  auto each_candidate = [&](auto&& f) {
-    auto from_global = [&](int x, uint32_t j0, uint32_t len) {
-      const uint32_t* sp = gpos + (int64_t)x * kSelectChunk;
-      const uint32_t* sk = gkey + (int64_t)x * kSelectChunk;
-      for (; j0 < len; j0 += 256) {
-        uint32_t pp[4], kk[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const uint32_t j = min(j0 + 64 * u + lane, len - 1);
-          pp[u] = sp[j];
-          kk[u] = sk[j];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (j0 + 64 * u + lane < len) f(pp[u], kk[u]);
-      }
-    };
-#pragma unroll
-    for (int q = 0; q < kPreSlices; ++q) {
-      const int x = wv + q * kFinWaves;
-      if (x < nsel) {
-        const uint32_t len = clen[q];
-        if ((uint32_t)lane < len) f(cpos[q][0], ckey[q][0]);
-        if ((uint32_t)lane + 64 < len) f(cpos[q][1], ckey[q][1]);
-        from_global(x, 128, len);
-      }
-    }
-    for (int x = wv + kPreSlices * kFinWaves; x < nsel; x += kFinWaves) from_global(x, 0, wgc[x]);
-  };
-
-  // level 3: the keys with digit d2 into a short list (at most 64) or their
-  // low 8 bits into a histogram
-  each_candidate([&](uint32_t, uint32_t key) {
-    if (((key >> kDigit3Bits) & (kHist2 - 1)) != d2) return;
-    if (n3 <= 64) hist3[atomicAdd(n_few, 1u)] = key;
-    else atomicAdd(&hist3[key & (kHist3 - 1)], 1u);
-  });
-  __syncthreads();
-  uint32_t kth, ties_kept;   // the k-th key and how many positions holding it to keep
-  if (n3 <= 64) {
-    if (wave == 0) {
-      // lane l holds key l; it counts the keys above it and those not below it
-      const uint32_t mine = lane < (int)n3 ? hist3[lane] : 0u;
-      uint32_t gt = 0, ge = 0;
-      for (int j = 0; j < (int)n3; ++j) {
-        const uint32_t other = __builtin_amdgcn_readlane(mine, j);
-        gt += other > mine;
-        ge += other >= mine;
-      }
-      if (lane < (int)n3 && gt < r2 && r2 <= ge) {   // the lanes holding the k-th key agree
-        n_few[1] = mine;
-        n_few[2] = r2 - gt;
-      }
-    }
-    __syncthreads();
-    kth = n_few[1];
-    ties_kept = n_few[2];
-  } else {
-    uint32_t d3, above3;
-    block_cut<kFinThreads>(hist3, kHist3, r2, scratch, d3, above3);
-    ties_kept = r2 - above3;
-    kth = (d1 << (32 - kDigit1Bits)) | (d2 << kDigit3Bits) | d3;
-  }
-
-  // Candidates above the k-th key join the selection; ties at it are marked
-  // apart. Slice x holds the candidates of bitmap chunk x (kChunkWords words,
-  // positions [x * kSelectChunk, (x + 1) * kSelectChunk)), so wave x mod
-  // kFinWaves marks only inside its own chunks.
-  each_candidate([&](uint32_t p, uint32_t key) {
-    if (key >= kth) atomicOr(key > kth ? &selL[p >> 5] : &tie[p >> 5], 1u << (p & 31));
-  });
   int32_t* staged_out = reinterpret_cast<int32_t*>(out_stage);   // k <= kHist2: the output goes out coalesced
   const bool stage_out = a.k <= kHist2;
-  // Keeps the selected positions of word i and its ties while fewer than
-  // ties_kept lower ties were kept; o is the output slot of the word's first
-  // kept position, ties_seen the ties before it.
-  auto emit_word = [&](int i, uint32_t sbits, uint32_t tbits_all, uint32_t& o, uint32_t& ties_seen) {
-    uint32_t tbits = tbits_all;
-    if (ties_seen >= ties_kept) {
-      tbits = 0;
-    } else if (ties_seen + __popc(tbits) > ties_kept) {
-      uint32_t keep = ties_kept - ties_seen, nb = 0;   // the lowest `keep` ties of this word
-      for (; keep; --keep) {
-        const uint32_t low = tbits & (0u - tbits);
-        nb |= low;
-        tbits ^= low;
-      }
-      tbits = nb;
-    }
-    ties_seen += __popc(tbits_all);
-    uint32_t bits = sbits | tbits;
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      bits &= bits - 1;
-      if (o < (uint32_t)a.k) {
-        if (stage_out) staged_out[o] = (i << 5) + b;
-        else out[o] = (i << 5) + b;
-      }
-      ++o;
-    }
-  };
-  if (nsel >= kFinWaves) {
-    // Long contexts: the wave that marked a chunk also counts and emits it,
-    // with no barrier in between (a wave's LDS operations complete in order);
-    // lane l holds words 2l and 2l + 1 of the chunk. One barrier publishes the
-    // chunk counts.
-    auto chunk_words = [&](int x, uint32_t (&sw)[2], uint32_t (&tw)[2]) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int i = x * kChunkWords + 2 * lane + u;
-        sw[u] = i < words ? selL[i] : 0u;
-        tw[u] = i < words ? tie[i] : 0u;
-      }
-    };
-    for (int x = wv; x < nsel; x += kFinWaves) {
-      uint32_t sw[2], tw[2];
-      chunk_words(x, sw, tw);
-      const uint32_t ss = wave_incl_scan(__popc(sw[0]) + __popc(sw[1]));
-      const uint32_t ts = wave_incl_scan(__popc(tw[0]) + __popc(tw[1]));
-      if (lane == 63) {
-        chunk_cnt[x] = ss;
-        chunk_cnt[kMaxSelectWgs + x] = ts;
-      }
-    }
-    __syncthreads();
-    // the chunks' exclusive prefix sums, lane l holding chunks 2l and 2l + 1
-    const uint32_t cs0 = 2 * lane < nsel ? chunk_cnt[2 * lane] : 0u;
-    const uint32_t cs1 = 2 * lane + 1 < nsel ? chunk_cnt[2 * lane + 1] : 0u;
-    const uint32_t ct0 = 2 * lane < nsel ? chunk_cnt[kMaxSelectWgs + 2 * lane] : 0u;
-    const uint32_t ct1 = 2 * lane + 1 < nsel ? chunk_cnt[kMaxSelectWgs + 2 * lane + 1] : 0u;
-    const uint32_t cs_excl = wave_incl_scan(cs0 + cs1) - (cs0 + cs1);
-    const uint32_t ct_excl = wave_incl_scan(ct0 + ct1) - (ct0 + ct1);
-    for (int x = wv; x < nsel; x += kFinWaves) {
-      const int L = x >> 1;
-      uint32_t s_before = __builtin_amdgcn_readlane(cs_excl, L);
-      uint32_t t_before = __builtin_amdgcn_readlane(ct_excl, L);
-      if (x & 1) {
-        s_before += __builtin_amdgcn_readlane(cs0, L);
-        t_before += __builtin_amdgcn_readlane(ct0, L);
-      }
-      uint32_t sw[2], tw[2];
-      chunk_words(x, sw, tw);
-      const uint32_t s2 = __popc(sw[0]) + __popc(sw[1]), t2 = __popc(tw[0]) + __popc(tw[1]);
-      s_before += wave_incl_scan(s2) - s2;
-      t_before += wave_incl_scan(t2) - t2;
-      uint32_t o = s_before + min(t_before, ties_kept);
-      uint32_t ties_seen = t_before;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) emit_word(x * kChunkWords + 2 * lane + u, sw[u], tw[u], o, ties_seen);
-    }
-  } else {
-    // Short contexts (fewer chunks than waves): every thread takes a run of
-    // words, and a block scan gives each run its output slot.
-    __syncthreads();
-    const int per = (words + kFinThreads - 1) / kFinThreads;
-    const int w0 = min(words, (int)threadIdx.x * per), w1 = min(words, w0 + per);
-    uint32_t ns = 0, nt = 0;
-    for (int i = w0; i < w1; ++i) {
-      ns += __popc(selL[i]);
-      nt += __popc(tie[i]);
-    }
-    uint32_t s_before, t_before;
-    block_excl_scan2<kFinThreads>(ns, nt, scratch, s_before, t_before);
-    uint32_t o = s_before + min(t_before, ties_kept);
-    uint32_t ties_seen = t_before;
-    for (int i = w0; i < w1; ++i) emit_word(i, selL[i], tie[i], o, ties_seen);
-  }
+  fin.run(a, n, out_stage + kHist2, 0u, (uint32_t)a.k, [&](uint32_t o, uint32_t p) {
+    if (stage_out) staged_out[o] = (int32_t)p;
+    else out[o] = (int32_t)p;
+  });
   if (stage_out) {
     __syncthreads();
     for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = staged_out[i];
@@ -651,7 +414,7 @@ hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)topk_finalize_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)kFinalizeLds);
   if (e != hipSuccess) return e;
-  const size_t lds = (size_t)(kHist2 + kHist3 + 64 + 2 * kMaxSelectWgs + 2 * a.words) * sizeof(uint32_t);
+  const size_t lds = (size_t)(kHist2 + finalize_lds_words(a.words)) * sizeof(uint32_t);
   if (lds > kFinalizeLds) return hipErrorInvalidValue;
   topk_finalize_kernel<<<a.num_tokens, kFinThreads, lds, s>>>(a);
   return hipGetLastError();
