@@ -40,12 +40,13 @@
  *   e = 255 (NaN) is not a valid exponent. The kernels widen payload * 2^(e-127)
  *   to bf16, which is exact while the products are bf16 normals or zero, so
  *   every exponent of a nonzero block must be at least 10 (scale >= 2^-117);
- *   below that the smallest values lose bits.
+ *   below that the smallest values lose bits. It must also be at most 200
+ *   (values below 2^82), so that fp32 sums over up to 65,536 rows stay finite.
  * - SGA_MXFP4_E2M1 is the same block-32 form with OCP E2M1 elements (values
  *   0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives), two per byte, element
  *   2i in the low nibble of byte i: 64 payload bytes per indexer key row and
  *   288 per latent row, with the same exponent arrays. Exponents of nonzero
- *   blocks must be at least 2 (scale >= 2^-125).
+ *   blocks must lie in [2, 200] (scale >= 2^-125; values below 2^76).
  */
 #ifndef SGA_H
 #define SGA_H
@@ -196,7 +197,11 @@ SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t
  *   for bf16. indices [T,k] int32.
  *   out [T,64,512] fp32. lse [T,64] fp32 or NULL.
  * Logits and softmax are fp32. Probabilities enter the value product as
- * bf16, and accumulation is fp32.
+ * bf16, and accumulation is fp32. When a token's rows are split over several
+ * workgroups, each split's normalised output is held in fp16, scaled per head
+ * and 256-column half by its largest magnitude: a column then carries, beside
+ * the relative rounding, an absolute error below 2^-25 of the largest value
+ * in its half of the selected rows.
  */
 SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k);
 SGA_API sga_status sga_sparse_mla_attn(const sga_batch* batch, const void* q_abs, const void* kv,

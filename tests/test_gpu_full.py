@@ -32,8 +32,11 @@ def test_chunked_prefill_sampled():
     dev = Dev(wl)
     idx, out, lse = dev.forward()
     del dev
-    # sample: first, last and evenly spaced tokens of the 8192-token chunk
-    sample = sorted({0, 1, 4095, 8190, 8191, *range(0, 8192, 1024)})
+    # sample: first, last and evenly spaced tokens of the 8192-token chunk, and
+    # eight consecutive tokens at eight places, so every one of the eight
+    # token slots of the prefill indexer's workgroup is checked
+    sample = sorted({0, 1, 4095, 8190, 8191, *range(0, 8192, 1024),
+                     *(1024 * i + j for i in range(8) for j in range(8))})
     ref = run_oracle(wl, tokens=sample)
     got_idx = idx.cpu().numpy()[sample]
     assert np.array_equal(got_idx, ref["indices"])

@@ -404,3 +404,132 @@ def test_prefill_mx4():
     pos = sorted(rng.choice(4200, size=70, replace=False).tolist())
     wl = si.build("prefill_mx4", [4200], [(0, p) for p in pos], seed=28, mx4=True)
     _check_forward(wl)
+
+
+# ------------------------------------------------------------------ k above 4096
+def test_k_6000_two_tokens():
+    # two tokens: the select kernels and the top-k stage inside the attention
+    # (47 splits, so the merge takes three rounds); the standalone top-k on the
+    # oracle's scores stores its output unstaged (k > 4096)
+    wl = si.build("k6000_t2", [20000], [(0, 19999), (0, 15000)], seed=35, k=6000)
+    _, (idx, _, _), ref = _check_forward(wl)
+    say("[topk] k=6000, oracle scores, select + finalize")
+    ref_s = run_oracle(wl, keep_scores=True)
+    sc = torch.full((wl.num_tokens, wl.max_len), float("nan"))
+    for i, r in enumerate(ref_s["scores"]):
+        sc[i, :r.shape[0]] = torch.from_numpy(r.astype(np.float32))
+    got = Dev(wl).topk(sc.cuda()).cpu().numpy()
+    assert np.array_equal(got, ref["indices"])
+
+
+def test_k_6000_many_tokens():
+    # 512 tokens: one workgroup per token selects, one split per token
+    rng = np.random.default_rng(36)
+    pos = np.sort(rng.integers(0, 20000, 512))
+    pos[-1] = 19999
+    pos[:8] = np.arange(8)          # a few tokens with fewer positions than k
+    wl = si.build("k6000_t512", [20000], [(0, int(p)) for p in pos], seed=36, k=6000)
+    _check_forward(wl)
+
+
+def test_k_65536_at_100k():
+    # the largest k: 64 splits of 1,024 rows, merged in four rounds
+    wl = si.build("k65536", [100000], [(0, 99999), (0, 70000)], seed=37, k=65536)
+    _check_forward(wl)
+    say("[topk] k=65536, oracle scores, select + finalize")
+    ref_s = run_oracle(wl, keep_scores=True)
+    sc = torch.full((wl.num_tokens, wl.max_len), float("nan"))
+    for i, r in enumerate(ref_s["scores"]):
+        sc[i, :r.shape[0]] = torch.from_numpy(r.astype(np.float32))
+    got = Dev(wl).topk(sc.cuda()).cpu().numpy()
+    assert np.array_equal(got, ref_s["indices"])
+
+
+# ------------------------------------------- MX block exponents over their range
+MX_EXP_MIN = {"mx": 10, "mx4": 2}
+MX_EXP_MAX = 200
+
+
+def _mx_build(fmt, name, lengths, tokens, seed, **kw):
+    return si.build(name, lengths, tokens, seed, mx=fmt == "mx", mx4=fmt == "mx4", **kw)
+
+
+@pytest.mark.parametrize("fmt", ["mx", "mx4"])
+def test_mx_attention_exponent_range_single_rows(fmt):
+    # every block exponent of the latent rows drawn over the whole accepted
+    # range; each of 256 tokens (one split each) attends to a single row, so its
+    # output is that row's decoded values, exactly, and its lse is 0
+    T, k = 256, 64
+    wl = _mx_build(fmt, f"{fmt}_exp_rows", [4096], [(0, 4095)] * T, 38, k=k)
+    rng = np.random.default_rng(38)
+    e = rng.integers(MX_EXP_MIN[fmt], MX_EXP_MAX + 1, size=tuple(wl.kv_scale.shape))
+    wl.kv_scale = torch.from_numpy(e.astype(np.uint8))
+    wl.q_abs.zero_()
+    rows = rng.choice(4096, size=T, replace=False)
+    ind = np.full((T, k), -1, dtype=np.int32)
+    ind[np.arange(T), rng.integers(0, k, size=T)] = rows
+    say(f"[attention] {fmt} rows, block exponents {MX_EXP_MIN[fmt]}..{MX_EXP_MAX}, one row per token")
+    out, lse = Dev(wl).attention(torch.from_numpy(ind).cuda(), gate=False)
+    _, vs = stores(wl)
+    got, got_lse = out.cpu().numpy().astype(np.float64), lse.cpu().numpy()
+    for t in range(T):
+        o, l = oracle.sparse_mla(wl.q_abs[t].double().numpy(), vs.rows(rows[t:t + 1]), wl.sm_scale)
+        assert np.array_equal(got[t], o), f"token {t}"
+        assert np.array_equal(got_lse[t], l), f"token {t}"
+
+
+@pytest.mark.parametrize("fmt", ["mx", "mx4"])
+def test_mx_attention_exponent_range_oracle_indices(fmt):
+    # the first 256 latent columns (values only: their query columns are zero)
+    # take block exponents over the whole accepted range; the rest keep the
+    # usual ones. Two tokens, 16 splits each: every column is held to its
+    # error bound, 2^-8 of sum_j p_j |v_j| plus 2^-24 of the largest |v| in its
+    # half of the selected rows (the fp16 partials)
+    wl = _mx_build(fmt, f"{fmt}_exp_attn", [6000], [(0, 5999), (0, 3000)], 39)
+    rng = np.random.default_rng(39)
+    e = wl.kv_scale.numpy().copy()
+    e[:, :8] = rng.integers(MX_EXP_MIN[fmt], MX_EXP_MAX + 1, size=(e.shape[0], 8))
+    wl.kv_scale = torch.from_numpy(e)
+    wl.q_abs[:, :, :256] = 0
+    ref = run_oracle(wl, gate=False)
+    say(f"[attention] {fmt} rows, value-block exponents {MX_EXP_MIN[fmt]}..{MX_EXP_MAX}, oracle indices")
+    out, lse = Dev(wl).attention(torch.from_numpy(ref["indices"]).cuda(), gate=False)
+    assert_lse_close(lse.cpu().numpy(), ref["lse"], f"{fmt} exponent range")
+    got = out.cpu().numpy().astype(np.float64)
+    _, vs = stores(wl)
+    for t in range(wl.num_tokens):
+        kept = ref["indices"][t][ref["indices"][t] >= 0].astype(np.int64)
+        v = vs.rows(int(wl.seq_start[wl.token_seq[t]]) + kept)
+        z = wl.sm_scale * (wl.q_abs[t].double().numpy() @ v.T)
+        p = np.exp(z - z.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        a = p @ np.abs(v[:, :512])
+        half_max = np.repeat([np.abs(v[:, :256]).max(), np.abs(v[:, 256:512]).max()], 256)
+        bound = 2.0 ** -8 * a + 2.0 ** -24 * half_max[None, :] + 2.0 ** -140
+        err = np.abs(got[t] - ref["out"][t])
+        assert np.all(err <= bound), (fmt, t, float((err / bound).max()))
+
+
+@pytest.mark.parametrize("fmt", ["mx", "mx4"])
+def test_mx_index_scores_exponent_range(fmt):
+    # each key row keeps one nonzero 32-element block, whose exponent is drawn
+    # over the whole accepted range: every score is still an exact sum of
+    # same-scale integers, so scores and indices match bit for bit
+    wl = _mx_build(fmt, f"{fmt}_key_exps", [3000, 900], [(0, 2999), (1, 899), (0, 100)], 40)
+    rng = np.random.default_rng(40)
+    rows = wl.k_idx.shape[0]
+    keep = rng.integers(0, 4, size=rows)
+    raw = wl.k_idx.view(torch.uint8).numpy().copy()
+    per_block = raw.shape[1] // 4
+    for b in range(4):
+        raw[keep != b, b * per_block:(b + 1) * per_block] = 0      # +0 in both element codes
+    e = rng.integers(MX_EXP_MIN[fmt], MX_EXP_MAX + 1, size=(rows, 4))
+    wl.k_idx = torch.from_numpy(raw).view(wl.k_idx.dtype)
+    wl.k_idx_scale = torch.from_numpy(e.astype(np.uint8))
+    say(f"[index_scores] {fmt} keys, block exponents {MX_EXP_MIN[fmt]}..{MX_EXP_MAX}")
+    s = Dev(wl).scores().cpu().numpy()
+    ref = run_oracle(wl, keep_scores=True)
+    for i, r in enumerate(ref["scores"]):
+        n = r.shape[0]
+        assert np.array_equal(s[i, :n].astype(np.float64), r), f"token {i}"
+    _check_forward(wl, what=f"{fmt} keys over the exponent range")
