@@ -11,15 +11,21 @@ previous step's data in the 256 MB Infinity Cache.
 
 Prints one JSON line with:
 - query-tokens/s;
-- roofline: the indexer kernel, timed with HIP events on the library's stream
-  inside the timed steps (one step in EVENT_EVERY records them; they are the
-  only events the timed steps record), against the 8 TB/s HBM peak. The
-  algorithmic bytes
-  are the indexer keys it must read plus its query inputs. For a chunked
-  prefill, where thousands of tokens share one sequence's keys, the roof is
-  the 2.5 PFLOP/s dense bf16 MFMA peak instead;
+- roofline: the dominant kernel, the indexer, timed with HIP events on the
+  library's stream inside the timed steps (one step in EVENT_EVERY records
+  them; they are the only events the timed steps record), against the 8 TB/s
+  HBM peak. The algorithmic bytes are the indexer keys it must read plus its
+  query inputs. For a chunked prefill, where thousands of tokens share one
+  sequence's keys, the roof is the 2.5 PFLOP/s dense bf16 MFMA peak instead.
+  Beside it: the whole step against the same peak (roofline.step), the
+  bandwidth a plain 1 GiB device copy and sum reach here, and, when the
+  committed rocprofv3 counter summary matches the kernel sources, the HBM
+  traffic and the MFMA utilisation per kernel;
 - cpu_baseline: the float64 CPU oracle, timed on this host over whole batches
   of the same workload.
+
+The timed steps start after W warm-up steps and at least --settle-seconds of
+untimed steps, so a short warm-up still times settled clocks.
 """
 from __future__ import annotations
 
@@ -48,12 +54,13 @@ WORKLOADS = {"tiny_decode_4k": 0, "batched_decode_ragged_16k_32k": 1, "long_deco
              "chunked_prefill_128k": 3,
              "extended_decode_256k_fp8": 4, "extended_decode_256k_mxfp8": 5,
              "extended_decode_256k_mxfp4": 6}
-PMC_WORKLOAD = "long_decode_128k"
 EVENT_EVERY = 4                     # timed steps per step that times the indexer
-PMC_FILE = os.path.join(ROOT, "profiles", "indexer_long_decode_128k_pmc.json")
-# the sources the indexer kernel is built from
-INDEXER_SRC = [os.path.join(ROOT, "sparse_gated_mla_amd", "csrc", f)
-               for f in ("indexer.hip", "sga_kernels.h", "sga_device.h", "sga_block.h")]
+SIMD_NUM = 1024                     # 256 compute units x 4 SIMDs
+CSRC = os.path.join(ROOT, "sparse_gated_mla_amd", "csrc")
+
+
+def pmc_file(workload: str) -> str:
+    return os.path.join(ROOT, "profiles", f"pmc_{workload}.json")
 
 
 # ---------------------------------------------------------------- HIP events
@@ -245,74 +252,125 @@ def time_indexer_loss(wl, s, idx, lse, ev, reps: int) -> dict:
 
 # ---------------------------------------------------------------- traffic
 def src_digest() -> str:
+    """Digest of every kernel source: counter figures taken on other sources are stale."""
     h = hashlib.sha256()
-    for p in INDEXER_SRC:
-        with open(p, "rb") as f:
-            h.update(f.read())
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per indexer launch from the committed rocprofv3 counter summary,
-    or None when it is missing or was taken on a different indexer source."""
+def counter_summary(workload: str):
+    """The committed rocprofv3 counter summary of a workload, or None when it is
+    missing or was taken on different kernel sources."""
     try:
-        with open(PMC_FILE) as f:
+        with open(pmc_file(workload)) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("indexer_source_sha256_16") != src_digest():
-        return None
-    return d.get("traffic_bytes_per_launch")
+    return d if d.get("csrc_sha256_16") == src_digest() else None
 
 
-def summarize_pmc(root: str) -> dict:
-    """Writes the indexer's HBM traffic summary from rocprofv3 counter runs.
+def kernel_key(name: str) -> str:
+    """A kernel's short name, with its template arguments: 'attn_kernel<0, false, true>'."""
+    import re
+    m = re.search(r"(\w+_kernel|copyBuffer)(<[^>]*>)?", name)
+    return m.group(0) if m else name[:40]
 
-    `root` holds one rocprofv3 output folder per pass: a FETCH_SIZE pass and a
-    WRITE_SIZE pass over a short bench run, and the same two counters over
-    `--copy-calibration` (five copies of 1 GiB). Both counters read KiB per
-    dispatch; each is scaled by the bytes a known copy moves over what the
-    counter reads for that copy."""
+
+def summarize_pmc(root: str, workload: str) -> dict:
+    """Writes a workload's per-kernel counter summary from rocprofv3 runs.
+
+    `root` holds one rocprofv3 output folder per pass (each `-o run`):
+    fetch/ and write/ (FETCH_SIZE, WRITE_SIZE over a short bench run),
+    copy_fetch/ and copy_write/ (the same counters over `--copy-calibration`,
+    five copies of 1 GiB) and mfma/ (MfmaUtil with its inputs and the bf16
+    MFMA op count). FETCH_SIZE and WRITE_SIZE read KiB per dispatch; each is
+    scaled by the bytes the known copy moves over what the counter reads for
+    it. MfmaUtil is rocprofv3's derived counter: the summed MFMA-busy cycles of
+    all SIMDs over the busiest XCD's active cycles times the SIMD count."""
     import csv
-    import glob
-    per = {}                        # (run, kernel, counter) -> values per dispatch
-    for f in glob.glob(os.path.join(root, "*", "*counter_collection.csv")):
+    per = {}                        # (pass, kernel, counter) -> values per dispatch
+    for pas in ("fetch", "write", "copy_fetch", "copy_write", "mfma"):
+        f = os.path.join(root, pas, "run_counter_collection.csv")
+        if not os.path.exists(f):
+            continue
         for row in csv.DictReader(open(f)):
-            per.setdefault((f, row["Kernel_Name"], row["Counter_Name"]), []).append(
+            per.setdefault((pas, kernel_key(row["Kernel_Name"]), row["Counter_Name"]), []).append(
                 float(row["Counter_Value"]))
     mean = lambda v: sum(v) / len(v)
-    copy_kib = COPY_BYTES / 1024.0
-    out = {"indexer_source_sha256_16": src_digest(), "workload": PMC_WORKLOAD,
-           "copy_bytes": COPY_BYTES,
-           "commands": [
-               "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/fetch -o run "
-               "-- python3 bench.py --steps 3 --warmup 1 --copies 1 --no-cpu-baseline",
-               "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/write -o run "
-               "-- python3 bench.py --steps 3 --warmup 1 --copies 1 --no-cpu-baseline",
-               "rocprofv3 --pmc FETCH_SIZE --kernel-trace --output-format csv -d <dir>/copy_fetch "
-               "-o run -- python3 bench.py --copy-calibration",
-               "rocprofv3 --pmc WRITE_SIZE --kernel-trace --output-format csv -d <dir>/copy_write "
-               "-o run -- python3 bench.py --copy-calibration",
-               "python3 bench.py --summarize-pmc <dir>"]}
-    total = 0.0
-    for ctr, name in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
-        copies = [mean(v) for (_, k, c), v in per.items() if c == ctr and "copyBuffer" in k]
-        idx = [v for (_, k, c), v in per.items() if c == ctr and "indexer_kernel" in k]
-        if not copies or not idx:
-            raise SystemExit(f"no {ctr} rows for the copy or the indexer under {root}")
-        # the calibration copy moves the largest amount of any copy in the runs
-        factor = copy_kib / max(copies)
-        kib = mean(idx[0])
-        out[f"{name}_kib_per_dispatch"] = kib
-        out[f"{name}_copy_kib_per_dispatch"] = max(copies)
-        out[f"{name}_scale"] = factor
-        out[f"{name}_bytes_per_launch"] = kib * 1024.0 * factor
-        total += kib * 1024.0 * factor
-    out["traffic_bytes_per_launch"] = total
-    os.makedirs(os.path.dirname(PMC_FILE), exist_ok=True)
-    with open(PMC_FILE, "w") as f:
+    cmd = ("rocprofv3 --pmc {c} --kernel-trace --output-format csv -d <dir>/{d} -o run -- python3 "
+           "bench.py {a}")
+    run = f"--workload {workload} --steps 3 --warmup 1 --settle-seconds 0 --copies 1 --no-cpu-baseline"
+    out = {"csrc_sha256_16": src_digest(), "workload": workload, "copy_bytes": COPY_BYTES,
+           "commands": [cmd.format(c="FETCH_SIZE", d="fetch", a=run),
+                        cmd.format(c="WRITE_SIZE", d="write", a=run),
+                        cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-calibration"),
+                        cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-calibration"),
+                        cmd.format(c="MfmaUtil SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                                     "SQ_INSTS_VALU_MFMA_MOPS_BF16", d="mfma", a=run),
+                        f"python3 bench.py --workload {workload} --summarize-pmc <dir>"],
+           "kernels": {}}
+    scale = {}
+    for ctr, pas in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+        copies = [mean(v) for (p, k, c), v in per.items() if p == "copy_" + pas and "copyBuffer" in k]
+        if not copies:
+            raise SystemExit(f"no {ctr} rows for the calibration copy under {root}")
+        # the calibration copy moves the largest amount of any copy in the run
+        scale[pas] = (COPY_BYTES / 1024.0) / max(copies)
+        out[f"{pas}_scale"] = scale[pas]
+    for (pas, k, c), v in sorted(per.items()):
+        if "copyBuffer" in k or pas.startswith("copy"):
+            continue
+        e = out["kernels"].setdefault(k, {})
+        e["dispatches"] = max(e.get("dispatches", 0), len(v))
+        if pas in ("fetch", "write"):
+            e[f"{pas}_bytes_per_launch"] = round(mean(v) * 1024.0 * scale[pas])
+        elif c == "MfmaUtil":
+            e["mfma_util_pct"] = round(mean(v), 2)
+        elif c == "SQ_INSTS_VALU_MFMA_MOPS_BF16":
+            e["bf16_mfma_flops_per_launch"] = round(mean(v) * 512)
+    for e in out["kernels"].values():
+        if "fetch_bytes_per_launch" in e and "write_bytes_per_launch" in e:
+            e["traffic_bytes_per_launch"] = e["fetch_bytes_per_launch"] + e["write_bytes_per_launch"]
+    os.makedirs(os.path.dirname(pmc_file(workload)), exist_ok=True)
+    with open(pmc_file(workload), "w") as f:
         json.dump(out, f, indent=1)
     return out
+
+
+def measure_bandwidth(dev, n: int = COPY_BYTES, reps: int = 10) -> dict:
+    """HBM bandwidth of plain device operations on 1 GiB buffers, timed with
+    events on torch's stream: a copy (read + write) and a sum (read)."""
+    a = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    r = torch.empty((), dtype=torch.float32, device=dev)
+    res = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * n),
+                            ("read", lambda: torch.sum(a, dim=0, out=r), n)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[f"{name}_gbps"] = round(moved * reps / (e0.elapsed_time(e1) / 1e3) / 1e9, 1)
+    del a, b
+    return res
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 # ---------------------------------------------------------------- CPU oracle
@@ -340,6 +398,7 @@ def cpu_baseline(wl, min_seconds: float):
         if el >= min_seconds:
             break
     return {"value": done / el, "unit": "query-tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{passes} full pass(es) over the {wl.num_tokens}-token {wl.name} batch "
                       f"({done} query tokens, {el:.1f} s, float64 numpy)"}
 
@@ -349,8 +408,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=200,
-                    help="untimed steps first (the clocks settle over the first few dozen)")
+    ap.add_argument("--warmup", type=int, default=200, help="untimed steps first")
+    ap.add_argument("--settle-seconds", type=float, default=1.0,
+                    help="after the warm-up steps, untimed steps until this much time has "
+                         "passed since the first, so the timed steps start at settled clocks")
     ap.add_argument("--workload", default="long_decode_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -358,10 +419,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
     ap.add_argument("--summarize-pmc", metavar="DIR",
-                    help="write the indexer traffic summary from rocprofv3 counter runs under DIR")
+                    help="write the workload's per-kernel counter summary from rocprofv3 runs under DIR")
     args = ap.parse_args()
     if args.summarize_pmc:
-        print(json.dumps(summarize_pmc(args.summarize_pmc)))
+        print(json.dumps(summarize_pmc(args.summarize_pmc, args.workload)))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -416,9 +477,18 @@ def main():
                         s["kv"], s["kv_scale"], wl.k, wl.sm_scale, s["gate"], out, lse, idx,
                         ws=ws, trace=trace)
 
+    t_settle = time.perf_counter()
     for i in range(W):
         step(i)
     torch.cuda.synchronize()
+    # time-based settle: the clocks and caches reach their steady state over
+    # the first tenths of a second of back-to-back steps, whatever W is
+    settle = 0
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for _ in range(32):
+            step(W + settle)
+            settle += 1
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         step(i, tr[i])
@@ -439,11 +509,16 @@ def main():
     topk_ms = [ev.elapsed_ms(tb[i].indexer_end, tb[i].topk_end) for i in range(KB)]
     attn_ms = [ev.elapsed_ms(tb[i].topk_end, tb[i].attn_end) for i in range(KB)]
     ev.close()
+    bw = measure_bandwidth(dev)
     ms_per_step = 1e3 * wall / K
     value = T * K / wall
     ib = indexer_bytes(wl)
     idx_avg_s = float(np.mean(idx_ms)) / 1e3
     sb = step_bytes(wl)
+    counters = counter_summary(wl.name)
+    kc = (counters or {}).get("kernels", {})
+    mfma_util = {k: e["mfma_util_pct"] for k, e in kc.items()
+                 if "mfma_util_pct" in e and (k.startswith("indexer") or k.startswith("attn"))}
     # the indexer's roof: HBM for decode; the MFMA when many tokens share one
     # sequence's keys (chunked prefill), whichever takes longer at peak
     flops = indexer_flops(wl)
@@ -454,12 +529,22 @@ def main():
                 "traffic": None, "algorithmic_flops_per_launch": flops}
     else:
         achieved = ib / idx_avg_s / 1e9
+        traffic = [e["traffic_bytes_per_launch"] for k, e in kc.items()
+                   if k.startswith("indexer_kernel") and "traffic_bytes_per_launch" in e]
         roof = {"bound": "hbm", "kernel": "indexer_kernel", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic() if wl.name == PMC_WORKLOAD else None,
-                "algorithmic_bytes_per_launch": ib}
+                "traffic": traffic[0] if len(traffic) == 1 else None,
+                "algorithmic_bytes_per_launch": ib,
+                "frac_of_measured_copy": round(achieved / bw["copy_gbps"], 4)}
     roof["avg_launch_us"] = round(idx_avg_s * 1e6, 2)
     roof["timed_launches"] = len(idx_ms)
+    # the whole step against the same peak: every byte the step must move
+    roof["step"] = {"achieved": round(sb / (ms_per_step / 1e3) / 1e9, 1), "unit": "GB/s",
+                    "frac": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                    "algorithmic_bytes": sb, "us": round(ms_per_step * 1e3, 2)}
+    roof["measured_hbm_gbps"] = bw
+    roof["mfma_util_pct"] = mfma_util or None
+    roof["counters"] = os.path.relpath(pmc_file(wl.name), ROOT) if counters else None
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "query-tokens/s", "n_gpus": 1,
         "steps": K, "warmup": W, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
@@ -467,7 +552,8 @@ def main():
         "data": "synthetic",
         "config": dict(si.describe(wl), parallelism="single GPU"),
         "roofline": roof,
-        "extra": {"step_algorithmic_bytes": sb,
+        "extra": {"settle_steps": settle,
+                  "step_algorithmic_bytes": sb,
                   "step_gbps": round(sb / (ms_per_step / 1e3) / 1e9, 1),
                   "step_frac_of_hbm_peak": round(sb / (ms_per_step / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                   "indexer_us": round(float(np.mean(idx_ms)) * 1e3, 2),

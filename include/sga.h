@@ -196,8 +196,9 @@ SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t
  *   kv_scale [cache_rows] fp32 (fp8), [cache_rows,18] uint8 E8M0 (MX), NULL
  *   for bf16. indices [T,k] int32.
  *   out [T,64,512] fp32. lse [T,64] fp32 or NULL.
- * Logits and softmax are fp32. Probabilities enter the value product as
- * bf16, and accumulation is fp32. When a token's rows are split over several
+ * Logits and softmax are fp32. Probabilities enter the value product as a
+ * bf16 hi/lo pair (p = hi + lo, about 16 significant bits), and accumulation
+ * is fp32. When a token's rows are split over several
  * workgroups, each split's normalised output is held in fp16, scaled per head
  * and 256-column half by its largest magnitude: a column then carries, beside
  * the relative rounding, an absolute error below 2^-25 of the largest value

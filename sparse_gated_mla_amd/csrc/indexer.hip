@@ -20,8 +20,9 @@
 //   The dims are visited in a permuted order, the same in A and B: lane group
 //   g of step s covers dims 64g + 8s .. 64g + 8s + 7.
 // - Epilogue, per lane: ReLU, times w, summed over the lane's 32 heads. One
-//   cross-half shuffle then gives each position's score, which is stored at
-//   once (and counted, see below) while the wave's next tiles are in flight.
+//   cross-half shuffle then gives each position's score, which is kept in LDS
+//   (and counted, see below) while the wave's next tiles are in flight. The
+//   workgroup writes its chunk's scores in one contiguous run at the end.
 // - fp8 and MX. Keys are widened to bf16 exactly on the LDS read. A per-row fp32
 //   scale multiplies each head's dot product before the ReLU. An MX block-32
 //   key (fact sheet, Training: MXFP8 with one scale per 32 consecutive
@@ -230,6 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
   __shared__ __attribute__((aligned(16))) float lds_w[kIdxHeads];
   __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
+  __shared__ __attribute__((aligned(16))) float lds_sc[indexer_chunk(kFp8)];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the head weights and the query need no batch metadata: their loads go
@@ -261,7 +263,6 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
         kFp8 ? (const void*)(static_cast<const uint32_t*>(a.k_scale) + base + chunk0) : (const void*)a.k_idx,
         kFp8 ? (uint32_t)len * 4u : 0u);
     const int ngroups = (len + Tile::kGroupRows - 1) / Tile::kGroupRows;
-    float* srow = a.scores + (int64_t)t * a.ld + chunk0;
 
     // this wave's tile of every group; kStages groups in flight. Loads are
     // never skipped (past the chunk they read zeros), so each wait is exact.
@@ -276,18 +277,29 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
         const uint32_t ks = st[j].scale;
         st[j].load(keys, scales, i + j + S, wave, lane);
         if (i + j < ngroups) {
-          // scores go out as they are made: each is stored and counted while
-          // the wave's later tiles are still in flight
+          // each score is kept in LDS and counted while the wave's later
+          // tiles are still in flight
           const float sc = score_tile<kFmt>(lds, ks, lane, qa,
                                             [&](int k) { return tile_weight(lds_w, lane, k); });
           const int p = Tile::position(i + j, wave, lane);
           if (lane < 32 && p < len) {
-            srow[p] = sc;
+            lds_sc[p] = sc;
             if constexpr (kHist) atomicAdd(&lds_hist[score_key(sc) >> (32 - kDigit1Bits)], 1u);
           }
         }
       }
     }
+  }
+  // the chunk's scores go out in one contiguous run (16-byte stores where the
+  // row is aligned): written in small pieces between the key loads, they cost
+  // the stream about 4 us at 16 x 128K
+  __syncthreads();
+  if (len > 0) {
+    float* srow = a.scores + (int64_t)t * a.ld + chunk0;
+    const int vec = ((reinterpret_cast<uintptr_t>(srow) & 15) == 0) ? (len & ~3) : 0;
+    for (int i = 4 * (int)threadIdx.x; i < vec; i += 4 * kThreads)
+      *reinterpret_cast<f32x4*>(srow + i) = *reinterpret_cast<const f32x4*>(lds_sc + i);
+    for (int i = vec + (int)threadIdx.x; i < len; i += kThreads) srow[i] = lds_sc[i];
   }
   if constexpr (kHist) hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
 }
