@@ -352,6 +352,21 @@ SGA_API sga_status sga_output_proj(int32_t num_tokens, const float* o_latent, co
                                    const void* w_o, int32_t d_model, float* y, void* ws,
                                    size_t ws_bytes, hipStream_t stream);
 
+/*
+ * sga_hbm_read_probe: a measurement helper, not a step of the method. Reads
+ * the `bytes` bytes at device address `src` once, as the indexer reads its
+ * keys (1 KiB of contiguous memory per wave instruction, streaming cache
+ * policy, one contiguous chunk per workgroup, 1,024 workgroups), and folds
+ * them into a value that is written to the device buffer `sink` only in a
+ * case no input is expected to meet (sink must hold 262,144 uint32 words;
+ * its contents are unspecified afterwards). Timing it gives the HBM read rate
+ * this GPU reaches. bytes: a nonzero multiple of 4,096, with at most about
+ * 4 GiB per workgroup chunk (SGA_ERR_UNSUPPORTED beyond). Asynchronous on
+ * `stream`; the caller keeps src and sink alive until it completes.
+ */
+SGA_API sga_status sga_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
+                                      hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 SGA_API const char* sga_status_string(sga_status status);
 /* Library version as major*10000 + minor*100 + patch. */

@@ -4,19 +4,20 @@ The whole path runs in libsga.so: hand-written HIP kernels behind the C ABI in
 include/sga.h. This package is its ctypes binding. The entry points are
 sga_index_scores, sga_topk, sga_sparse_mla_attn, sga_forward,
 sga_forward_noalloc, sga_cache_append, sga_output_proj and sga_indexer_loss, with the same names
-and meaning as the C functions.
+and meaning as the C functions; sga_hbm_read_probe is a measurement helper.
 """
 from ._lib import (Batch, SgaError, SgaTrace, load, status_string, version, workspace,
                    sga_index_scores, sga_topk, sga_topk_workspace_size, sga_sparse_mla_attn,
                    sga_attn_workspace_size, sga_forward, sga_forward_workspace_size,
                    sga_forward_noalloc, sga_forward_noalloc_scratch_bytes, sga_cache_append, sga_output_proj, sga_output_proj_workspace_size,
-                   sga_indexer_loss, sga_indexer_loss_workspace_size, LIB_PATH, EXPORTS)
+                   sga_indexer_loss, sga_indexer_loss_workspace_size, sga_hbm_read_probe, LIB_PATH,
+                   EXPORTS)
 
 __all__ = ["Batch", "SgaError", "SgaTrace", "load", "status_string", "version", "workspace",
            "sga_index_scores", "sga_topk", "sga_topk_workspace_size", "sga_sparse_mla_attn",
            "sga_attn_workspace_size", "sga_forward", "sga_forward_workspace_size",
            "sga_forward_noalloc", "sga_forward_noalloc_scratch_bytes", "sga_cache_append", "sga_output_proj", "sga_output_proj_workspace_size",
-           "sga_indexer_loss", "sga_indexer_loss_workspace_size",
+           "sga_indexer_loss", "sga_indexer_loss_workspace_size", "sga_hbm_read_probe",
            "batch_to_device", "LIB_PATH", "EXPORTS"]
 
 

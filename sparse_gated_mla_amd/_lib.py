@@ -27,7 +27,7 @@ EXPORTS = ("sga_index_scores", "sga_topk_workspace_size", "sga_topk", "sga_attn_
            "sga_forward_noalloc_scratch_bytes", "sga_forward_noalloc",
            "sga_cache_append", "sga_output_proj_workspace_size", "sga_output_proj",
            "sga_indexer_loss_workspace_size", "sga_indexer_loss",
-           "sga_status_string", "sga_version")
+           "sga_hbm_read_probe", "sga_status_string", "sga_version")
 
 
 class SgaBatch(ctypes.Structure):
@@ -84,6 +84,7 @@ def load(path: Optional[str] = None) -> ctypes.CDLL:
         "sga_indexer_loss": ([bp, vp, vp, vp, ctypes.c_int, vp, i32, f32, vp, vp, i64, vp, vp, sz, vp],
                              ctypes.c_int),
         "sga_output_proj": ([i32, vp, vp, vp, i32, vp, vp, sz, vp], ctypes.c_int),
+        "sga_hbm_read_probe": ([vp, sz, vp, vp], ctypes.c_int),
         "sga_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "sga_version": ([], ctypes.c_int),
     }
@@ -369,3 +370,12 @@ def sga_indexer_loss(batch: Batch, q_abs, kv, kv_scale, indices, k: int, sm_scal
     _raise("sga_indexer_loss", load().sga_indexer_loss(
         ctypes.byref(b), _ptr(q_abs), _ptr(kv), _ptr(kv_scale), dt, _ptr(indices), k, float(sm_scale),
         _ptr(lse), _ptr(scores), scores.shape[1], _ptr(loss), _ptr(ws), ws.numel(), _stream(q_abs)))
+
+
+def sga_hbm_read_probe(src, sink) -> None:
+    """Reads the device byte buffer src once in the indexer's access pattern
+    (a measurement helper); sink: int32 device buffer of 262,144 words."""
+    _check(src, "src", (torch.uint8,))
+    _check(sink, "sink", (torch.int32,), (262144,))
+    _raise("sga_hbm_read_probe",
+           load().sga_hbm_read_probe(_ptr(src), src.numel(), _ptr(sink), _stream(src)))

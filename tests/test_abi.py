@@ -236,3 +236,12 @@ def test_workspace_sizes_grow_with_the_problem(lib):
     assert 0 < a < b
     assert lib.sga_forward_workspace_size(0, 100, 8) == 0
     assert lib.sga_topk_workspace_size(4, 4096, 2048) > 4 * 4096 * 4
+
+
+def test_hbm_read_probe_rejects_bad_arguments(lib):
+    dummy = ctypes.c_void_p(0x1000)
+    # null pointers, an empty read and a size that is not a multiple of 4 KiB
+    assert lib.sga_hbm_read_probe(None, 4096, dummy, None) == 1
+    assert lib.sga_hbm_read_probe(dummy, 4096, None, None) == 1
+    assert lib.sga_hbm_read_probe(dummy, 0, dummy, None) == 1
+    assert lib.sga_hbm_read_probe(dummy, 4097, dummy, None) == 1
