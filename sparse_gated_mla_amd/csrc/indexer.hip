@@ -5,7 +5,8 @@
 //
 // Mapping onto gfx950:
 // - Streaming. A workgroup streams indexer_chunk() positions of one token's key
-//   cache; its four waves take 32-position tiles in turn. Every load
+//   cache (fewer for small batches, down to 128, so the grid fills the GPU);
+//   its four waves take 32-position tiles in turn. Every load
 //   instruction reads 1 KiB of contiguous keys (16 B per lane), so each wave
 //   instruction covers whole cache lines. Each wave keeps three tiles of loads
 //   in flight.
@@ -252,8 +253,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   if (threadIdx.x < kIdxHeads) lds_w[threadIdx.x] = wt;
   __syncthreads();
 
-  const int chunk0 = blockIdx.x * indexer_chunk(kFp8);
-  const int len = min(n - chunk0, indexer_chunk(kFp8));   // positions of this chunk (<= 0: none)
+  const int chunk0 = blockIdx.x * a.chunk;
+  const int len = min(n - chunk0, a.chunk);   // positions of this chunk (<= 0: none)
   if (len > 0) {
     uint8_t* lds = lds_tiles + wave * kTileBytes;
 
@@ -460,10 +461,20 @@ hipError_t launch_prefill_fmt(const IndexerArgs& a, bool fused_hist, hipStream_t
   return hipGetLastError();
 }
 
+// Small batches take shorter chunks, halved until the grid has two workgroups
+// per CU or a chunk is one 128-row group (4,096 positions x 4 tokens: 128
+// workgroups instead of 8).
+constexpr int kIndexerMinChunk = kWaves * kTile;
+constexpr int64_t kIndexerWgTarget = 512;
+
 template <int kFmt>
-hipError_t launch_indexer_fmt(const IndexerArgs& a, bool fused_hist, hipStream_t s) {
-  const int chunk = indexer_chunk(kFmt != kFmtBf16);
-  const dim3 grid((a.batch.max_len + chunk - 1) / chunk, a.num_tokens);
+hipError_t launch_indexer_fmt(const IndexerArgs& args, bool fused_hist, hipStream_t s) {
+  IndexerArgs a = args;
+  a.chunk = indexer_chunk(kFmt != kFmtBf16);
+  while (a.chunk > kIndexerMinChunk &&
+         (int64_t)((a.batch.max_len + a.chunk - 1) / a.chunk) * a.num_tokens < kIndexerWgTarget)
+    a.chunk >>= 1;
+  const dim3 grid((a.batch.max_len + a.chunk - 1) / a.chunk, a.num_tokens);
   if (fused_hist) indexer_kernel<kFmt, true><<<grid, kThreads, 0, s>>>(a);
   else indexer_kernel<kFmt, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();

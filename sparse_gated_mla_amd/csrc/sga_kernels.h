@@ -51,6 +51,7 @@ struct IndexerArgs {
   uint32_t* hist;          // [T,4096]
   TopkCtrl* ctrl;          // [T]
   int k;
+  int chunk;               // positions per workgroup (set by the launch)
 };
 
 struct TopkArgs {
