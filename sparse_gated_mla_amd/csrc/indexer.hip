@@ -313,7 +313,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
 // once (16 B apiece), through a ring of register stages into one of two LDS
 // slots, in the same swizzled layout as above; after one barrier every wave
 // scores the tile for its own token. The work is then bound by the MFMA
-// pipe, not by memory. Tokens of the eight that lie in different sequences
+// pipe, not by memory. Each head block's ReLU and weighted sum run between
+// MFMAs of the other block: block 0's during block 1's MFMAs of the same
+// tile, block 1's during block 0's MFMAs of the next tile (its accumulators
+// carry over the barrier), so no epilogue runs with the matrix pipe idle. Tokens of the eight that lie in different sequences
 // are taken one sequence at a time. Each token's digit-1 histogram lives in
 // LDS and, since one workgroup owns the token, goes out with plain stores.
 constexpr int kPfTokens = 8;                  // tokens per workgroup, one per wave
@@ -420,6 +423,33 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
 #pragma unroll
     for (int j = 0; j < kPfStages; ++j) issue(j, j);
     static_assert(kPfStages % 2 == 0, "tile i uses LDS slot i & 1 == j & 1");
+    // the second head block of tile i finishes during the first block's
+    // MFMAs of tile i+1: its accumulators, the first block's sum, the row
+    // scale and the tile's first position carry over (-1: nothing pending)
+    f32x16 acc1p = {};
+    float sc0p = 0.0f, ksp = 0.0f;
+    int pp = -1;
+    auto epi = [&](const f32x16& acc, int mb, float kscale) {
+      float sc = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 w = wv[2 * q + mb];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float d = acc[4 * q + j];
+          if constexpr (kFmt == kFmtFp8) d *= kscale;
+          sc = fmaf(w[j], relu(d), sc);
+        }
+      }
+      return sc;
+    };
+    auto emit = [&](float sc, int p0) {
+      const int p = p0 + lane;
+      if (lane < 32 && p < n) {
+        srow[p] = sc;
+        if constexpr (kHist) atomicAdd(&lds_hist[wave][score_key(sc) >> (32 - kDigit1Bits)], 1u);
+      }
+    };
     for (int i0 = 0; i0 < ntiles; i0 += kPfStages) {
 #pragma unroll
       for (int j = 0; j < kPfStages; ++j) {
@@ -433,16 +463,36 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
         __syncthreads();
         if (mine && i < ntiles) {
           const uint32_t ks = kFp8 ? lds_scale[slot][lane & 31] : 0u;
-          const float sc = score_tile<kFmt>(lds_tiles[slot], ks, lane, qa, [&](int k) { return wv[k]; });
-          // tile row r is position 32i + r in this layout
-          const int p = i * kTile + lane;
-          if (lane < 32 && p < n) {
-            srow[p] = sc;
-            if constexpr (kHist) atomicAdd(&lds_hist[wave][score_key(sc) >> (32 - kDigit1Bits)], 1u);
+          u32x4 b[8];
+          Tile::operands(lds_tiles[slot], lane, ks, b);
+          f32x16 acc0 = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc0 = mfma32x32x16(qa[0][s], b[s], acc0);
+          const float sc1p = epi(acc1p, 1, ksp);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
           }
+          const float scp = sum_xor32(sc0p + sc1p);
+          if (pp >= 0) emit(scp, pp);
+          f32x16 acc1 = {};
+#pragma unroll
+          for (int s = 0; s < 8; ++s) acc1 = mfma32x32x16(qa[1][s], b[s], acc1);
+          const float sc0 = epi(acc0, 0, __uint_as_float(ks));
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+          acc1p = acc1;
+          sc0p = sc0;
+          ksp = __uint_as_float(ks);
+          pp = i * kTile;   // tile row r is position 32i + r in this layout
         }
       }
     }
+    if (mine && pp >= 0) emit(sum_xor32(sc0p + epi(acc1p, 1, ksp)), pp);
   }
   if constexpr (kHist) {
     __syncthreads();
