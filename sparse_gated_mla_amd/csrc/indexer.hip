@@ -8,7 +8,7 @@
 //   cache (fewer for small batches, down to 128, so the grid fills the GPU);
 //   its four waves take 32-position tiles in turn. Every load
 //   instruction reads 1 KiB of contiguous keys (16 B per lane), so each wave
-//   instruction covers whole cache lines. Each wave keeps three tiles of loads
+//   instruction covers whole cache lines. Each wave keeps two tiles of loads
 //   in flight.
 // - Re-layout. A wave writes its tile into a private 8 KiB LDS region. The
 //   16-byte slots of each row are XOR-swizzled by row, so the 16 lanes of a
@@ -42,8 +42,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kTile = 32;
-// key tiles in flight per wave (more did not help the fp8 variant)
-constexpr int kStages = 3;
+// key tiles in flight per wave: two (8 KiB for bf16 keys); three were 1.2 us
+// slower on the ragged batch and 1 us on the 256K fp8 one, more slower still
+constexpr int kStages = 2;
 
 constexpr int kNonTemporal = 2;         // cache-policy bit: streaming (read-once) data
 
