@@ -150,6 +150,99 @@ __global__ __launch_bounds__(kProjThreads) void proj_kernel(ProjArgs a) {
       }
 }
 
+// The output projection for at most 16 rows (decode batches). Each wave
+// streams 16 weight rows over the workgroup's K range, two 256-wide chunks of
+// B operands in flight; the block of A over that range is split into its bf16
+// hi/lo pair and staged in LDS once, after the first weight loads have gone
+// out, so the weight stream runs with no barrier. Per column the K order, and
+// the splits' order in proj_reduce_kernel, are those of proj_kernel<1, 1>.
+constexpr int kVecThreads = 512;
+
+__global__ __launch_bounds__(kVecThreads) void proj_vec_kernel(ProjArgs a) {
+  constexpr int kChunk = 256;
+  constexpr int kSteps = kChunk / 32;
+  constexpr int kStride = kProjVecMaxK + 8;          // bf16 per LDS row (16-byte pad)
+  constexpr int kUnits = kProjRows * kProjVecMaxK / 8;   // 8-float units of the largest block
+  __shared__ __attribute__((aligned(16))) uint16_t lds_hi[kProjRows][kStride];
+  __shared__ __attribute__((aligned(16))) uint16_t lds_lo[kProjRows][kStride];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n16 = lane & 15, g = lane >> 4;
+  const int split = blockIdx.y;
+  const int kr = a.K / a.splits;   // this workgroup's K range: a multiple of kChunk, <= kProjVecMaxK
+  const int chunks = kr / kChunk;
+  const int k_begin = split * kr;
+  const int n = blockIdx.x * kProjVecCols + 16 * wave + n16;
+  const uint16_t* B = a.b + (int64_t)n * a.ldb + k_begin;
+
+  u32x4 bq[2][kSteps];
+  auto load_b = [&](u32x4 (&dst)[kSteps], int c) {
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) dst[s] = *reinterpret_cast<const u32x4*>(B + c * kChunk + proj_k(s, g));
+  };
+  load_b(bq[0], 0);
+  if (chunks > 1) load_b(bq[1], 1);
+
+  // A block: unit i holds row i / (kr / 8), floats 8 (i % (kr / 8)) .. +7;
+  // rows past M are zeros
+  const int per_row = kr / 8;
+  const int units = kProjRows * per_row;
+  f32x4 av[kUnits / kVecThreads][2];
+#pragma unroll
+  for (int q = 0; q < kUnits / kVecThreads; ++q) {
+    const int i = q * kVecThreads + (int)threadIdx.x;
+    const int m = i / per_row, c8 = i - m * per_row;
+    const bool live = i < units && m < a.M;
+    const float* p = a.a + (int64_t)(live ? m : 0) * a.lda + k_begin + 8 * c8;
+    av[q][0] = live ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    av[q][1] = live ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int q = 0; q < kUnits / kVecThreads; ++q) {
+    const int i = q * kVecThreads + (int)threadIdx.x;
+    if (i < units) {
+      const int m = i / per_row, c8 = i - m * per_row;
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        hi[j] = split_bf16x2(av[q][j >> 1][2 * (j & 1)], av[q][j >> 1][2 * (j & 1) + 1], lo[j]);
+      *reinterpret_cast<u32x4*>(&lds_hi[m][8 * c8]) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+      *reinterpret_cast<u32x4*>(&lds_lo[m][8 * c8]) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < chunks; c += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int cc = c + h;
+      if (cc < chunks) {
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s) {
+          const int k = cc * kChunk + proj_k(s, g);
+          const u32x4 ahi = *reinterpret_cast<const u32x4*>(&lds_hi[n16][k]);
+          const u32x4 alo = *reinterpret_cast<const u32x4*>(&lds_lo[n16][k]);
+          acc = mfma16x16x32(ahi, bq[h][s], acc);
+          acc = mfma16x16x32(alo, bq[h][s], acc);
+        }
+        if (cc + 2 < chunks) load_b(bq[h], cc + 2);
+      }
+    }
+  }
+
+  // acc[r] = C[4g + r][n]
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int m = 4 * g + r;
+    if (m < a.M) {
+      if (a.splits == 1)
+        a.c[(int64_t)m * a.ldc + n] = acc[r];
+      else
+        a.part[((int64_t)split * a.M + m) * a.N + n] = acc[r];
+    }
+  }
+}
+
 // C[b][m][n] = sum over splits s, in order, of part[s][b][m][n].
 __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
   const int64_t per = (int64_t)a.batch * a.M * a.N;
@@ -164,10 +257,7 @@ __global__ __launch_bounds__(256) void proj_reduce_kernel(ProjArgs a) {
   }
 }
 
-}  // namespace
-
-hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
-  if (a.M == 0) return hipSuccess;
+void launch_proj_blocks(const ProjArgs& a, hipStream_t s) {
   const int mb = proj_row_blocks(a.M), nb = proj_col_blocks(a.M, a.N);
   const dim3 grid(a.N / (kProjCols * nb), (a.M + kProjRows * mb - 1) / (kProjRows * mb), a.batch * a.splits);
   if (mb == 4) {
@@ -176,6 +266,18 @@ hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
   } else {
     if (nb == 2) proj_kernel<1, 2><<<grid, kProjThreads, 0, s>>>(a);
     else proj_kernel<1, 1><<<grid, kProjThreads, 0, s>>>(a);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_proj(const ProjArgs& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  const int kr = a.K / a.splits;
+  if (proj_vec(a.M, a.N, a.batch) && kr * a.splits == a.K && kr % 256 == 0 && kr <= kProjVecMaxK) {
+    proj_vec_kernel<<<dim3(a.N / kProjVecCols, a.splits), kVecThreads, 0, s>>>(a);
+  } else {
+    launch_proj_blocks(a, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;

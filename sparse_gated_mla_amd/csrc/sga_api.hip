@@ -270,6 +270,18 @@ ProjPlan plan_proj(int32_t T, int32_t d_model) {
   p.uv_splits = 1;
   const int nb = sga::proj_col_blocks(T, d_model);
   p.o_splits = proj_splits(mt * (d_model / (sga::kProjCols * nb)), sga::kHeads * sga::kDV / chunk);
+  if (sga::proj_vec(T, d_model, 1)) {
+    // one workgroup per CU (its A block fills the LDS): the most splits of K
+    // that keep the grid within 256 workgroups, each K range at most
+    // kProjVecMaxK
+    const int tiles = d_model / sga::kProjVecCols, kchunks = sga::kHeads * sga::kDV / 256;
+    int best = 0;
+    for (int s = 1; s <= kchunks; ++s) {
+      if (kchunks % s || sga::kHeads * sga::kDV / s > sga::kProjVecMaxK) continue;
+      if (best == 0 || tiles * s <= 256) best = s;
+    }
+    p.o_splits = best;
+  }
   p.u_floats = (size_t)T * sga::kHeads * sga::kDV;
   const size_t uv_part = p.uv_splits > 1 ? (size_t)p.uv_splits * T * sga::kHeads * sga::kDV : 0;
   const size_t o_part = p.o_splits > 1 ? (size_t)p.o_splits * T * d_model : 0;

@@ -139,6 +139,14 @@ __host__ __device__ constexpr int proj_chunk(int mb) { return mb == 4 ? 128 : 25
 __host__ __device__ constexpr int proj_col_blocks(int M, int N) {
   return (M >= 32 && N % (2 * kProjCols) == 0) ? 2 : 1;
 }
+// A few rows (at most one MFMA row block): the output projection's kernel for
+// decode batches, 8 waves and 128 columns of C per workgroup, whose block of A
+// over its K range (at most kProjVecMaxK) is staged in LDS once.
+constexpr int kProjVecCols = 128;
+constexpr int kProjVecMaxK = 2048;
+__host__ __device__ constexpr bool proj_vec(int M, int N, int batch) {
+  return M <= kProjRows && batch == 1 && N % kProjVecCols == 0;
+}
 struct ProjArgs {
   const float* a;
   int64_t lda, a_batch;
