@@ -197,30 +197,37 @@ def time_cache_append(wl, s, ev, reps: int) -> dict:
 def time_output_proj(wl, out, ev, reps: int) -> dict:
     """Times sga_output_proj of the step's gated output (the output epilogue
     after the gate), with synthetic bf16 weights for a 7,168-wide hidden state,
-    the same way as the cache append."""
+    the same way as the cache append: with one weight set reused ("us"; the
+    256 MB MALL can hold part of it between calls) and with three sets
+    alternating ("us_three_weight_sets"; as in a model whose layers each have
+    their own weights)."""
     dev = out.device
-    w_uv, w_o = si.proj_weights(seed=98)
-    w_uv, w_o = w_uv.to(dev), w_o.to(dev)
+    sets = [tuple(x.to(dev) for x in si.proj_weights(seed=98 + i)) for i in range(3)]
+    w_uv, w_o = sets[0]
     T, d_model = wl.num_tokens, w_o.shape[0]
     y = torch.empty((T, d_model), dtype=torch.float32, device=dev)
     ws = sga.workspace(sga.sga_output_proj_workspace_size(T, d_model), dev)
-    run = lambda: sga.sga_output_proj(out, w_uv, w_o, y, ws=ws)
-    for _ in range(3):
-        run()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev).cuda_stream
-    pairs = [(ev.create(), ev.create()) for _ in range(reps)]
-    torch.cuda._sleep(5_000_000)
-    for a, b in pairs:
-        ev.record(a, stream)
-        run()
-        ev.record(b, stream)
-    torch.cuda.synchronize()
-    us = float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs])) * 1e3
+    res = {}
+    for key, pick in (("us", lambda i: sets[0]), ("us_three_weight_sets", lambda i: sets[i % 3])):
+        run = lambda i: sga.sga_output_proj(out, *pick(i), y, ws=ws)
+        for i in range(3):
+            run(i)
+        torch.cuda.synchronize()
+        pairs = [(ev.create(), ev.create()) for _ in range(reps)]
+        torch.cuda._sleep(5_000_000)
+        for i, (a, b) in enumerate(pairs):
+            ev.record(a, stream)
+            run(i)
+            ev.record(b, stream)
+        torch.cuda.synchronize()
+        res[key] = round(float(np.mean([ev.elapsed_ms(a, b) for a, b in pairs])) * 1e3, 2)
     nbytes = (w_uv.numel() + w_o.numel()) * 2 + out.numel() * 4 + y.numel() * 4
     flops = 2 * T * (64 * 128 * 512 + d_model * 64 * 128)
-    return {"us": round(us, 2), "d_model": int(d_model), "algorithmic_bytes": int(nbytes),
-            "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+    us = res["us"]
+    return {"us": us, "us_three_weight_sets": res["us_three_weight_sets"], "d_model": int(d_model),
+            "algorithmic_bytes": int(nbytes), "gbps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "gbps_three_weight_sets": round(nbytes / (res["us_three_weight_sets"] * 1e-6) / 1e9, 1),
             "tflops": round(flops / (us * 1e-6) / 1e12, 2)}
 
 
