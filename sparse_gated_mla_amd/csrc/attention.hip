@@ -440,10 +440,15 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
 #pragma unroll
     for (int s = 0; s < 9; ++s) qb[s] = *reinterpret_cast<const u32x4*>(q + 32 * s);
   }
+  // the batch metadata (needed only for the row gathers): its two scalar
+  // rounds run while the selecting variant's final stage works
+  int64_t base;
+  int n;
+  a.batch.token(t, base, n);
   if constexpr (kSelect) {
     // this split's ranks [j_begin, j_begin + nrows) of the token's selection;
     // the visible count comes with the cut, so the stage does not wait for the
-    // batch metadata (needed only for the row gathers)
+    // batch metadata
     const int nv = fin.visible();
     if (nv <= a.k) {   // every visible position is kept: rank r is position r
       for (int j = threadIdx.x; j < nrows; j += kAttnThreads) lds_idx[j] = j_begin + j < nv ? j_begin + j : -1;
@@ -458,9 +463,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
     s0.load_idx_lds(lds_idx, 0);
     s1.load_idx_lds(lds_idx, 1);
   }
-  int64_t base;
-  int n;
-  a.batch.token(t, base, n);
   const uint32_t rows_bytes = (uint32_t)max(n, 0) * Stage::kRowBytes;
   const rsrc_t rows = make_rsrc(a.kv + base * Stage::kRowBytes, rows_bytes);
   const rsrc_t scales =
