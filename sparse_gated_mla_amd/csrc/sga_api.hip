@@ -207,6 +207,13 @@ sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int
     SGA_HIP(sga::launch_topk_token(a, stream));
   } else {
     a.lds_cand_cap = 0;
+    // the final stage's ordered pass spread over several workgroups per
+    // token, about one per CU in all, each handing out a window of at least
+    // 64 ranks
+    int windows = 256 / (batch->num_tokens > 0 ? batch->num_tokens : 1);
+    if (windows < 1) windows = 1;
+    if (windows > (k + 63) / 64) windows = (k + 63) / 64;
+    a.fin_window = (k + windows - 1) / windows;
     SGA_HIP(sga::launch_topk_select(a, stream));
     SGA_HIP(sga::launch_topk_finalize(a, stream));
   }

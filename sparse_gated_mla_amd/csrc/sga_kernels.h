@@ -73,6 +73,7 @@ struct TopkArgs {
   uint32_t* wg_count;      // [T,max_select_wgs] candidates each select workgroup wrote
   int max_select_wgs;
   int lds_cand_cap;        // candidates the one-kernel top-k can stage in LDS
+  int fin_window;          // ranks per workgroup of the standalone final stage
 };
 
 struct AttnArgs {

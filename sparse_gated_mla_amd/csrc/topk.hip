@@ -134,30 +134,36 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
 }
 
-// One workgroup per token runs the final stage (sga_finalize.h) and writes the
-// k kept positions, staged in LDS for coalesced stores when k <= 4096.
+// The final stage (sga_finalize.h) for one window of ranks of one token:
+// workgroup (g, t) writes ranks [g * W, min(k, (g + 1) * W)) of token t's
+// selection (W = a.fin_window), staged in LDS for coalesced stores when the
+// window holds at most 4,096 ranks. Several workgroups per token each run the
+// stage's cut and counting and hand out only their own ranks, so the ordered
+// pass over a long context is spread over them.
 // Dynamic LDS: staged output (4096 words) | the stage's finalize_lds_words.
 __global__ __launch_bounds__(kFinThreads) void topk_finalize_kernel(TopkArgs a) {
   extern __shared__ uint32_t lds[];
   uint32_t* out_stage = lds;
-  const int t = blockIdx.x;
+  const int t = blockIdx.y;
+  const uint32_t lo = (uint32_t)blockIdx.x * (uint32_t)a.fin_window;
+  const uint32_t hi = min((uint32_t)a.k, lo + (uint32_t)a.fin_window);
   TokenFinalize<kFinThreads> fin;
   fin.prefetch(a, t);
   const int n = fin.visible();   // recorded by the select kernel
   int32_t* out = a.indices + (int64_t)t * a.k;
   if (n <= a.k) {
-    for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = i < n ? i : -1;
+    for (int i = (int)lo + threadIdx.x; i < (int)hi; i += kFinThreads) out[i] = i < n ? i : -1;
     return;
   }
-  int32_t* staged_out = reinterpret_cast<int32_t*>(out_stage);   // k <= kHist2: the output goes out coalesced
-  const bool stage_out = a.k <= kHist2;
-  fin.run(a, n, out_stage + kHist2, 0u, (uint32_t)a.k, [&](uint32_t o, uint32_t p) {
-    if (stage_out) staged_out[o] = (int32_t)p;
+  int32_t* staged_out = reinterpret_cast<int32_t*>(out_stage);   // the window goes out coalesced
+  const bool stage_out = hi - lo <= (uint32_t)kHist2;
+  fin.run(a, n, out_stage + kHist2, lo, hi, [&](uint32_t o, uint32_t p) {
+    if (stage_out) staged_out[o - lo] = (int32_t)p;
     else out[o] = (int32_t)p;
   });
   if (stage_out) {
     __syncthreads();
-    for (int i = threadIdx.x; i < a.k; i += kFinThreads) out[i] = staged_out[i];
+    for (int i = (int)lo + threadIdx.x; i < (int)hi; i += kFinThreads) out[i] = staged_out[i - lo];
   }
 }
 
@@ -416,7 +422,9 @@ hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
   const size_t lds = (size_t)(kHist2 + finalize_lds_words(a.words)) * sizeof(uint32_t);
   if (lds > kFinalizeLds) return hipErrorInvalidValue;
-  topk_finalize_kernel<<<a.num_tokens, kFinThreads, lds, s>>>(a);
+  if (a.fin_window < 1) return hipErrorInvalidValue;
+  const unsigned windows = (unsigned)((a.k + a.fin_window - 1) / a.fin_window);
+  topk_finalize_kernel<<<dim3(windows, a.num_tokens), kFinThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
