@@ -494,6 +494,8 @@ def main():
     ap.add_argument("--workload", default="long_decode_128k", choices=sorted(WORKLOADS))
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-two-streams", action="store_true",
+                    help="skip the phase with two batches in flight (profiles of single kernels)")
     ap.add_argument("--copies", type=int, default=2, help="input sets alternated between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
@@ -578,7 +580,7 @@ def main():
         step(K + i, tb[i])
     torch.cuda.synchronize()
 
-    two = time_two_streams(wl, sets, dev, steps=max(K, 50))
+    two = None if args.no_two_streams else time_two_streams(wl, sets, dev, steps=max(K, 50))
     # around the step, after it: the indexer loss over the last step's selection
     # (input set (K - 1) % copies), the output epilogue of its output, then the
     # cache append (which writes into the caches, so it comes last)
