@@ -232,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   constexpr int kTileBytes = Tile::kRowBytes * kTile;
   __shared__ __attribute__((aligned(16))) uint8_t lds_tiles[kWaves * kTileBytes];
   __shared__ __attribute__((aligned(16))) float lds_w[kIdxHeads];
-  __shared__ uint32_t lds_hist[kHist ? kHist1 : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_hist[kHist ? kHist1 : 1];
+  __shared__ uint32_t lds_scan[kWaves];
   __shared__ __attribute__((aligned(16))) float lds_sc[indexer_chunk(kFp8)];
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -303,7 +304,18 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
       *reinterpret_cast<f32x4*>(srow + i) = *reinterpret_cast<const f32x4*>(lds_sc + i);
     for (int i = vec + (int)threadIdx.x; i < len; i += kThreads) srow[i] = lds_sc[i];
   }
-  if constexpr (kHist) hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
+  if constexpr (kHist) {
+    if (a.hist_slot_words) {
+      // the chunk's bins as a list in its own slot; the first chunk's
+      // workgroup zeroes the token's second-level histogram for the select
+      // kernel (the kernel boundary orders both before it)
+      if (blockIdx.x == 0) hist2_zero<kThreads>(a.hist2 + (int64_t)t * kHist2, threadIdx.x);
+      hist1_list_store<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1 + (int64_t)blockIdx.x * a.hist_slot_words,
+                                 a.hist_slot_words, blockIdx.x, lds_scan);
+    } else {
+      hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -500,6 +512,9 @@ __global__ __launch_bounds__(kPfThreads, 1) void indexer_prefill_kernel(IndexerA
     if (live) {
       uint32_t* gh = a.hist + (int64_t)t * kHist1;
       for (int b = lane; b < kHist1; b += 64) gh[b] = lds_hist[wave][b];
+      // the second level, zeroed for the select kernel (the one-workgroup
+      // top-k keeps its own in LDS)
+      if (a.hist2) hist2_zero<64>(a.hist2 + (int64_t)t * kHist2, lane);
     }
   }
 }
@@ -518,13 +533,21 @@ hipError_t launch_prefill_fmt(const IndexerArgs& a, bool fused_hist, hipStream_t
 constexpr int kIndexerMinChunk = kWaves * kTile;
 constexpr int64_t kIndexerWgTarget = 512;
 
+int decode_chunk(int fmt, int max_len, int num_tokens) {
+  int chunk = indexer_chunk(fmt != kFmtBf16);
+  while (chunk > kIndexerMinChunk && (int64_t)((max_len + chunk - 1) / chunk) * num_tokens < kIndexerWgTarget)
+    chunk >>= 1;
+  return chunk;
+}
+
 template <int kFmt>
 hipError_t launch_indexer_fmt(const IndexerArgs& args, bool fused_hist, hipStream_t s) {
   IndexerArgs a = args;
-  a.chunk = indexer_chunk(kFmt != kFmtBf16);
-  while (a.chunk > kIndexerMinChunk &&
-         (int64_t)((a.batch.max_len + a.chunk - 1) / a.chunk) * a.num_tokens < kIndexerWgTarget)
-    a.chunk >>= 1;
+  a.chunk = decode_chunk(kFmt, a.batch.max_len, a.num_tokens);
+  // list slots need one slot per chunk of the grid
+  if (fused_hist && a.hist_slot_words &&
+      (int64_t)a.hist_slot_words * ((a.batch.max_len + a.chunk - 1) / a.chunk) > kHist1)
+    return hipErrorInvalidValue;
   const dim3 grid((a.batch.max_len + a.chunk - 1) / a.chunk, a.num_tokens);
   if (fused_hist) indexer_kernel<kFmt, true><<<grid, kThreads, 0, s>>>(a);
   else indexer_kernel<kFmt, false><<<grid, kThreads, 0, s>>>(a);
@@ -539,6 +562,10 @@ hipError_t launch_indexer_prefill(const IndexerArgs& a, int fmt, bool fused_hist
   if (fmt == kFmtMx) return launch_prefill_fmt<kFmtMx>(a, fused_hist, s);
   if (fmt == kFmtMx4) return launch_prefill_fmt<kFmtMx4>(a, fused_hist, s);
   return launch_prefill_fmt<kFmtBf16>(a, fused_hist, s);
+}
+
+int indexer_decode_chunk(int fmt, int max_len, int num_tokens) {
+  return decode_chunk(fmt, max_len, num_tokens);
 }
 
 hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s) {

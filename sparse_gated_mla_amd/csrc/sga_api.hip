@@ -167,8 +167,15 @@ sga_status record(hipEvent_t e, hipStream_t s) {
   return hip_status(hipEventRecord(e, s));
 }
 
+// First-level histogram form, fixed by whichever kernel fills it: list slots
+// of hist_slot_words words, one per chunk of hist_chunk positions, or the
+// dense histogram (hist_slot_words 0), which needs a cleared region.
+struct HistForm {
+  int slot_words, chunk;
+};
+
 TopkArgs topk_args(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
-                   int32_t* indices, const TopkLayout& L) {
+                   int32_t* indices, const TopkLayout& L, HistForm hf) {
   TopkArgs a;
   memset(&a, 0, sizeof(a));
   a.batch = view_of(batch);
@@ -178,6 +185,8 @@ TopkArgs topk_args(const sga_batch* batch, const float* scores, int64_t ld, int3
   a.k = k;
   a.indices = indices;
   a.hist = L.hist;
+  a.hist_slot_words = hf.slot_words;
+  a.hist_chunk = hf.chunk;
   a.hist2 = L.hist + (size_t)batch->num_tokens * sga::kHist1;
   a.ctrl = L.ctrl;
   a.sel = L.sel;
@@ -195,14 +204,23 @@ bool use_token_topk(int32_t T, const TopkLayout& L) {
   return T >= kTokenTopkMinTokens && sga::topk_token_lds_cap(L.words) > 0;
 }
 
+// run_topk with hist_ready: the indexer has filled the first level in form
+// hf and zeroed the second. Otherwise the histogram kernel fills it: as list
+// slots when the context allows (and then zeroes the second level itself),
+// else densely after a clear of both levels.
 sga_status run_topk(const sga_batch* batch, const float* scores, int64_t ld, int32_t k,
-                    int32_t* indices, const TopkLayout& L, bool hist_ready, hipStream_t stream) {
-  TopkArgs a = topk_args(batch, scores, ld, k, indices, L);
+                    int32_t* indices, const TopkLayout& L, bool hist_ready, HistForm hf,
+                    hipStream_t stream) {
+  // (the one-workgroup top-k reads only the dense form)
+  const bool token_topk = use_token_topk(batch->num_tokens, L);
+  if (!hist_ready)
+    hf = HistForm{token_topk ? 0 : sga::topk_hist_slot_words(batch->max_len), sga::kIndexerChunk};
+  TopkArgs a = topk_args(batch, scores, ld, k, indices, L, hf);
   if (!hist_ready) {
-    SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
+    if (!hf.slot_words) SGA_HIP(sga::launch_clear(L.hist, (int64_t)L.clear_words, stream));
     SGA_HIP(sga::launch_topk_hist(a, stream));
   }
-  if (use_token_topk(batch->num_tokens, L)) {
+  if (token_topk) {
     a.lds_cand_cap = sga::topk_token_lds_cap(L.words);
     SGA_HIP(sga::launch_topk_token(a, stream));
   } else {
@@ -422,7 +440,7 @@ SGA_API sga_status sga_topk(const sga_batch* batch, const float* scores, int64_t
   if (!ws || ws_bytes < need) return SGA_ERR_WORKSPACE;
   Carver c(ws);
   TopkLayout L = carve_topk(c, batch->num_tokens, batch->max_len);
-  return run_topk(batch, scores, ld, k, indices, L, false, stream);
+  return run_topk(batch, scores, ld, k, indices, L, false, HistForm{0, 0}, stream);
 }
 
 SGA_API size_t sga_attn_workspace_size(int32_t num_tokens, int32_t k) {
@@ -491,12 +509,20 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
 
   const bool prefill_indexer = many_tokens_per_seq(batch);
   const bool token_topk = use_token_topk(T, TL);
-  // The prefill indexer stores each token's whole first-level histogram, and
-  // the one-workgroup top-k reads no other level: then nothing needs zeroing
-  // (8,192 tokens: 268 MB, 38 us).
-  if (!(prefill_indexer && token_topk))
+  // The first level needs no cleared memory when each workgroup writes its own
+  // part with plain stores: the prefill indexer stores each token's whole
+  // histogram, and the decode indexer writes per-chunk lists (read by the
+  // select kernel, not by the one-workgroup top-k). Both zero the second
+  // level. Only the dense histogram of atomics needs the clear kernel.
+  HistForm hf{0, 0};
+  if (!prefill_indexer && !token_topk) {
+    hf.chunk = sga::indexer_decode_chunk((int)k_idx_dtype, batch->max_len, T);
+    hf.slot_words = sga::hist_slot_words(((int64_t)batch->max_len + hf.chunk - 1) / hf.chunk);
+  }
+  if (!prefill_indexer && !hf.slot_words)
     SGA_HIP(sga::launch_clear(TL.hist, (int64_t)TL.clear_words, stream));
   IndexerArgs ia;
+  memset(&ia, 0, sizeof(ia));
   ia.batch = view_of(batch);
   ia.num_tokens = T;
   ia.q_idx = static_cast<const uint16_t*>(q_idx);
@@ -506,6 +532,8 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
   ia.scores = scores;
   ia.ld = batch->max_len;
   ia.hist = TL.hist;
+  ia.hist2 = TL.hist + (size_t)T * sga::kHist1;
+  ia.hist_slot_words = hf.slot_words;
   ia.ctrl = TL.ctrl;
   ia.k = k;
   if (trace) SGA_TRY(record(trace->indexer_begin, stream));
@@ -518,7 +546,7 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
       TL.words <= sga::kSelectMaxWords) {
     // the top-k's final stage runs inside the attention kernel: each split
     // takes its own rows of the selection (and writes them to indices_out)
-    const TopkArgs ta = topk_args(batch, scores, batch->max_len, k, nullptr, TL);
+    const TopkArgs ta = topk_args(batch, scores, batch->max_len, k, nullptr, TL, hf);
     SGA_HIP(sga::launch_topk_select(ta, stream));
     if (trace) SGA_TRY(record(trace->topk_end, stream));
     AttnArgs aa = attn_args(batch, q_abs, kv, kv_scale, nullptr, k, sm_scale, gate_logits, out, lse,
@@ -527,7 +555,7 @@ SGA_API sga_status sga_forward(const sga_batch* batch, const void* q_idx, const 
     SGA_HIP(sga::launch_attention_select(aa, ta, (int)kv_dtype, stream));
     SGA_HIP(sga::launch_combine(aa, stream));
   } else {
-    SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, stream));
+    SGA_TRY(run_topk(batch, scores, batch->max_len, k, indices, TL, true, hf, stream));
     if (trace) SGA_TRY(record(trace->topk_end, stream));
     SGA_TRY(run_attention(batch, q_abs, kv, kv_scale, kv_dtype, indices, k, sm_scale, gate_logits,
                           out, lse, plan, AL, stream));

@@ -174,6 +174,77 @@ __device__ __forceinline__ void hist1_flush(const uint32_t* lds_hist, uint32_t* 
   }
 }
 
+// Writes a workgroup's LDS digit-1 histogram (kHist1 bins) as a list into its
+// slot of slot_words words, with plain stores: word 0 the number m of nonzero
+// bins, then one entry (bin << 16 | count) per nonzero bin, or word 0 =
+// kHistOverflow when m > slot_words - 1. Counts are below 2^16 (a chunk holds
+// at most 4,096 positions). The entries are in ascending bin order rotated
+// left by `rot` places (the reader sums them in any order; chunks of one
+// token list mostly the same bins, and rotating each by its chunk index
+// spreads the reader's same-offset LDS atomics over different bins). Thread j
+// takes bins [P*j, P*j + P); a wave scan and one LDS exchange place its
+// entries. scratch: NT/64 words of LDS. All threads must call; no barrier follows.
+template <int NT>
+__device__ __forceinline__ void hist1_list_store(const uint32_t* lds_hist, uint32_t* slot,
+                                                 int slot_words, uint32_t rot, uint32_t* scratch) {
+  constexpr int P = kHist1 / NT;
+  constexpr int kWaves = NT / 64;
+  static_assert(P % 4 == 0 && P * NT == kHist1, "whole 16-byte runs per thread");
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int b0 = (int)threadIdx.x * P;
+  uint32_t h[P];
+#pragma unroll
+  for (int q = 0; q < P / 4; ++q) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(lds_hist + b0 + 4 * q);
+    h[4 * q] = x.x;
+    h[4 * q + 1] = x.y;
+    h[4 * q + 2] = x.z;
+    h[4 * q + 3] = x.w;
+  }
+  uint32_t cnt = 0;
+#pragma unroll
+  for (int i = 0; i < P; ++i) cnt += h[i] != 0u;
+  const uint32_t x = wave_incl_scan(cnt);
+  if (lane == 63) scratch[wid] = x;
+  __syncthreads();
+  uint32_t before = x - cnt, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const uint32_t sw = scratch[w];
+    if (w < wid) before += sw;
+    total += sw;
+  }
+  if (total >= (uint32_t)slot_words) {
+    if (threadIdx.x == 0) slot[0] = kHistOverflow;
+    return;
+  }
+  if (total == 0) {
+    if (threadIdx.x == 0) slot[0] = 0u;
+    return;
+  }
+  // rank r goes to word 1 + (r + rot) mod total
+  uint32_t o = before + rot % total;
+  if (o >= total) o -= total;
+#pragma unroll
+  for (int i = 0; i < P; ++i)
+    if (h[i]) {
+      slot[1 + o] = ((uint32_t)(b0 + i) << 16) | h[i];
+      o = o + 1 == total ? 0u : o + 1;
+    }
+  if (threadIdx.x == 0) slot[0] = total;
+}
+
+// Zeroes one token's kHist2-word second-level histogram with 16-byte stores
+// (a workgroup of NT threads, or one wave with NT = 64).
+template <int NT>
+__device__ __forceinline__ void hist2_zero(uint32_t* h2, int tid) {
+  static_assert(kHist2 % (4 * NT) == 0, "whole 16-byte stores per thread");
+#pragma unroll
+  for (int q = 0; q < kHist2 / (4 * NT); ++q)
+    reinterpret_cast<u32x4*>(h2)[q * NT + tid] = u32x4{0u, 0u, 0u, 0u};
+}
+
 // A radix cut straight from a histogram in global memory, with no LDS copy.
 // Thread j holds bins [nbins - P(j+1), nbins - Pj) in registers (P = nbins/NT,
 // a multiple of 4), so thread 0 holds the top bins. load() issues the loads;
@@ -190,6 +261,39 @@ struct HistRun {
     const u32x4* src = reinterpret_cast<const u32x4*>(ghist + NBINS - P * ((int)threadIdx.x + 1));
 #pragma unroll
     for (int q = 0; q < P / 4; ++q) v[q] = src[q];
+  }
+
+  // The same runs, read from a histogram in LDS.
+  __device__ __forceinline__ void load_lds(const uint32_t* lhist) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(lhist + NBINS - P * ((int)threadIdx.x + 1));
+#pragma unroll
+    for (int q = 0; q < P / 4; ++q) v[q] = src[q];
+  }
+
+  // After load() of a region of list slots (see hist1_list_store): adds every
+  // listed entry into the LDS histogram lhist (zeroed, and the zeroing
+  // published by a barrier) and marks overflowed slots in ovf (zeroed bit
+  // mask, one bit per slot). Thread j holds region words [NBINS - P(j+1),
+  // NBINS - Pj); a slot of sw words (16 <= P <= sw, sw <= 64 P) spans
+  // sw / P consecutive lanes of one wave, its header word 0 held by the
+  // highest of them. Slots at or past `slots` are not read.
+  __device__ __forceinline__ void add_lists(int sw, int slots, uint32_t* lhist, uint32_t* ovf) const {
+    const int lane = threadIdx.x & 63;
+    const int w0 = NBINS - P * ((int)threadIdx.x + 1);   // first region word of this thread
+    const int s = w0 / sw, o0 = w0 - s * sw;               // its slot and offset there
+    const int tps = sw / P;                                 // threads per slot
+    const uint32_t m = (uint32_t)__shfl((int)v[0].x, lane | (tps - 1));
+    if (s >= slots) return;
+    if (m == kHistOverflow) {
+      if (o0 == 0) atomicOr(&ovf[s >> 5], 1u << (s & 31));
+      return;
+    }
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const uint32_t o = (uint32_t)(o0 + i);
+      const uint32_t e = v[i / 4][i % 4];
+      if (o >= 1u && o <= m) atomicAdd(&lhist[e >> 16], e & 0xffffu);
+    }
   }
 
   __device__ __forceinline__ void cut(uint32_t r, uint32_t* scratch, uint32_t& d, uint32_t& above,

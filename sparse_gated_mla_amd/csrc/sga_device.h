@@ -143,6 +143,7 @@ constexpr int kDigit3Bits = 8;   // key bits 7..0
 constexpr int kHist1 = 1 << kDigit1Bits;
 constexpr int kHist2 = 1 << kDigit2Bits;
 constexpr int kHist3 = 1 << kDigit3Bits;
+constexpr uint32_t kHistOverflow = 0xffffffffu;   // list slot header: the bins did not fit
 
 // ---------------------------------------------------------------- visibility
 // Visible rows of a token, clamped so inconsistent metadata never leaves the

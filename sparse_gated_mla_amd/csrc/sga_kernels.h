@@ -37,6 +37,27 @@ constexpr int kMaxSelectWgs = 128;    // select workgroups of the longest contex
 constexpr int kAttnTileRows = 32;     // latent rows per attention tile
 constexpr int kMaxLenRows = 1 << 19;  // longest visible context (SGA_MAX_LEN)
 
+// First-level histogram lists. A decode indexer workgroup (token t, chunk c)
+// writes the nonzero digit-1 bins of its chunk into slot c of the token's
+// kHist1-word histogram region, with plain stores: word 0 holds the number m
+// of entries, words 1..m one entry (bin << 16 | count) each, in ascending bin
+// order; when more than slot_words - 1 bins are nonzero, word 0 holds
+// kHistOverflow and the select kernel counts that chunk from its scores.
+// Every workgroup writes its slot, so nothing needs zeroing beforehand (a
+// dense histogram filled by atomics needs a cleared region and a kernel to
+// clear it). Slots are powers of two from 32 to 256 words and fill at most
+// the kHist1 words of the region; with more chunks per token than 128 the
+// dense histogram is used.
+constexpr int kHistSlotMin = 32;
+constexpr int kHistSlotMax = 256;
+constexpr int kMaxHistSlots = kHist1 / kHistSlotMin;   // 128 chunks per token
+static_assert(kMaxHistSlots == 128, "the select kernel's overflow mask is four words");
+__host__ __device__ constexpr int hist_slot_words(int64_t chunks) {
+  int w = kHistSlotMax;
+  while (w >= kHistSlotMin && (int64_t)w * chunks > kHist1) w >>= 1;
+  return w >= kHistSlotMin ? w : 0;
+}
+
 struct IndexerArgs {
   BatchView batch;
   int num_tokens;
@@ -48,7 +69,9 @@ struct IndexerArgs {
   float* scores;           // [T,ld]
   int64_t ld;
   // top-k first level, filled by the fused variant
-  uint32_t* hist;          // [T,4096]
+  uint32_t* hist;          // [T,4096] dense histogram, or the per-chunk lists
+  uint32_t* hist2;         // [T,4096] second level: zeroed here for the select kernel
+  int hist_slot_words;     // 0: dense histogram (atomics into a cleared region); else list slots
   TopkCtrl* ctrl;          // [T]
   int k;
   int chunk;               // positions per workgroup (set by the launch)
@@ -61,7 +84,9 @@ struct TopkArgs {
   int64_t ld;
   int k;
   int32_t* indices;        // [T,k]
-  uint32_t* hist;          // [T,4096] digit-1 histogram (zeroed per call)
+  uint32_t* hist;          // [T,4096] digit-1 histogram (zeroed per call), or the per-chunk lists
+  int hist_slot_words;     // 0: dense histogram; else words per list slot
+  int hist_chunk;          // list slots: positions per slot's chunk
   uint32_t* hist2;         // [T,4096] digit-2 histogram of the candidates (zeroed per call)
   TopkCtrl* ctrl;          // [T]
   uint32_t* sel;           // [T,words]
@@ -163,12 +188,17 @@ hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s);
 hipError_t launch_proj(const ProjArgs& a, hipStream_t s);
 hipError_t launch_cache_append(const CacheArgs& a, hipStream_t s);
 hipError_t launch_indexer(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s);
+// Positions per workgroup of the decode indexer for this batch shape.
+int indexer_decode_chunk(int fmt, int max_len, int num_tokens);
 // Eight tokens per workgroup sharing each key tile: for batches with many
 // tokens per sequence. With fused_hist it writes each token's digit-1
 // histogram with plain stores (it owns the token).
 hipError_t launch_indexer_prefill(const IndexerArgs& a, int fmt, bool fused_hist, hipStream_t s);
 constexpr int kPrefillTokensPerSeq = 64;   // mean tokens per sequence from which it is used
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s);
+// List slots for the stand-alone histogram kernel (kIndexerChunk positions per
+// workgroup), 0 when the dense histogram is needed.
+int topk_hist_slot_words(int max_len);
 hipError_t launch_topk_select(const TopkArgs& a, hipStream_t s);
 hipError_t launch_topk_finalize(const TopkArgs& a, hipStream_t s);
 constexpr size_t kFinalizeLds = 160 * 1024;  // dynamic LDS of the finalize kernels

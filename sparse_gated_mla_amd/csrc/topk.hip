@@ -43,7 +43,8 @@ __global__ __launch_bounds__(256) void clear_kernel(uint32_t* __restrict__ p, in
 }
 
 __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
-  __shared__ uint32_t lds_hist[kHist1];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_hist[kHist1];
+  __shared__ uint32_t scan_scratch[kHistThreads / 64];
   const int t = blockIdx.y;
   int64_t base;
   int n;
@@ -55,12 +56,20 @@ __global__ __launch_bounds__(kHistThreads) void topk_hist_kernel(TopkArgs a) {
   const float* srow = a.scores + (int64_t)t * a.ld;
   for (int p = c0 + threadIdx.x; p < c1; p += kHistThreads)
     atomicAdd(&lds_hist[score_key(srow[p]) >> (32 - kDigit1Bits)], 1u);
-  hist1_flush<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
+  if (a.hist_slot_words) {
+    if (blockIdx.x == 0) hist2_zero<kHistThreads>(a.hist2 + (int64_t)t * kHist2, threadIdx.x);
+    hist1_list_store<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1 + (int64_t)blockIdx.x * a.hist_slot_words,
+                                   a.hist_slot_words, blockIdx.x, scan_scratch);
+  } else {
+    hist1_flush<kHistThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
+  }
 }
 
 __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t scratch[32];
   __shared__ uint32_t lds_count;
+  __shared__ __attribute__((aligned(16))) uint32_t lds_h1[kHist1];   // list slots summed
+  __shared__ uint32_t lds_ovf[kMaxHistSlots / 32];
   constexpr int kSteps = kSelectChunk / kSelThreads;   // 64-position steps per wave
   const int t = blockIdx.y;
   const int c0 = blockIdx.x * kSelectChunk;   // < max_len: the grid covers max_len
@@ -71,12 +80,20 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   // in flight. Scores past the token's visible rows (below max_len, inside the
   // row) are read and then masked.
   HistRun<kSelThreads, kHist1> h1;
-  h1.load(a.hist + (int64_t)t * kHist1);
+  h1.load(a.hist + (int64_t)t * kHist1);   // the dense histogram, or the region of list slots
   const rsrc_t srs = make_rsrc(srow + c0, (uint32_t)(min(a.batch.max_len, c0 + kSelectChunk) - c0) * 4u);
   float v[kSteps];
 #pragma unroll
   for (int i = 0; i < kSteps; ++i)
     v[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(srs, (i * kSelThreads + wave * 64 + lane) * 4, 0, 0));
+  const int hsw = a.hist_slot_words;
+  if (hsw) {
+    // list slots: their entries are summed into an LDS histogram first
+#pragma unroll
+    for (int q = 0; q < kHist1 / (4 * kSelThreads); ++q)
+      reinterpret_cast<u32x4*>(lds_h1)[q * kSelThreads + threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+    lds_ovf[threadIdx.x % (kMaxHistSlots / 32)] = 0u;   // no branch on the thread index here
+  }
   int64_t base;
   int n;
   a.batch.token(t, base, n);
@@ -84,6 +101,32 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   if (n <= a.k) return;  // every visible position is kept; finalize writes them
   if (c0 >= n) return;
   const int c1 = min(n, c0 + kSelectChunk);
+  if (hsw) {
+    __syncthreads();
+    const int hc = a.hist_chunk;
+    const int slots = (a.batch.max_len + hc - 1) / hc;
+    h1.add_lists(hsw, slots, lds_h1, lds_ovf);
+    __syncthreads();
+    // a chunk whose bins did not fit its slot is counted from its scores
+    // (positions [c * hc, min(n, (c + 1) * hc)), all written by the indexer)
+    uint32_t ovf[kMaxHistSlots / 32];
+#pragma unroll
+    for (int wd = 0; wd < kMaxHistSlots / 32; ++wd) ovf[wd] = lds_ovf[wd];
+    if (ovf[0] | ovf[1] | ovf[2] | ovf[3]) {
+      for (int wd = 0; wd < kMaxHistSlots / 32; ++wd) {
+        uint32_t bits = ovf[wd];
+        while (bits) {
+          const int c = 32 * wd + __ffs(bits) - 1;
+          bits &= bits - 1u;
+          const int p1 = min(n, (c + 1) * hc);
+          for (int p = c * hc + (int)threadIdx.x; p < p1; p += kSelThreads)
+            atomicAdd(&lds_h1[score_key(srow[p]) >> (32 - kDigit1Bits)], 1u);
+        }
+      }
+      __syncthreads();
+    }
+    h1.load_lds(lds_h1);
+  }
   if (threadIdx.x == 0) lds_count = 0;
   // first radix cut, taken redundantly by every workgroup of the token from the
   // histogram the previous kernel completed (no cross-workgroup hand-off)
@@ -377,6 +420,10 @@ hipError_t launch_clear(uint32_t* p, int64_t words, hipStream_t s) {
   if (blocks > 1024) blocks = 1024;
   clear_kernel<<<(unsigned)blocks, 256, 0, s>>>(p, words);
   return hipGetLastError();
+}
+
+int topk_hist_slot_words(int max_len) {
+  return hist_slot_words(((int64_t)max_len + kIndexerChunk - 1) / kIndexerChunk);
 }
 
 hipError_t launch_topk_hist(const TopkArgs& a, hipStream_t s) {

@@ -177,6 +177,33 @@ def test_ragged_batch_many_tokens_per_sequence():
     _check_forward(wl)
 
 
+def test_histogram_lists_overflow_to_scores():
+    # Keys scaled by powers of two (row r by 2^(r mod 10) in alternate blocks of
+    # 2,048 rows, else by 2^(r mod 3)): a 256-position indexer chunk then holds
+    # 70-85 distinct first-level bins in the wide blocks, more than its list
+    # slot takes (63 entries at 64 chunks per token), and 25-30 in the others.
+    # The select kernel counts the overflowed chunks from their scores and the
+    # rest from their lists. Scores stay integers below 2^24, so exact.
+    lengths = [16384, 12000, 16384, 9000, 16384, 15000, 16384, 700]
+    wl = si.build("hist_overflow", lengths, [(b, L - 1) for b, L in enumerate(lengths)], seed=41)
+    r = torch.arange(wl.k_idx.shape[0])
+    mult = torch.pow(2.0, torch.where((r // 2048) % 2 == 0, r % 10, r % 3)).unsqueeze(1)
+    wl.k_idx = (wl.k_idx.float() * mult).to(torch.bfloat16)
+    say(f"[forward] {wl.name}: T={wl.num_tokens} max_len={wl.max_len}")
+    ref = run_oracle(wl, keep_scores=True)
+    spread = 0
+    for sc in ref["scores"]:
+        assert np.all(sc == np.round(sc)) and np.abs(sc).max() < 2.0 ** 24
+        keys = sc.astype(np.float32).view(np.uint32)
+        digit = np.where(keys >> 31, ~keys, keys | np.uint32(0x80000000)) >> 20
+        spread += sum(len(np.unique(digit[c:c + 256])) > 63 for c in range(0, sc.shape[0], 256))
+    assert spread > 0, "no chunk holds more bins than its slot"
+    idx, out, lse = Dev(wl).forward()
+    assert np.array_equal(idx.cpu().numpy(), ref["indices"]), "indices differ"
+    assert_out_close(out.cpu().numpy(), ref["out"], False, wl.name)
+    assert_lse_close(lse.cpu().numpy(), ref["lse"], wl.name)
+
+
 def test_fp8_caches_small():
     wl = si.build("fp8_small", [3000, 2100], [(0, 2999), (1, 2099), (0, 1000)], seed=8, fp8=True)
     _check_forward(wl)
