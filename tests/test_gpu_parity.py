@@ -204,6 +204,16 @@ def test_histogram_lists_overflow_to_scores():
     assert_lse_close(lse.cpu().numpy(), ref["lse"], wl.name)
 
 
+def test_many_short_sequences_one_token_each():
+    # 520 sequences with one decode token each: with 512 or more tokens the
+    # one-workgroup top-k selects, so the decode indexer adds into a dense
+    # first-level histogram, which the clear kernel zeroes first
+    rng = np.random.default_rng(43)
+    lens = rng.integers(300, 700, 520).tolist()
+    wl = si.build("many_short_seqs", lens, [(b, L - 1) for b, L in enumerate(lens)], seed=43, k=128)
+    _check_forward(wl)
+
+
 def test_fp8_caches_small():
     wl = si.build("fp8_small", [3000, 2100], [(0, 2999), (1, 2099), (0, 1000)], seed=8, fp8=True)
     _check_forward(wl)
