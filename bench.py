@@ -483,6 +483,140 @@ def cpu_baseline(wl, min_seconds: float):
 
 
 # ---------------------------------------------------------------- main
+# ---------------------------------------------------------------- device timeline
+TIMELINE_LIB = os.path.join(ROOT, "sparse_gated_mla_amd", "libsga_timeline.so")
+TL_WORDS = 1 << 16                   # 64-bit words per stamp record (slot s, point k: 8s + k)
+TL_RECORDS = ("indexer", "topk", "attn")
+
+
+def timeline_summary(ix: np.ndarray, tk: np.ndarray, at: np.ndarray, cus: int) -> list:
+    """Text lines for one forward step from the timeline build's three stamp
+    records (uint64 words; point k of slot s at 8s + k, point 7 the ids XCC_ID
+    << 32 | HW_ID; slots and points the step did not reach read 0). Times are
+    microseconds of the 100 MHz device clock from the first indexer
+    workgroup's start. Indexer slots (decode indexer of the forward pass): 0
+    start, 1 keys set up (batch metadata known), 2 first key tile in LDS, 3
+    last tile scored, 4 end. Select slots: 0 start, 2 inputs in, 3 list slots
+    summed, 4 cut taken, 5 candidates written, 1 end. Attention slots below
+    4,096: 0 start, 1 the top-k's final stage done (selecting variant), 2 first
+    row tile in LDS, 3 tiles done, 4 partials written; combine slots from
+    4,096: 0 start, 1 end."""
+    ix, tk, at = (r.reshape(-1, 8).astype(np.int64) for r in (ix, tk, at))
+    wi = ix[ix[:, 0] > 0]
+    if len(wi) == 0:
+        return ["no indexer stamps (the decode indexer of the forward pass did not run)"]
+    base = wi[:, 0].min()
+
+    def t(col):   # microseconds from base; unstamped points become NaN
+        return np.where(col > 0, (col - base) / 100.0, np.nan)
+
+    def med(x):
+        x = x[~np.isnan(x)]
+        return f"{np.median(x):7.2f}" if len(x) else "      -"
+
+    def lo(x):
+        x = x[~np.isnan(x)]
+        return f"{x.min():7.2f}" if len(x) else "      -"
+
+    def hi(x):
+        x = x[~np.isnan(x)]
+        return f"{x.max():7.2f}" if len(x) else "      -"
+
+    slots = np.nonzero(ix[:, 0] > 0)[0]
+    lines = [f"indexer: {len(wi)} workgroups, last end {hi(t(wi[:, 4]))}",
+             "  dispatch group (slots)        n   start  keys set up  first tile      end   last end"]
+    groups = ((f"first per CU (0-{cus - 1})", slots < cus),
+              (f"second per CU ({cus}-{2 * cus - 1})", (slots >= cus) & (slots < 2 * cus)),
+              (f"later ({2 * cus}-)", slots >= 2 * cus))
+    for name, m in groups:
+        if not m.any():
+            continue
+        g = wi[m]
+        lines.append(f"  {name:<27}{m.sum():>5} {med(t(g[:, 0]))}      {med(t(g[:, 1]))}    {med(t(g[:, 2]))}  "
+                     f"{med(t(g[:, 4]))}    {hi(t(g[:, 4]))}")
+    xcc = (wi[:, 7] >> 32) & 0xF
+    lines.append("  last end per XCD: " + " ".join(f"{x}:{hi(t(wi[xcc == x, 4])).strip()}"
+                                                for x in range(8) if (xcc == x).any()))
+    ws = tk[tk[:, 0] > 0]
+    if len(ws):
+        full = ws[(ws[:, 1:6] > 0).all(axis=1)]   # workgroups that ran every phase
+        lines.append(f"select: {len(ws)} workgroups, start {lo(t(ws[:, 0]))}, end {hi(t(ws[:, 1]))}")
+        if len(full):
+            d = lambda a, b: (full[:, a] - full[:, b]) / 100.0
+            lines.append(f"  per workgroup (medians): inputs in {med(d(2, 0))}, list slots summed {med(d(3, 2))}, "
+                         f"cut {med(d(4, 3))}, candidates written {med(d(5, 4))}, whole {med(d(1, 0))}")
+    wa = at[:4096][at[:4096, 0] > 0]
+    if len(wa):
+        lines.append(f"attention: {len(wa)} workgroups, start {lo(t(wa[:, 0]))}, final stage done {med(t(wa[:, 1]))}, "
+                     f"first tile {med(t(wa[:, 2]))}, tiles done {med(t(wa[:, 3]))}, end {hi(t(wa[:, 4]))}")
+    wc = at[4096:][at[4096:, 0] > 0]
+    if len(wc):
+        lines.append(f"combine: {len(wc)} workgroups, start {lo(t(wc[:, 0]))}, end {hi(t(wc[:, 1]))}")
+    return lines
+
+
+def run_timeline(workload: str, steps: int, reps: int = 3) -> None:
+    """Prints the device-clock timeline of the last of `steps` back-to-back
+    forward steps, `reps` times, from libsga_timeline.so (the same kernels
+    with per-workgroup stamps; see sga_device.h)."""
+    if not os.path.exists(TIMELINE_LIB):
+        raise SystemExit(f"{TIMELINE_LIB} is missing: build it with "
+                         "`python -m sparse_gated_mla_amd.build --timeline`")
+    from sparse_gated_mla_amd import _lib as L
+    lib = L.load(TIMELINE_LIB)
+    L._lib = lib
+    for r in TL_RECORDS:
+        for fn in (f"sga_tl_read_{r}", f"sga_tl_clear_{r}"):
+            getattr(lib, fn).argtypes = [ctypes.c_void_p]
+            getattr(lib, fn).restype = ctypes.c_int
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = si.config(WORKLOADS[workload])
+    T = wl.num_tokens
+    sets = []
+    for _ in range(2):
+        d = lambda x: None if x is None else x.to(dev)
+        batch = sga.batch_to_device(wl.token_seq, wl.token_pos, wl.seq_start, wl.seq_len,
+                                    wl.cache_rows, device=dev, max_len=wl.max_len)
+        sets.append(dict(batch=batch, q_idx=d(wl.q_idx), w=d(wl.w), k_idx=d(wl.k_idx),
+                         k_idx_scale=d(wl.k_idx_scale), q_abs=d(wl.q_abs), kv=d(wl.kv),
+                         kv_scale=d(wl.kv_scale), gate=d(wl.gate)))
+    out = torch.empty((T, 64, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((T, 64), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, wl.k), dtype=torch.int32, device=dev)
+    ws = sga.workspace(sga.sga_forward_workspace_size(T, wl.max_len, wl.k), dev)
+
+    def step(i):
+        s = sets[i % 2]
+        sga.sga_forward(s["batch"], s["q_idx"], s["w"], s["k_idx"], s["k_idx_scale"], s["q_abs"],
+                        s["kv"], s["kv_scale"], wl.k, wl.sm_scale, s["gate"], out, lse, idx, ws=ws)
+
+    for i in range(200):
+        step(i)
+    torch.cuda.synchronize()
+    zeros = np.zeros(TL_WORDS, dtype=np.uint64)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    print(f"device timeline: {workload}; the last of {steps} back-to-back forward steps, "
+          f"microseconds from the first indexer workgroup's start", flush=True)
+    for rep in range(reps):
+        for r in TL_RECORDS:
+            if getattr(lib, f"sga_tl_clear_{r}")(zeros.ctypes.data) != 0:
+                raise SystemExit(f"sga_tl_clear_{r} failed")
+        # every step stamps the same slots and points, so the records hold the last step's
+        for i in range(steps):
+            step(i)
+        torch.cuda.synchronize()
+        recs = []
+        for r in TL_RECORDS:
+            buf = np.zeros(TL_WORDS, dtype=np.uint64)
+            if getattr(lib, f"sga_tl_read_{r}")(buf.ctypes.data) != 0:
+                raise SystemExit(f"sga_tl_read_{r} failed")
+            recs.append(buf)
+        print(f"run {rep + 1}:", flush=True)
+        for line in timeline_summary(*recs, cus):
+            print("  " + line, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -499,6 +633,9 @@ def main():
     ap.add_argument("--copies", type=int, default=2, help="input sets alternated between steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device copy of known size (for counter calibration)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="print the device-clock timeline of a forward step from libsga_timeline.so "
+                         "(python -m sparse_gated_mla_amd.build --timeline) instead of the benchmark")
     ap.add_argument("--summarize-pmc", metavar="DIR",
                     help="write the workload's per-kernel counter summary from rocprofv3 runs under DIR")
     args = ap.parse_args()
@@ -512,6 +649,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.timeline:
+        run_timeline(args.workload, steps=20)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 

@@ -1,9 +1,13 @@
 """Builds libsga.so (the gfx950 HIP kernels and the C ABI) in-tree with hipcc.
 
-    python -m sparse_gated_mla_amd.build
+    python -m sparse_gated_mla_amd.build              # libsga.so
+    python -m sparse_gated_mla_amd.build --timeline   # libsga_timeline.so
 
 hipcc cross-compiles for gfx950 and needs no GPU. Packed-fp32 instructions are
-switched off for all device code.
+switched off for all device code. The timeline library is the same sources
+built with SGA_TIMELINE defined: the step's kernels also record per-workgroup
+device-clock stamps, which `bench.py --timeline` reads. Nothing loads it
+unless asked to.
 """
 from __future__ import annotations
 
@@ -17,6 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libsga.so")
+TIMELINE_LIB = os.path.join(PKG, "libsga_timeline.so")
 SOURCES = ["sga_api.hip", "indexer.hip", "topk.hip", "attention.hip", "cache.hip", "proj.hip",
            "measure.hip"]
 ARCH = "gfx950"
@@ -36,18 +41,20 @@ def command(out: str = LIB, extra=()) -> list:
             *[os.path.join(CSRC, s) for s in SOURCES], *extra, "-o", out]
 
 
-def build(verbose: bool = False) -> str:
-    """Compiles every HIP source into libsga.so next to this file; returns its path."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Compiles every HIP source into libsga.so next to this file (or, with
+    timeline, into libsga_timeline.so with the device-clock stamps); returns its path."""
+    lib = TIMELINE_LIB if timeline else LIB
+    tmp = lib + ".tmp"
+    cmd = command(tmp, ("-DSGA_TIMELINE",) if timeline else ())
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if proc.returncode != 0:
         raise RuntimeError(f"hipcc failed ({proc.returncode}):\n{proc.stdout}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, timeline="--timeline" in sys.argv))

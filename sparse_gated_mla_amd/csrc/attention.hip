@@ -46,6 +46,8 @@
 #include "sga_finalize.h"
 #include "sga_kernels.h"
 
+SGA_TL_RECORD(attn)
+
 namespace sga {
 namespace {
 
@@ -417,6 +419,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
   using Stage = RowStage<kFmt>;
   const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int t = wg / a.splits, split = wg % a.splits;
+  if constexpr (!kProbs) {
+    SGA_TL_STAMP(wg, 0);
+    SGA_TL_ID(wg);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the two waves of a pair share a SIMD and leave each barrier together; the
   // first gets the higher issue priority, so it reaches its value product while
@@ -465,6 +471,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
               [&](uint32_t o, uint32_t p) { lds_idx[o - j_begin] = (int32_t)p; });
     }
     __syncthreads();   // the indices are in LDS, and the stage's LDS is free again
+    if constexpr (!kProbs) SGA_TL_STAMP(wg, 1);
     if (a.indices_out)
       for (int j = threadIdx.x; j < nrows; j += kAttnThreads)
         a.indices_out[(int64_t)t * a.k + j_begin + j] = lds_idx[j];
@@ -501,6 +508,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
   s0.load_rows(rows, scales, 2, nrows, n);
   load_idx(s0, 4);
   __syncthreads();
+  if constexpr (!kProbs) SGA_TL_STAMP(wg, 2);
 
   // step i: store tile i+1 from its stage into region (i+1) % 3, refill the
   // stage with tile i+3 (indices loaded two tiles earlier) and the indices of
@@ -530,7 +538,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(AttnArgs a, TopkArgs
     step(s1, i);
     step(s0, i + 1);
   }
-  if constexpr (!kProbs) finish_half(a, st, t, split, head, lane, half);
+  if constexpr (!kProbs) {
+    SGA_TL_STAMP(wg, 3);
+    finish_half(a, st, t, split, head, lane, half);
+    SGA_TL_STAMP(wg, 4);
+  }
 }
 
 // Merges the split partials by log-sum-exp, then gates. One workgroup of two
@@ -545,6 +557,8 @@ constexpr int kCombineRound = 16;
 __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
   const int wg = xcd_grouped(blockIdx.y * gridDim.x + blockIdx.x, gridDim.x * gridDim.y);
   const int db = wg % (kDLatent / 16), t = wg / (kDLatent / 16);
+  SGA_TL_STAMP(4096 + wg, 0);
+  SGA_TL_ID(4096 + wg);
   const int h = threadIdx.x >> 1, q = threadIdx.x & 1;
   const int S = a.splits;
   const int64_t th = (int64_t)t * kHeads + h;
@@ -589,6 +603,7 @@ __global__ __launch_bounds__(128) void combine_kernel(AttnArgs a) {
   *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 16 * db + 8 * q) = acc0 * inv;
   *reinterpret_cast<f32x4*>(a.out + th * kDLatent + 16 * db + 8 * q + 4) = acc1 * inv;
   if (a.lse && db == 0 && q == 0) a.lse[th] = L > 0.0f ? (M + log2f(L)) * kLn2 : -INFINITY;
+  SGA_TL_STAMP(4096 + wg, 1);
 }
 
 // The sparse indexer loss of one token: KL(p || q) over its selected rows,

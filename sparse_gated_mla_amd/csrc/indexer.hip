@@ -36,6 +36,8 @@
 #include "sga_block.h"
 #include "sga_kernels.h"
 
+SGA_TL_RECORD(indexer)
+
 namespace sga {
 namespace {
 
@@ -236,6 +238,10 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   __shared__ uint32_t lds_scan[kWaves];
   __shared__ __attribute__((aligned(16))) float lds_sc[indexer_chunk(kFp8)];
   const int t = blockIdx.y;
+  if constexpr (kHist) {
+    SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 0);
+    SGA_TL_ID(blockIdx.y * gridDim.x + blockIdx.x);
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   // the head weights and the query need no batch metadata: their loads go
   // out first (the weights first, so that the wait for them leaves the query
@@ -266,6 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
         kFp8 ? (const void*)(static_cast<const uint32_t*>(a.k_scale) + base + chunk0) : (const void*)a.k_idx,
         kFp8 ? (uint32_t)len * 4u : 0u);
     const int ngroups = (len + Tile::kGroupRows - 1) / Tile::kGroupRows;
+    if constexpr (kHist) SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 1);
 
     // this wave's tile of every group; kStages groups in flight. Loads are
     // never skipped (past the chunk they read zeros), so each wait is exact.
@@ -277,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
 #pragma unroll
       for (int j = 0; j < S; ++j) {
         st[j].store(lds, lane);
+        if constexpr (kHist) if (i == 0 && j == 0) SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 2);
         const uint32_t ks = st[j].scale;
         st[j].load(keys, scales, i + j + S, wave, lane);
         if (i + j < ngroups) {
@@ -299,6 +307,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
   // select kernel reads the scores once, after the kernel boundary, and lines
   // left dirty in L2 would only be written back when the kernel ends (0.5 us
   // per step less at 16 x 128K)
+  if constexpr (kHist) SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 3);
   __syncthreads();
   if (len > 0) {
     float* srow = a.scores + (int64_t)t * a.ld + chunk0;
@@ -318,6 +327,7 @@ __global__ __launch_bounds__(kThreads, 2) void indexer_kernel(IndexerArgs a) {
     } else {
       hist1_flush<kThreads>(lds_hist, a.hist + (int64_t)t * kHist1);
     }
+    SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 4);
   }
 }
 

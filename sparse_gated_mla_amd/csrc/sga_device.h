@@ -215,4 +215,44 @@ __device__ __forceinline__ int xcd_grouped(int b, int total) {
   return x * per + min(x, rem) + j;
 }
 
+// ---------------------------------------------------------------- timeline build
+// Built with SGA_TIMELINE defined (`python -m sparse_gated_mla_amd.build
+// --timeline`, into a library of its own), the step's kernels record, per
+// workgroup, the 100 MHz real-time counter (s_memrealtime) at a few points and
+// the workgroup's XCD and hardware ids, for the device-clock timeline that
+// `bench.py --timeline` prints. Each source file that stamps holds its own
+// record of 2^16 words, word 8s + k for point k of slot s (slots below 8,192;
+// point 7 holds the ids: XCC_ID << 32 | HW_ID), and exports a reader and a
+// clear (both synchronous copies, from or to a host buffer of 2^16 words). In the
+// library that the path normally runs these expand to nothing.
+#ifdef SGA_TIMELINE
+#define SGA_TL_RECORD(tag)                                                                  \
+  static __device__ uint64_t sga_tl_words[1 << 16];                                        \
+  extern "C" __attribute__((visibility("default"))) int sga_tl_read_##tag(void* dst) {      \
+    return (int)hipMemcpyFromSymbol(dst, HIP_SYMBOL(sga_tl_words), sizeof(sga_tl_words), 0, \
+                                    hipMemcpyDeviceToHost);                                \
+  }                                                                                         \
+  extern "C" __attribute__((visibility("default"))) int sga_tl_clear_##tag(const void* zeros) { \
+    return (int)hipMemcpyToSymbol(HIP_SYMBOL(sga_tl_words), zeros, sizeof(sga_tl_words), 0,   \
+                                  hipMemcpyHostToDevice);                                     \
+  }
+#define SGA_TL_STAMP(slot, k)                                                 \
+  do {                                                                        \
+    const int sga_tl_slot = (slot);                                           \
+    if (threadIdx.x == 0 && sga_tl_slot < 8192)                               \
+      sga_tl_words[sga_tl_slot * 8 + (k)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#define SGA_TL_ID(slot)                                                                      \
+  do {                                                                                       \
+    const int sga_tl_slot = (slot);                                                          \
+    if (threadIdx.x == 0 && sga_tl_slot < 8192)                                              \
+      sga_tl_words[sga_tl_slot * 8 + 7] = ((uint64_t)__builtin_amdgcn_s_getreg(0x7814) << 32) | \
+                                          (uint32_t)__builtin_amdgcn_s_getreg(0xF804);        \
+  } while (0)
+#else
+#define SGA_TL_RECORD(tag)
+#define SGA_TL_STAMP(slot, k) do {} while (0)
+#define SGA_TL_ID(slot) do {} while (0)
+#endif
+
 }  // namespace sga

@@ -29,6 +29,8 @@
 #include "sga_finalize.h"
 #include "sga_kernels.h"
 
+SGA_TL_RECORD(topk)
+
 namespace sga {
 namespace {
 
@@ -72,6 +74,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   __shared__ uint32_t lds_ovf[kMaxHistSlots / 32];
   constexpr int kSteps = kSelectChunk / kSelThreads;   // 64-position steps per wave
   const int t = blockIdx.y;
+  SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 0);
+  SGA_TL_ID(blockIdx.y * gridDim.x + blockIdx.x);
   const int c0 = blockIdx.x * kSelectChunk;   // < max_len: the grid covers max_len
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const float* srow = a.scores + (int64_t)t * a.ld;
@@ -105,8 +109,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     __syncthreads();
     const int hc = a.hist_chunk;
     const int slots = (a.batch.max_len + hc - 1) / hc;
+    SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 2);
     h1.add_lists(hsw, slots, lds_h1, lds_ovf);
     __syncthreads();
+    SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 3);
     // a chunk whose bins did not fit its slot is counted from its scores
     // (positions [c * hc, min(n, (c + 1) * hc)), all written by the indexer)
     uint32_t ovf[kMaxHistSlots / 32];
@@ -132,6 +138,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
   // histogram the previous kernel completed (no cross-workgroup hand-off)
   uint32_t d1, above1, n1;
   h1.cut((uint32_t)a.k, scratch, d1, above1, n1);
+  SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 4);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     a.ctrl[t].digit1 = d1;
     a.ctrl[t].above1 = above1;
@@ -173,8 +180,10 @@ __global__ __launch_bounds__(kSelThreads) void topk_select_kernel(TopkArgs a) {
     }
     off += (uint32_t)__popcll(cmask[i]);
   }
+  SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 5);
   __syncthreads();
   if (threadIdx.x == 0) a.wg_count[(int64_t)t * a.max_select_wgs + blockIdx.x] = lds_count;
+  SGA_TL_STAMP(blockIdx.y * gridDim.x + blockIdx.x, 1);
 }
 
 // The final stage (sga_finalize.h) for one window of ranks of one token:

@@ -128,3 +128,30 @@ def test_summary_without_calibration_copy_is_an_error(tmp_path, monkeypatch):
     with pytest.raises(SystemExit):
         bench.summarize_pmc(root, "long_decode_128k")
     assert not (tmp_path / "pmc.json").exists()
+
+
+def test_timeline_summary_reads_the_stamp_layout():
+    # two indexer workgroups, one select, one attention and one combine
+    # workgroup, stamped at known device-clock ticks (100 per microsecond)
+    ix = np.zeros((8192, 8), np.uint64)
+    tk = np.zeros((8192, 8), np.uint64)
+    at = np.zeros((8192, 8), np.uint64)
+    t0 = 10_000_000
+    ix[0, [0, 1, 2, 3, 4]] = [t0, t0 + 200, t0 + 400, t0 + 2900, t0 + 3000]
+    ix[0, 7] = (3 << 32) | 0x123
+    ix[1, [0, 1, 2, 3, 4]] = [t0 + 10, t0 + 500, t0 + 1300, t0 + 4300, t0 + 4400]
+    ix[1, 7] = (5 << 32) | 0x456
+    tk[0, [0, 2, 3, 4, 5, 1]] = [t0 + 4600, t0 + 4740, t0 + 4820, t0 + 4920, t0 + 5180, t0 + 5190]
+    at[0, [0, 1, 2, 3, 4]] = [t0 + 5400, t0 + 6200, t0 + 6540, t0 + 7360, t0 + 7460]
+    at[4096, [0, 1]] = [t0 + 7650, t0 + 8090]
+    lines = bench.timeline_summary(ix.reshape(-1), tk.reshape(-1), at.reshape(-1), cus=1)
+    text = "\n".join(lines)
+    assert "indexer: 2 workgroups, last end   44.00" in text
+    rows = {ln.split("(")[0].strip(): ln.split(")")[1].split() for ln in lines if "per CU (" in ln}
+    assert rows["first per CU"] == ["1", "0.00", "2.00", "4.00", "30.00", "30.00"]
+    assert rows["second per CU"] == ["1", "0.10", "5.00", "13.00", "44.00", "44.00"]
+    assert "3:30.00" in text and "5:44.00" in text
+    assert "select: 1 workgroups, start   46.00, end   51.90" in text
+    assert "inputs in    1.40, list slots summed    0.80, cut    1.00, candidates written    2.60, whole    5.90" in text
+    assert "start   54.00, final stage done   62.00, first tile   65.40, tiles done   73.60, end   74.60" in text
+    assert "combine: 1 workgroups, start   76.50, end   80.90" in text
